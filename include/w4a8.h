@@ -1,0 +1,146 @@
+/*
+ * w4a8.h -- C ABI of libw4a8: a W4A8 quantized linear layer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ *   Y[M,N] (fp16) = X[M,K] . W[N,K]^T
+ *
+ * Weights are quantized offline in two levels (per-output-channel symmetric
+ * INT8 in the protective range [-119, 119] with an fp16 scale s0, then per
+ * group of 128 consecutive k asymmetric UINT4 with an integer scale s1 and a
+ * zero point z).  Activations are quantized per token to INT8 by their
+ * absolute maximum.  The GEMM main loop rebuilds INT8 weights in registers as
+ * q4*s1 - z*s1 and contracts them with the INT8 activations on the INT8 matrix
+ * cores into INT32; an fp32 epilogue applies s_a[m] and s0[n] and writes fp16.
+ *
+ * Pages the operations follow (by title and section):
+ *  - QServe: W4A8KV4 Quantization and System Co-design for Efficient LLM
+ *    Serving (talk summary): "Progressive Group Quantization for W4A8 GEMM",
+ *    "Precision Data Flow and Activation Quantization Fusion", "Quantized
+ *    Matrix Multiplication (GEMM) Kernel on GPUs", "Challenges and Design
+ *    Details of QServe GEMM Kernel".
+ *  - Lecture 15 notes: 15.5 (dequantization inside the main loop) and 15.6
+ *    (two-level quantization, int4 -> int8 by one multiply and one subtract).
+ *  - QFactory reading notes: 2.1 (asymmetric quantization, w = (q - zero) * scale).
+ *
+ * Conventions for every entry point:
+ *  - Ownership: every buffer argument is device memory allocated and freed by
+ *    the caller (unless marked "host").  The library never allocates, frees
+ *    or keeps per-call state; it is safe to call from several host threads.
+ *  - Streams: all device work is enqueued on `stream` (0 = the null stream)
+ *    and is asynchronous; results are ready when the stream is synchronised.
+ *  - Alignment: device pointers must be 16-byte aligned.
+ *  - Errors: argument errors (W4A8_E_NULL, W4A8_E_SHAPE, W4A8_E_ALIGN,
+ *    W4A8_E_WORKSPACE) are detected on the host before anything is launched
+ *    and leave every buffer untouched.  W4A8_E_HIP reports a launch failure
+ *    (hipGetLastError after the launch).  No C++ exception crosses the ABI.
+ *  - Shapes: K > 0 and K % 128 == 0; N > 0 and N % 16 == 0; M >= 0.  M == 0
+ *    is a successful no-op.  Inputs must be finite; the results for NaN or
+ *    Inf inputs are unspecified.
+ *  - Results are deterministic: bit-identical from run to run.
+ */
+#ifndef W4A8_H
+#define W4A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum w4a8_status {
+    W4A8_OK = 0,
+    W4A8_E_NULL = -1,       /* a required pointer is NULL                  */
+    W4A8_E_SHAPE = -2,      /* M < 0, N <= 0, K <= 0, K % 128, N % 16, ld  */
+    W4A8_E_ALIGN = -3,      /* a device pointer is not 16-byte aligned      */
+    W4A8_E_WORKSPACE = -4,  /* workspace missing or smaller than required   */
+    W4A8_E_HIP = -5         /* a HIP launch or runtime call failed          */
+} w4a8_status;
+
+/* Text for a status code (host; static storage, never NULL). */
+const char *w4a8_status_string(w4a8_status st);
+
+/* Library version as "major.minor.patch" (host; static storage). */
+const char *w4a8_version(void);
+
+/* ------------------------------------------------------------------------
+ * Offline weight quantization (QServe talk summary, "Progressive Group
+ * Quantization for W4A8 GEMM"; Lecture 15 notes, 15.6).
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of the device weight stream for an N x K weight (host).  Returns 0
+ * for an invalid shape.  The stream holds the packed UINT4 codes (N*K/2
+ * bytes) followed by one byte of group parameters per (n, group)
+ * ((s1 - 1) | z << 4); its internal order is private to the library. */
+size_t w4a8_packed_weight_bytes(int64_t N, int64_t K);
+
+/* Quantize fp32 weights w [N, K] (row-major, row stride K) in two levels.
+ *   level 1, per output channel n:
+ *     s0[n] = fp16_rne(max_k |w[n,k]| / 119)   (fp32 division)
+ *     q8    = clamp(rint(w / float(s0[n])), -119, 119)   (0 if s0 == 0)
+ *   level 2, per group j of 128 consecutive k in row n (integers):
+ *     lo = min(0, min q8), hi = max(0, max q8)
+ *     s1 = max(1, ceil((hi - lo) / 15))  in [1, 16]
+ *     z  = rne(-lo / s1)                 in [0, 15]
+ *     q4 = clamp(rne(q8 / s1) + z, 0, 15)
+ * Writes the device weight stream `wpacked` (w4a8_packed_weight_bytes(N, K)
+ * bytes) and s0_fp16 [N] (fp16 bit patterns).  s1 and z [N, K/128] receive
+ * the canonical group parameters when non-NULL (for inspection and tests).
+ * w, wpacked and s0_fp16 are required. */
+w4a8_status quantize_weights_w4g128(const float *w, int64_t N, int64_t K,
+                                    void *wpacked, uint8_t *s1, uint8_t *z,
+                                    uint16_t *s0_fp16, hipStream_t stream);
+
+/* Inverse of the packing step: rebuild the canonical codes from a device
+ * weight stream.  q4_canon [N, K/2]: byte (n, k/2) holds q4[n,k] for even k
+ * in its low nibble and q4[n,k+1] in its high nibble.  s1, z [N, K/128].
+ * All pointers required.  For tests and inspection. */
+w4a8_status w4a8_unpack_weights(const void *wpacked, int64_t N, int64_t K,
+                                uint8_t *q4_canon, uint8_t *s1, uint8_t *z,
+                                hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Per-token INT8 activation quantization (QServe talk summary, "Precision
+ * Data Flow and Activation Quantization Fusion": every linear layer takes
+ * 8-bit activations).
+ *   s_a[m] = max_k |x[m,k]| / 127   (fp32 division)
+ *   qx[m,k] = clamp(rint(x[m,k] / s_a[m]), -127, 127)   (0 if s_a == 0)
+ * x_fp16: [M, K] fp16 bit patterns, row stride ldx >= K elements (ldx must
+ * be a multiple of 8).  qx: [M, K] int8, row stride K.  s_a: [M] fp32.
+ * ------------------------------------------------------------------------ */
+w4a8_status quantize_act_per_token_i8(const uint16_t *x_fp16, int64_t M,
+                                      int64_t K, int64_t ldx, int8_t *qx,
+                                      float *s_a, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * W4A8 GEMM (QServe talk summary, "Quantized Matrix Multiplication (GEMM)
+ * Kernel on GPUs" and "Challenges and Design Details of QServe GEMM Kernel";
+ * Lecture 15 notes, 15.5-15.6).
+ *   acc[m,n] = sum_k qx[m,k] * (q4[n,k]*s1[n,k/128] - z[n,k/128]*s1[n,k/128])
+ *              (exact, INT32)
+ *   y[m,n]   = fp16_rne((float(acc) * s_a[m]) * float(s0[n]))
+ * qx [M, K] int8 and s_a [M] fp32 as written by quantize_act_per_token_i8;
+ * wpacked and s0_fp16 as written by quantize_weights_w4g128.
+ * y_fp16: [M, N] fp16 bit patterns, row-major.  acc_out: optional [M, N]
+ * int32, row-major; when non-NULL the raw accumulators of the same main loop
+ * are written too.
+ * ws: workspace of at least gemm_w4a8_workspace_bytes(M, N, K) bytes, zeroed
+ * by the caller once after allocation; every call leaves it zeroed again.
+ * ws may be NULL only when that size is 0.  Calls that share one workspace
+ * must be ordered (same stream, or synchronised): concurrent calls on one
+ * workspace race.
+ * ------------------------------------------------------------------------ */
+size_t gemm_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+w4a8_status gemm_w4a8(const int8_t *qx, const float *s_a, const void *wpacked,
+                      const uint16_t *s0_fp16, int64_t M, int64_t N, int64_t K,
+                      uint16_t *y_fp16, int32_t *acc_out, void *ws,
+                      size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A8_H */

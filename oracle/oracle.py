@@ -1,0 +1,239 @@
+"""ctypes wrappers around the C oracle (``w4a8_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Every function takes and
+returns numpy arrays on the host; none touches a GPU.  Each wrapper names the
+step of the method it computes; the citations of the pages are next to the C
+implementation of that step.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "w4a8_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# A different build of the same source may be substituted (the mutation test
+# of the pins loads deliberately broken copies this way).
+_LIB_OVERRIDE = os.environ.get("W4A8_ORACLE_LIB")
+_lock = threading.Lock()
+_lib = None
+
+GROUP = 128
+PROTECT = 119
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no FMA contraction)."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB_PATH):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        lib.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.orc_f16_to_f32.restype = ctypes.c_float
+        lib.orc_f32_to_f16.argtypes = [ctypes.c_float]
+        lib.orc_f32_to_f16.restype = ctypes.c_uint16
+        lib.orc_rne_div.argtypes = [I64, I64]
+        lib.orc_rne_div.restype = I64
+        lib.orc_quantize_act.argtypes = [P, I64, I64, I64, P, P]
+        lib.orc_quantize_act.restype = None
+        lib.orc_weights_level1.argtypes = [P, I64, I64, P, P]
+        lib.orc_weights_level1.restype = None
+        lib.orc_weights_level2.argtypes = [P, I64, I64, P, P, P]
+        lib.orc_weights_level2.restype = None
+        lib.orc_pack_q4.argtypes = [P, I64, I64, P]
+        lib.orc_pack_q4.restype = None
+        lib.orc_dequant_i8.argtypes = [P, P, P, I64, I64, P]
+        lib.orc_dequant_i8.restype = I64
+        lib.orc_gemm_acc.argtypes = [P, P, I64, I64, I64, P]
+        lib.orc_gemm_acc.restype = I64
+        lib.orc_epilogue.argtypes = [P, P, P, I64, I64, P]
+        lib.orc_epilogue.restype = None
+        lib.orc_linear.argtypes = [P, I64, I64, P, P, P, P, I64, P, P, P, P, P]
+        lib.orc_linear.restype = ctypes.c_int
+        lib.orc_num_threads.argtypes = []
+        lib.orc_num_threads.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _p(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def _as(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# --------------------------------------------------------------------------
+# Scalar helpers
+# --------------------------------------------------------------------------
+def f32_to_f16_bits(x: float) -> int:
+    return int(_load().orc_f32_to_f16(float(x)))
+
+
+def f16_bits_to_f32(h: int) -> float:
+    return float(_load().orc_f16_to_f32(int(h) & 0xFFFF))
+
+
+def f32_to_f16_bits_array(x: np.ndarray) -> np.ndarray:
+    lib = _load()
+    flat = _as(x, np.float32).ravel()
+    out = np.empty(flat.shape, np.uint16)
+    for i, v in enumerate(flat):
+        out[i] = lib.orc_f32_to_f16(float(v))
+    return out.reshape(np.shape(x))
+
+
+def rne_div(p: int, d: int) -> int:
+    return int(_load().orc_rne_div(int(p), int(d)))
+
+
+def num_threads() -> int:
+    return int(_load().orc_num_threads())
+
+
+# --------------------------------------------------------------------------
+# The steps of the path
+# --------------------------------------------------------------------------
+def quantize_act(x_f16: np.ndarray):
+    """Per-token absmax INT8 activations.  x: fp16 [M, K] -> (qx int8 [M,K], s_a fp32 [M])."""
+    x = _as(x_f16, np.float16)
+    M, K = x.shape
+    qx = np.empty((M, K), np.int8)
+    sa = np.empty((M,), np.float32)
+    _load().orc_quantize_act(_p(x), M, K, K, _p(qx), _p(sa))
+    return qx, sa
+
+
+def weights_level1(w: np.ndarray):
+    """Per-channel INT8 in [-119, 119] with fp16 scale.  -> (q8 int8 [N,K], s0 fp16-bits uint16 [N])."""
+    w = _as(w, np.float32)
+    N, K = w.shape
+    q8 = np.empty((N, K), np.int8)
+    s0 = np.empty((N,), np.uint16)
+    _load().orc_weights_level1(_p(w), N, K, _p(q8), _p(s0))
+    return q8, s0
+
+
+def weights_level2(q8: np.ndarray):
+    """Per-group-128 UINT4 with integer scale and zero.  -> (q4 uint8 [N,K] one code per byte, s1 [N,G], z [N,G])."""
+    q8 = _as(q8, np.int8)
+    N, K = q8.shape
+    assert K % GROUP == 0
+    G = K // GROUP
+    q4 = np.empty((N, K), np.uint8)
+    s1 = np.empty((N, G), np.uint8)
+    z = np.empty((N, G), np.uint8)
+    _load().orc_weights_level2(_p(q8), N, K, _p(q4), _p(s1), _p(z))
+    return q4, s1, z
+
+
+def pack_q4(q4: np.ndarray) -> np.ndarray:
+    """Canonical packing [N, K/2], even k in the low nibble."""
+    q4 = _as(q4, np.uint8)
+    N, K = q4.shape
+    out = np.empty((N, K // 2), np.uint8)
+    _load().orc_pack_q4(_p(q4), N, K, _p(out))
+    return out
+
+
+def dequant_i8(q4: np.ndarray, s1: np.ndarray, z: np.ndarray):
+    """Subtract-after-multiply reconstruction r = q4*s1 - z*s1.  -> (r int8 [N,K], number of out-of-range values)."""
+    q4 = _as(q4, np.uint8)
+    s1 = _as(s1, np.uint8)
+    z = _as(z, np.uint8)
+    N, K = q4.shape
+    r = np.empty((N, K), np.int8)
+    bad = _load().orc_dequant_i8(_p(q4), _p(s1), _p(z), N, K, _p(r))
+    return r, int(bad)
+
+
+def gemm_acc(qx: np.ndarray, r: np.ndarray):
+    """Exact INT32 accumulators acc[m,n] = sum_k qx[m,k] r[n,k] (int64 inside).  -> (acc int32 [M,N], overflow count)."""
+    qx = _as(qx, np.int8)
+    r = _as(r, np.int8)
+    M, K = qx.shape
+    N, K2 = r.shape
+    assert K == K2
+    acc = np.empty((M, N), np.int32)
+    bad = _load().orc_gemm_acc(_p(qx), _p(r), M, N, K, _p(acc))
+    return acc, int(bad)
+
+
+def epilogue(acc: np.ndarray, s_a: np.ndarray, s0: np.ndarray) -> np.ndarray:
+    """fp16 output bits y = fp16((float(acc) * s_a[m]) * float(s0[n]))."""
+    acc = _as(acc, np.int32)
+    s_a = _as(s_a, np.float32)
+    s0 = _as(s0, np.uint16)
+    M, N = acc.shape
+    y = np.empty((M, N), np.uint16)
+    _load().orc_epilogue(_p(acc), _p(s_a), _p(s0), M, N, _p(y))
+    return y
+
+
+def quantize_weights(w: np.ndarray) -> dict:
+    """Both levels of the progressive weight quantization."""
+    q8, s0 = weights_level1(w)
+    q4, s1, z = weights_level2(q8)
+    return {"q8": q8, "s0": s0, "q4": q4, "s1": s1, "z": z}
+
+
+def linear(x_f16: np.ndarray, wq: dict) -> dict:
+    """The serving-time path: activation quantization, dequant, contraction, epilogue."""
+    qx, sa = quantize_act(x_f16)
+    r, bad_r = dequant_i8(wq["q4"], wq["s1"], wq["z"])
+    assert bad_r == 0
+    acc, bad_a = gemm_acc(qx, r)
+    assert bad_a == 0
+    y = epilogue(acc, sa, wq["s0"])
+    return {"qx": qx, "s_a": sa, "r": r, "acc": acc, "y": y}
+
+
+def linear_timed_buffers(M: int, N: int, K: int):
+    """Preallocated outputs for ``linear_into`` (used to time the oracle)."""
+    return {"qx": np.empty((M, K), np.int8), "s_a": np.empty((M,), np.float32),
+            "r": np.empty((N, K), np.int8), "acc": np.empty((M, N), np.int32),
+            "y": np.empty((M, N), np.uint16)}
+
+
+def linear_into(x_f16: np.ndarray, wq: dict, bufs: dict) -> int:
+    """One whole serving-time call in C; returns the thread count it used."""
+    x = _as(x_f16, np.float16)
+    M, K = x.shape
+    N = wq["q4"].shape[0]
+    return int(_load().orc_linear(_p(x), M, K, _p(wq["q4"]), _p(wq["s1"]), _p(wq["z"]),
+                                  _p(wq["s0"]), N, _p(bufs["qx"]), _p(bufs["s_a"]),
+                                  _p(bufs["r"]), _p(bufs["acc"]), _p(bufs["y"])))
+
+
+__all__ = [
+    "GROUP", "PROTECT", "build", "f32_to_f16_bits", "f16_bits_to_f32", "f32_to_f16_bits_array",
+    "rne_div", "num_threads", "quantize_act", "weights_level1", "weights_level2", "pack_q4",
+    "dequant_i8", "gemm_acc", "epilogue", "quantize_weights", "linear",
+    "linear_timed_buffers", "linear_into",
+]

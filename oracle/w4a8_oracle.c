@@ -1,0 +1,350 @@
+/*
+ * w4a8_oracle.c -- plain CPU oracle for the W4A8 progressive-quantized linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU library never
+ * links, includes or calls it, and it shares no code, header or table with the
+ * GPU kernels.
+ *
+ * It computes, step by step and in the most direct form, what the method
+ * defines:
+ *
+ *   Y[M,N] = X[M,K] . W[N,K]^T
+ *
+ * with W progressively quantized (per-output-channel symmetric INT8 inside a
+ * protective range, then per-group-of-128 asymmetric UINT4 with an integer
+ * scale and a zero point), X quantized per token to INT8 by its absolute
+ * maximum, an exact integer contraction (int64 accumulation, stored as int32),
+ * and an fp32 epilogue that applies the two scales and rounds to fp16.
+ *
+ * Sources (pages, by title):
+ *  - "QServe: W4A8KV4 Quantization and System Co-design for Efficient LLM
+ *    Serving" (MLSys'25 talk summary), sections "Progressive Group Quantization
+ *    for W4A8 GEMM", "Quantized Matrix Multiplication (GEMM) Kernel on GPUs",
+ *    "Challenges and Design Details of QServe GEMM Kernel".
+ *  - Lecture 15 notes (cs2680), section 15.6 "QServe: W4A8KV4, and paying for
+ *    dequant once".
+ *  - "QFactory: Accelerating Quantized Large Language Model Serving with Qtile
+ *    Graphs" (reading notes), section 2.1 (asymmetric quantization and its
+ *    dequantization w = (w_quant - zero) * scale).
+ *
+ * Where the pages leave a rounding or tie rule open, the reading used here is
+ * written next to the step.  All floating-point steps are IEEE fp32 with
+ * round-to-nearest-even; build with -ffp-contract=off so no FMA is formed.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int orc_num_threads(void);
+
+/* ------------------------------------------------------------------------ */
+/* IEEE 754 binary16 conversions, written from the format's definition:     */
+/* 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits; subnormals have  */
+/* value frac * 2^-24.                                                       */
+/* ------------------------------------------------------------------------ */
+
+/* binary16 bits -> float (exact: every binary16 value is a float). */
+float orc_f16_to_f32(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int f = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = (f == 0) ? INFINITY : NAN;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return (float)(sign ? -v : v);
+}
+
+/* float -> binary16 bits, round to nearest, ties to even.
+ * Every float is exactly representable in double, and scaling by a power of
+ * two is exact, so rint() on the scaled value takes the rounding decision on
+ * the exact value. */
+uint16_t orc_f32_to_f16(float x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs((double)x);
+    if (isnan(x))
+        return (uint16_t)(sign | 0x7E00);
+    /* The largest finite binary16 is 65504; the midpoint to the next binade
+     * (65536, which overflows) is 65520, and the tie goes to the even
+     * neighbour, i.e. to infinity. */
+    if (a >= 65520.0)
+        return (uint16_t)(sign | 0x7C00);
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range: integer multiple of 2^-24 (may round up to the
+         * smallest normal, 1024 * 2^-24, whose bit pattern is 0x0400) */
+        double n = rint(ldexp(a, 24));
+        return (uint16_t)(sign | (uint16_t)n);
+    }
+    int e2;
+    frexp(a, &e2);            /* a = m * 2^e2 with m in [0.5, 1) */
+    int e = e2 - 1;           /* a in [2^e, 2^(e+1)) */
+    double n = rint(ldexp(a, 10 - e));   /* in [1024, 2048] */
+    if (n == 2048.0) {
+        n = 1024.0;
+        e += 1;
+    }
+    if (e > 15)
+        return (uint16_t)(sign | 0x7C00);
+    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)((int)n - 1024));
+}
+
+/* ------------------------------------------------------------------------ */
+/* Integer division rounded to nearest, ties to even (d > 0).               */
+/* ------------------------------------------------------------------------ */
+int64_t orc_rne_div(int64_t p, int64_t d)
+{
+    int64_t q = p / d;
+    int64_t r = p % d;
+    if (r < 0) {              /* make q = floor(p / d), r in [0, d) */
+        q -= 1;
+        r += d;
+    }
+    if (2 * r > d)
+        q += 1;
+    else if (2 * r == d)
+        q += (q & 1);         /* exact half: go to the even quotient */
+    return q;
+}
+
+static float clampf(float v, float lo, float hi)
+{
+    return v < lo ? lo : (v > hi ? hi : v);
+}
+
+static int64_t clampi(int64_t v, int64_t lo, int64_t hi)
+{
+    return v < lo ? lo : (v > hi ? hi : v);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Activations: per-token symmetric INT8 by absolute maximum.               */
+/* The QServe talk summary ("Precision Data Flow and Activation             */
+/* Quantization Fusion") makes every linear layer take 8-bit inputs; the    */
+/* per-token absmax rule with 127 levels per side is the method's stated   */
+/* activation quantizer.  Readings: fp32 scale a/127 by IEEE division,      */
+/* code = rint(x / scale) (ties to even), clamped to [-127, 127]; an        */
+/* all-zero token gets scale 0 and all-zero codes.                          */
+/* x is fp16 bits, row stride ldx elements.                                 */
+/* ------------------------------------------------------------------------ */
+void orc_quantize_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                      int8_t *qx, float *s_a)
+{
+    for (int64_t m = 0; m < M; m++) {
+        float a = 0.0f;
+        for (int64_t k = 0; k < K; k++) {
+            float v = fabsf(orc_f16_to_f32(x[m * ldx + k]));
+            if (v > a)
+                a = v;
+        }
+        float s = a / 127.0f;
+        s_a[m] = s;
+        for (int64_t k = 0; k < K; k++) {
+            float q = 0.0f;
+            if (a != 0.0f) {
+                float t = orc_f16_to_f32(x[m * ldx + k]) / s;
+                q = clampf(rintf(t), -127.0f, 127.0f);
+            }
+            qx[m * K + k] = (int8_t)q;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Weights, level 1: per output channel, symmetric INT8 inside the          */
+/* protective range [-119, 119], with an fp16 scale (QServe talk summary,   */
+/* "Progressive Group Quantization for W4A8 GEMM"; Lecture 15 notes, 15.6,  */
+/* level 1 of the two-level scheme: int8 envelope, fp16 channel scales).    */
+/* Readings: s0 = fp16(absmax / 119) (fp32 division, then RNE to fp16);     */
+/* codes divide by the stored fp16 value; rint ties to even; a zero row     */
+/* has s0 = 0 and zero codes.                                               */
+/* ------------------------------------------------------------------------ */
+#define ORC_PROTECT 119
+
+void orc_weights_level1(const float *w, int64_t N, int64_t K,
+                        int8_t *q8, uint16_t *s0)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        float a = 0.0f;
+        for (int64_t k = 0; k < K; k++) {
+            float v = fabsf(w[n * K + k]);
+            if (v > a)
+                a = v;
+        }
+        uint16_t h = orc_f32_to_f16(a / (float)ORC_PROTECT);
+        s0[n] = h;
+        float s = orc_f16_to_f32(h);
+        for (int64_t k = 0; k < K; k++) {
+            float q = 0.0f;
+            if (s != 0.0f)
+                q = clampf(rintf(w[n * K + k] / s), -(float)ORC_PROTECT,
+                           (float)ORC_PROTECT);
+            q8[n * K + k] = (int8_t)q;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Weights, level 2: per group of 128 consecutive k in one output row,      */
+/* asymmetric UINT4 with an integer scale s1 and a zero point z             */
+/* (QServe talk summary, "Progressive Group Quantization for W4A8 GEMM":    */
+/* INT8 -> INT4 per group; Lecture 15 notes, 15.6: int8 scales per g=128    */
+/* group; QFactory notes 2.1: min and max map to the ends of the integer    */
+/* range).  All integer arithmetic.  Readings:                              */
+/*   lo = min(0, min q8), hi = max(0, max q8)   (range contains 0, so the  */
+/*                                              zero point is in [0, 15])  */
+/*   s1 = max(1, ceil((hi - lo) / 15))          (integer scale covering the */
+/*                                              whole range)               */
+/*   z  = rne(-lo / s1)                                                     */
+/*   q4 = clamp(rne(q8 / s1) + z, 0, 15)                                    */
+/* q4 is returned one code per byte, [N, K]; s1, z are [N, K/128].          */
+/* ------------------------------------------------------------------------ */
+#define ORC_GROUP 128
+
+void orc_weights_level2(const int8_t *q8, int64_t N, int64_t K,
+                        uint8_t *q4, uint8_t *s1, uint8_t *z)
+{
+    int64_t G = K / ORC_GROUP;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t g = 0; g < G; g++) {
+            const int8_t *src = q8 + n * K + g * ORC_GROUP;
+            int64_t lo = 0, hi = 0;
+            for (int64_t i = 0; i < ORC_GROUP; i++) {
+                if (src[i] < lo)
+                    lo = src[i];
+                if (src[i] > hi)
+                    hi = src[i];
+            }
+            int64_t D = hi - lo;
+            int64_t s = (D + 14) / 15;          /* ceil(D / 15) */
+            if (s < 1)
+                s = 1;
+            int64_t zz = orc_rne_div(-lo, s);
+            s1[n * G + g] = (uint8_t)s;
+            z[n * G + g] = (uint8_t)zz;
+            for (int64_t i = 0; i < ORC_GROUP; i++) {
+                int64_t c = clampi(orc_rne_div(src[i], s) + zz, 0, 15);
+                q4[n * K + g * ORC_GROUP + i] = (uint8_t)c;
+            }
+        }
+    }
+}
+
+/* Canonical packed form: [N, K/2] bytes, k even in the low nibble. */
+void orc_pack_q4(const uint8_t *q4, int64_t N, int64_t K, uint8_t *packed)
+{
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k += 2)
+            packed[n * (K / 2) + k / 2] =
+                (uint8_t)((q4[n * K + k] & 0xF) | ((q4[n * K + k + 1] & 0xF) << 4));
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dequantization UINT4 -> INT8 by subtraction after multiplication         */
+/* (QServe talk summary, "Challenges and Design Details of QServe GEMM      */
+/* Kernel": multiply by the scale, then subtract the precomputed            */
+/* zero*scale; Lecture 15 notes, 15.6).  Equal, as integers, to             */
+/* (q4 - z) * s1 (QFactory notes 2.1).                                       */
+/* Returns the number of reconstructions outside [-127, 127] or with       */
+/* q4*s1 or z*s1 above 240 (0 when the protective range holds).            */
+/* ------------------------------------------------------------------------ */
+int64_t orc_dequant_i8(const uint8_t *q4, const uint8_t *s1, const uint8_t *z,
+                       int64_t N, int64_t K, int8_t *r)
+{
+    int64_t G = K / ORC_GROUP, bad = 0;
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t k = 0; k < K; k++) {
+            int64_t s = s1[n * G + k / ORC_GROUP];
+            int64_t zz = z[n * G + k / ORC_GROUP];
+            int64_t prod = (int64_t)q4[n * K + k] * s;
+            int64_t zs = zz * s;
+            int64_t v = prod - zs;
+            if (v < -127 || v > 127 || prod > 240 || zs > 240)
+                bad++;
+            r[n * K + k] = (int8_t)clampi(v, -128, 127);
+        }
+    }
+    return bad;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exact integer contraction: acc[m,n] = sum_k qx[m,k] * r[n,k] in int64,   */
+/* stored as int32 (the main loop runs on INT8 matrix units with an INT32   */
+/* accumulator: QServe talk summary, "Quantized Matrix Multiplication       */
+/* (GEMM) Kernel on GPUs").  Returns the number of sums outside int32.      */
+/* ------------------------------------------------------------------------ */
+int64_t orc_gemm_acc(const int8_t *qx, const int8_t *r, int64_t M, int64_t N,
+                     int64_t K, int32_t *acc)
+{
+    int64_t bad = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t m = 0; m < M; m++) {
+            int64_t sum = 0;
+            for (int64_t k = 0; k < K; k++)
+                sum += (int64_t)qx[m * K + k] * (int64_t)r[n * K + k];
+            if (sum > INT32_MAX || sum < INT32_MIN)
+                bad++;
+            acc[m * N + n] = (int32_t)sum;
+        }
+    }
+    return bad;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Epilogue: y = fp16( (float(acc) * s_a[m]) * float(s0[n]) ), fp32, in    */
+/* that order (per-channel and per-token scales applied after the main      */
+/* loop: QServe talk summary, "Progressive Group Quantization for W4A8      */
+/* GEMM" and "Quantized Matrix Multiplication (GEMM) Kernel on GPUs").      */
+/* ------------------------------------------------------------------------ */
+void orc_epilogue(const int32_t *acc, const float *s_a, const uint16_t *s0,
+                  int64_t M, int64_t N, uint16_t *y)
+{
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t n = 0; n < N; n++) {
+            float t = (float)acc[m * N + n];
+            t = t * s_a[m];
+            t = t * orc_f16_to_f32(s0[n]);
+            y[m * N + n] = orc_f32_to_f16(t);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* The whole serving-time path for one call, from fp16 activations and the  */
+/* level-2 weight form to fp16 outputs.  Used to time the oracle.           */
+/* r (int8 [N,K]) is caller-provided scratch.  Returns the number of        */
+/* threads used by the contraction.                                         */
+/* ------------------------------------------------------------------------ */
+int orc_linear(const uint16_t *x, int64_t M, int64_t K, const uint8_t *q4,
+               const uint8_t *s1, const uint8_t *z, const uint16_t *s0,
+               int64_t N, int8_t *qx, float *s_a, int8_t *r, int32_t *acc,
+               uint16_t *y)
+{
+    orc_quantize_act(x, M, K, K, qx, s_a);
+    orc_dequant_i8(q4, s1, z, N, K, r);
+    orc_gemm_acc(qx, r, M, N, K, acc);
+    orc_epilogue(acc, s_a, s0, M, N, y);
+    return orc_num_threads();
+}
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

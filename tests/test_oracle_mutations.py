@@ -1,0 +1,50 @@
+"""The pins catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a copy of the oracle's C source (a wrong tie
+rule, a dropped factor, a transposed index, a wrong constant, ...), builds it
+on the CPU, and runs the pin suite against that build.  Every mutant must make
+at least one pin fail.  Nothing here touches a GPU.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "w4a8_oracle.c")
+
+MUTANTS = [
+    ("integer scale rounded instead of ceil", "int64_t s = (D + 14) / 15;", "int64_t s = (D + 7) / 15;"),
+    ("zero point truncated", "int64_t zz = orc_rne_div(-lo, s);", "int64_t zz = (-lo) / s;"),
+    ("activation ties away from zero", "q = clampf(rintf(t), -127.0f, 127.0f);",
+     "q = clampf(roundf(t), -127.0f, 127.0f);"),
+    ("wrong protective range", "orc_f32_to_f16(a / (float)ORC_PROTECT)", "orc_f32_to_f16(a / 127.0f)"),
+    ("zero not multiplied by the scale", "int64_t v = prod - zs;", "int64_t v = prod - zz;"),
+    ("transposed weight index", "(int64_t)r[n * K + k];", "(int64_t)r[k * N + n];"),
+    ("channel scale dropped", "t = t * orc_f16_to_f32(s0[n]);", "t = t * 1.0f;"),
+    ("token scale dropped", "t = t * s_a[m];", "t = t * 1.0f;"),
+    ("group range without zero", "int64_t lo = 0, hi = 0;", "int64_t lo = 127, hi = -128;"),
+    ("integer ties always up", "q += (q & 1);", "q += 1;"),
+    ("activation levels 128", "float s = a / 127.0f;", "float s = a / 128.0f;"),
+    ("group index off by one", "int64_t s = s1[n * G + k / ORC_GROUP];",
+     "int64_t s = s1[n * G + (k + 1) / ORC_GROUP % G];"),
+    ("fp16 rounding truncates", "double n = rint(ldexp(a, 10 - e));", "double n = floor(ldexp(a, 10 - e));"),
+    ("level-1 codes unclamped sign flip", "q8[n * K + k] = (int8_t)q;", "q8[n * K + k] = (int8_t)(-q);"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_reject_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation site not found: %s" % old
+    mutant = tmp_path / "mutant.c"
+    mutant.write_text(src.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+                    "-o", str(lib), str(mutant), "-lm"], check=True)
+    env = dict(os.environ, W4A8_ORACLE_LIB=str(lib))
+    res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                          os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                         cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert res.returncode != 0, "mutant '%s' passed every pin:\n%s" % (name, res.stdout[-2000:])

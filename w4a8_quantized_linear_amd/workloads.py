@@ -1,0 +1,98 @@
+"""Seeded synthetic inputs for the W4A8 linear layer.
+
+This module only draws random numbers; it holds none of the method's
+arithmetic, and both the CPU oracle's callers and the GPU path's callers take
+their inputs from it.
+
+Recipe (one per workload family; every draw is seeded):
+  * generator: numpy PCG64 seeded by SeedSequence([0x57A8, family, K, N, tensor_id(, M)])
+    with tensor_id 0 = weights, 1 = activations (M appended), 2 = outlier channels;
+  * weights: fp32, N(0, 0.02) -- or, for the heavy-tailed family, Student-t with
+    nu = 4 scaled to the same std (divide by the population std sqrt(2));
+  * activations: fp32 N(0, 1) with a fixed set of outlier channels (the same
+    channels for every token) multiplied by a large factor, then rounded to fp16.
+    Four channels x50 by default; 1% of channels x100 for the heavy-tailed family.
+The outlier structure follows the pages' description of LLM activations: a
+small fraction of feature channels, fixed across tokens, tens to hundreds of
+times larger than the rest.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Tuple
+
+import numpy as np
+
+SEED_ROOT = 0x57A8
+
+
+@dataclasses.dataclass(frozen=True)
+class Family:
+    """One workload family (value distributions + shapes)."""
+    index: int
+    name: str
+    ms: Tuple[int, ...]
+    kns: Tuple[Tuple[int, int], ...]       # (K, N) pairs
+    w_dist: str = "normal"                 # "normal" | "student_t4"
+    n_outlier: int = 4                     # or -1 for 1% of K
+    outlier_scale: float = 50.0
+
+
+FAMILIES: List[Family] = [
+    Family(0, "tiny: M=16, K=512, N=512", (16,), ((512, 512),)),
+    Family(1, "7B decode: hidden 4096, MLP 11008", (1, 8, 32),
+           ((4096, 12288), (4096, 4096), (4096, 22016), (11008, 4096))),
+    Family(2, "batched decode M=256, K=4096, N=11008, heavy-tailed weights", (256,),
+           ((4096, 11008),), w_dist="student_t4", n_outlier=-1, outlier_scale=100.0),
+    Family(3, "prefill M=4096", (4096,), ((4096, 11008), (11008, 4096))),
+    Family(4, "70B layers: hidden 8192, MLP 28672", (1, 64, 512),
+           ((8192, 10240), (8192, 57344), (28672, 8192))),
+]
+
+# The benchmark's workload: the 7B MLP projection K=4096 -> N=11008, swept over
+# token counts from one decode token to a 4096-token prefill.
+SWEEP_K, SWEEP_N = 4096, 11008
+SWEEP_MS = (1, 8, 32, 256, 4096)
+
+
+def _rng(family: int, K: int, N: int, tensor_id: int, *extra: int) -> np.random.Generator:
+    ss = np.random.SeedSequence([SEED_ROOT, family, K, N, tensor_id, *extra])
+    return np.random.Generator(np.random.PCG64(ss))
+
+
+def weights(family: int, K: int, N: int) -> np.ndarray:
+    """fp32 weights [N, K] (independent of M)."""
+    fam = FAMILIES[family]
+    rng = _rng(family, K, N, 0)
+    if fam.w_dist == "student_t4":
+        w = rng.standard_t(4.0, size=(N, K)) * (0.02 / np.sqrt(2.0))
+        return w.astype(np.float32)
+    w = rng.standard_normal((N, K), dtype=np.float32)
+    w *= np.float32(0.02)
+    return w
+
+
+def outlier_channels(family: int, K: int, N: int) -> np.ndarray:
+    fam = FAMILIES[family]
+    n_out = fam.n_outlier if fam.n_outlier >= 0 else int(round(0.01 * K))
+    n_out = min(n_out, K)
+    rng = _rng(family, K, N, 2)
+    return np.sort(rng.choice(K, n_out, replace=False))
+
+
+def activations(family: int, M: int, K: int, N: int) -> np.ndarray:
+    """fp16 activations [M, K] with fixed outlier channels."""
+    fam = FAMILIES[family]
+    rng = _rng(family, K, N, 1, M)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    cols = outlier_channels(family, K, N)
+    x[:, cols] *= np.float32(fam.outlier_scale)
+    return x.astype(np.float16)
+
+
+def all_cases():
+    """Every (family, M, K, N) the families name."""
+    for fam in FAMILIES:
+        for (K, N) in fam.kns:
+            for M in fam.ms:
+                yield fam.index, M, K, N
