@@ -1,0 +1,170 @@
+"""Host-only checks of libw4a8: it loads, exports every entry point the header
+declares, reports sizes, and rejects bad arguments before launching anything.
+
+No test here makes a compute call: every call below fails host-side
+validation.  They are skipped where a GPU is visible (the same checks run in
+the CPU suite), so a regression in validation can never launch a kernel on
+fake pointers.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a8.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from w4a8_quantized_linear_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from w4a8_quantized_linear_amd import build
+        build.build(verbose=False)
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("quantize_weights_w4g128", "quantize_act_per_token_i8", "gemm_w4a8"):
+        assert n in names
+    from w4a8_quantized_linear_amd import _lib
+    assert sorted(_lib.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from w4a8_quantized_linear_amd import _lib
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if " T " in l)
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings_and_version(lib):
+    from w4a8_quantized_linear_amd import _lib
+    for st in (0, -1, -2, -3, -4, -5, 7):
+        assert len(_lib.status_string(st)) > 0
+    assert re.match(r"^\d+\.\d+\.\d+$", _lib.version())
+
+
+def test_size_queries(lib):
+    from w4a8_quantized_linear_amd import _lib
+    # codes + one parameter byte per (channel, group), groups padded to a multiple of 4
+    assert _lib.w4a8_packed_weight_bytes(512, 512) == 512 * 256 + 512 * 4
+    assert _lib.w4a8_packed_weight_bytes(4096, 11008) == 4096 * 5504 + 4096 * 88
+    assert _lib.w4a8_packed_weight_bytes(16, 128) == 16 * 64 + 16 * 4
+    for N, K in ((0, 128), (16, 0), (15, 128), (16, 100), (-16, 128)):
+        assert _lib.w4a8_packed_weight_bytes(N, K) == 0
+    assert _lib.gemm_w4a8_workspace_bytes(0, 512, 512) == 0
+    assert _lib.gemm_w4a8_workspace_bytes(1, 15, 512) == 0
+    for (M, N, K) in ((1, 4096, 4096), (32, 22016, 4096), (4096, 11008, 4096)):
+        ws = _lib.gemm_w4a8_workspace_bytes(M, N, K)
+        assert ws == 0 or ws >= M * N * 4
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+needs_no_gpu = pytest.mark.skipif(_gpu_visible(), reason="validation checks use fake pointers; run on the CPU host only")
+
+A = ctypes.c_void_p(0x10000)      # 16-byte aligned fake pointers (never dereferenced)
+B = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x30008)    # misaligned
+NUL = None
+S = ctypes.c_void_p(0)
+
+
+@needs_no_gpu
+def test_quantize_weights_validation(lib):
+    f = lib.quantize_weights_w4g128
+    assert f(NUL, 16, 128, A, A, A, A, S) == -1
+    assert f(A, 16, 128, NUL, A, A, A, S) == -1
+    assert f(A, 16, 128, A, A, NUL, A, S) == -1           # s1 without z
+    assert f(A, 16, 128, A, A, A, NUL, S) == -1
+    assert f(A, 16, 100, A, NUL, NUL, A, S) == -2
+    assert f(A, 20, 128, A, NUL, NUL, A, S) == -2
+    assert f(A, 0, 128, A, NUL, NUL, A, S) == -2
+    assert f(A, 16, -128, A, NUL, NUL, A, S) == -2
+    assert f(MIS, 16, 128, A, NUL, NUL, A, S) == -3
+    assert f(A, 16, 128, MIS, NUL, NUL, A, S) == -3
+
+
+@needs_no_gpu
+def test_unpack_validation(lib):
+    f = lib.w4a8_unpack_weights
+    assert f(NUL, 16, 128, A, A, A, S) == -1
+    assert f(A, 16, 128, A, NUL, A, S) == -1
+    assert f(A, 16, 127, A, A, A, S) == -2
+    assert f(A, 16, 128, MIS, A, A, S) == -3
+
+
+@needs_no_gpu
+def test_act_quant_validation(lib):
+    f = lib.quantize_act_per_token_i8
+    assert f(A, 0, 128, 128, A, A, S) == 0                 # M == 0 is a no-op
+    assert f(NUL, 0, 128, 128, NUL, NUL, S) == 0
+    assert f(A, -1, 128, 128, A, A, S) == -2
+    assert f(A, 4, 100, 100, A, A, S) == -2
+    assert f(A, 4, 128, 64, A, A, S) == -2                 # ldx < K
+    assert f(A, 4, 128, 130, A, A, S) == -2                # ldx not a multiple of 8
+    assert f(NUL, 4, 128, 128, A, A, S) == -1
+    assert f(A, 4, 128, 128, NUL, A, S) == -1
+    assert f(A, 4, 128, 128, A, NUL, S) == -1
+    assert f(MIS, 4, 128, 128, A, A, S) == -3
+    assert f(A, 4, 128, 128, A, MIS, S) == -3
+
+
+@needs_no_gpu
+def test_gemm_validation(lib):
+    f = lib.gemm_w4a8
+    ok = dict(qx=A, sa=A, w=A, s0=A, M=1, N=16, K=128, y=B, acc=NUL, ws=NUL, wsb=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["qx"], a["sa"], a["w"], a["s0"], a["M"], a["N"], a["K"], a["y"], a["acc"],
+                 a["ws"], a["wsb"], S)
+
+    assert call(M=0, qx=NUL, y=NUL) == 0
+    assert call(M=-1) == -2
+    assert call(N=0) == -2
+    assert call(N=24) == -2
+    assert call(K=192) == -2
+    assert call(qx=NUL) == -1
+    assert call(sa=NUL) == -1
+    assert call(w=NUL) == -1
+    assert call(s0=NUL) == -1
+    assert call(y=NUL) == -1
+    assert call(qx=MIS) == -3
+    assert call(y=MIS) == -3
+    assert call(acc=MIS) == -3
+    # a split-K shape without (or with too small) a workspace
+    from w4a8_quantized_linear_amd import _lib
+    need = _lib.gemm_w4a8_workspace_bytes(1, 4096, 4096)
+    assert need > 0
+    assert call(N=4096, K=4096) == -4
+    assert call(N=4096, K=4096, ws=A, wsb=need - 1) == -4
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    from w4a8_quantized_linear_amd import _lib
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.load()

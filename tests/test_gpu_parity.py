@@ -1,0 +1,295 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact on every integer result (qx, s_a, s0, s1, z, the packed codes read
+back through w4a8_unpack_weights, and the INT32 accumulators of the real GEMM
+main loop); the fp16 outputs within |dy| <= 1e-2 + 1e-3 |y_ref|.  Small cases
+are compared element by element in full; at the full workload sizes the GPU
+runs the whole problem in the benchmark's launch configuration and the oracle
+recomputes a sample of rows (token rows and channel rows are independent).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle as orc
+from gpu_helpers import (assert_y_close, case_inputs, dev, f16_bits, gpu_weights,
+                         oracle_weights_rows, sample_rows, say, to_dev, to_host)
+from w4a8_quantized_linear_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from w4a8_quantized_linear_amd import _lib
+    _lib.load()           # raises if the HIP library is not built: no fallback
+    yield
+
+
+KN_ALL = sorted({(K, N) for fam in workloads.FAMILIES for (K, N) in fam.kns})
+FAMILY_OF = {}
+for fam in workloads.FAMILIES:
+    for kn in fam.kns:
+        FAMILY_OF.setdefault(kn, fam.index)
+
+
+# ---------------------------------------------------------------------------
+# activation quantizer
+# ---------------------------------------------------------------------------
+ACT_CASES = [(0, 16, 512, 512), (1, 1, 4096, 4096), (1, 8, 4096, 12288), (1, 32, 11008, 4096),
+             (2, 256, 4096, 11008), (3, 4096, 4096, 11008), (3, 4096, 11008, 4096),
+             (4, 512, 28672, 8192), (4, 64, 8192, 57344)]
+
+
+@pytest.mark.parametrize("family,M,K,N", ACT_CASES)
+def test_act_quant_bit_exact(family, M, K, N):
+    from w4a8_quantized_linear_amd import quantize_act_per_token_i8
+    say("act quant family=%d M=%d K=%d" % (family, M, K))
+    x = workloads.activations(family, M, K, N)
+    qx, sa = quantize_act_per_token_i8(to_dev(x))
+    qx_ref, sa_ref = orc.quantize_act(x)
+    assert np.array_equal(to_host(qx), qx_ref)
+    assert np.array_equal(to_host(sa).view(np.uint32), sa_ref.view(np.uint32))
+
+
+def test_act_quant_edges_and_row_stride():
+    import torch
+    from w4a8_quantized_linear_amd import quantize_act_per_token_i8
+    K = 256
+    x = np.zeros((6, K), np.float16)
+    x[1, 7] = -3.0                                   # single non-zero
+    x[2, :5] = [3, -1.5, 0.75, -0.375, 1]            # worked-example token (ties)
+    x[3, :8] = [127, -63.5, 31.25, 0.5, -0.5, 1.5, -127, 2.5]
+    x[4] = np.float16(65504.0)                       # largest fp16
+    x[5, ::2] = np.float16(2.0 ** -24)               # smallest subnormal
+    say("act quant edges")
+    qx, sa = quantize_act_per_token_i8(to_dev(x))
+    qx_ref, sa_ref = orc.quantize_act(x)
+    assert np.array_equal(to_host(qx), qx_ref)
+    assert np.array_equal(to_host(sa).view(np.uint32), sa_ref.view(np.uint32))
+    # row stride larger than K: quantize the left 512 columns of a 1024-wide buffer
+    wide = workloads.activations(0, 16, 1024, 512)
+    t = to_dev(wide)[:, :512]
+    assert t.stride(0) == 1024
+    qx2, sa2 = quantize_act_per_token_i8(t)
+    qx2_ref, sa2_ref = orc.quantize_act(np.ascontiguousarray(wide[:, :512]))
+    assert np.array_equal(to_host(qx2), qx2_ref)
+    assert np.array_equal(to_host(sa2).view(np.uint32), sa2_ref.view(np.uint32))
+    # M = 0 is a no-op
+    e = torch.empty((0, 128), dtype=torch.float16, device=dev())
+    quantize_act_per_token_i8(e)
+
+
+# ---------------------------------------------------------------------------
+# weight quantizer + packing (read back through the unpack entry point)
+# ---------------------------------------------------------------------------
+def _check_weights(w, wq, rows, where):
+    from w4a8_quantized_linear_amd import w4a8_unpack_weights
+    import torch
+    N, K = w.shape
+    ref = oracle_weights_rows(w, rows)
+    q4c, s1u, zu = w4a8_unpack_weights(wq["wpacked"], N, K)
+    idx = torch.from_numpy(rows).to(dev())
+    assert np.array_equal(f16_bits(wq["s0"][idx]), ref["s0"]), where + " s0"
+    assert np.array_equal(to_host(wq["s1"][idx]), ref["s1"]), where + " s1"
+    assert np.array_equal(to_host(wq["z"][idx]), ref["z"]), where + " z"
+    assert np.array_equal(to_host(s1u[idx]), ref["s1"]), where + " unpacked s1"
+    assert np.array_equal(to_host(zu[idx]), ref["z"]), where + " unpacked z"
+    assert np.array_equal(to_host(q4c[idx]), orc.pack_q4(ref["q4"])), where + " codes"
+
+
+@pytest.mark.parametrize("K,N", KN_ALL)
+def test_weight_quant_bit_exact(K, N):
+    import torch
+    fam = FAMILY_OF[(K, N)]
+    say("weight quant family=%d K=%d N=%d" % (fam, K, N))
+    w = workloads.weights(fam, K, N)
+    wq = gpu_weights(w)
+    rows = sample_rows(N, 512, seed=K + N)
+    _check_weights(w, wq, rows, "K=%d N=%d" % (K, N))
+    del wq
+    torch.cuda.empty_cache()
+
+
+def test_weight_quant_edges():
+    say("weight quant edges")
+    K = 384                                          # three groups (odd group count)
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((48, K)) * 0.02).astype(np.float32)
+    w[0] = 0                                         # zero channel
+    w[1] = np.abs(w[1])                              # one-signed channels
+    w[2] = -np.abs(w[2])
+    w[3, :128] = (np.arange(128) - 119) * 2.0 ** -10  # worked example row (group 0)
+    w[4] *= 0.05                                     # subnormal fp16 channel scale
+    w[5, 128:256] = 0                                # an all-zero group
+    w[6] = 0
+    w[6, 200] = 1.0                                  # a single non-zero weight
+    wq = gpu_weights(w)
+    _check_weights(w, wq, np.arange(48), "edges")
+
+
+# ---------------------------------------------------------------------------
+# GEMM
+# ---------------------------------------------------------------------------
+def _gemm_case(family, M, K, N, row_sample=None, wq=None, w=None):
+    import torch
+    from w4a8_quantized_linear_amd import gemm_w4a8, quantize_act_per_token_i8
+    say("gemm family=%d M=%d K=%d N=%d" % (family, M, K, N))
+    if w is None:
+        w = workloads.weights(family, K, N)
+    x = workloads.activations(family, M, K, N)
+    if wq is None:
+        wq = gpu_weights(w)
+    qx, sa = quantize_act_per_token_i8(to_dev(x))
+    acc = torch.empty((M, N), dtype=torch.int32, device=dev())
+    y = gemm_w4a8(qx, sa, wq["wpacked"], wq["s0"], N, acc_out=acc)
+    torch.cuda.synchronize()
+    rows = np.arange(M) if row_sample is None else sample_rows(M, row_sample, seed=M + K)
+    # oracle: quantized weights of every channel, activations of the sampled tokens
+    ref_w = orc.quantize_weights(w)
+    out = orc.linear(np.ascontiguousarray(x[rows]), ref_w)
+    idx = torch.from_numpy(rows).to(dev())
+    acc_g = to_host(acc[idx])
+    assert np.array_equal(acc_g, out["acc"]), "INT32 accumulators differ (%d of %d)" % (
+        (acc_g != out["acc"]).sum(), acc_g.size)
+    assert_y_close(f16_bits(y[idx]), out["y"], "M=%d K=%d N=%d" % (M, K, N))
+    return y, acc
+
+
+def test_gemm_tiny_family0():
+    _gemm_case(0, 16, 512, 512)
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+@pytest.mark.parametrize("K,N", workloads.FAMILIES[1].kns)
+def test_gemm_7b_decode(M, K, N):
+    _gemm_case(1, M, K, N)
+
+
+def test_gemm_batched_decode_m256():
+    _gemm_case(2, 256, 4096, 11008, row_sample=96)
+
+
+@pytest.mark.parametrize("K,N", workloads.FAMILIES[3].kns)
+def test_gemm_prefill_m4096(K, N):
+    _gemm_case(3, 4096, K, N, row_sample=48)
+
+
+@pytest.mark.parametrize("K,N", workloads.FAMILIES[4].kns)
+def test_gemm_70b_layers(K, N):
+    import torch
+    w = workloads.weights(4, K, N)
+    wq = gpu_weights(w)
+    for M in workloads.FAMILIES[4].ms:
+        _gemm_case(4, M, K, N, row_sample=(None if M == 1 else 12), wq=wq, w=w)
+    del wq
+    torch.cuda.empty_cache()
+
+
+EDGE = [(1, 128, 16), (5, 128, 48), (17, 384, 48), (33, 256, 80), (63, 640, 32), (65, 384, 16),
+        (100, 512, 144), (16, 384, 4096)]
+
+
+@pytest.mark.parametrize("M,K,N", EDGE)
+def test_gemm_edge_shapes(M, K, N):
+    import torch
+    from w4a8_quantized_linear_amd import gemm_w4a8, quantize_act_per_token_i8
+    say("gemm edge M=%d K=%d N=%d" % (M, K, N))
+    rng = np.random.default_rng(M * 1000 + K + N)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    x[M // 2] = 0                                      # an all-zero token
+    wq = gpu_weights(w)
+    qx, sa = quantize_act_per_token_i8(to_dev(x))
+    acc = torch.empty((M, N), dtype=torch.int32, device=dev())
+    y = gemm_w4a8(qx, sa, wq["wpacked"], wq["s0"], N, acc_out=acc)
+    out = orc.linear(x, orc.quantize_weights(w))
+    assert np.array_equal(to_host(acc), out["acc"])
+    assert_y_close(f16_bits(y), out["y"], "edge")
+    assert not to_host(acc)[M // 2].any()
+
+
+def _with_plan(plan, fn):
+    old = os.environ.get("W4A8_DECODE_PLAN")
+    os.environ["W4A8_DECODE_PLAN"] = plan
+    try:
+        return fn()
+    finally:
+        if old is None:
+            del os.environ["W4A8_DECODE_PLAN"]
+        else:
+            os.environ["W4A8_DECODE_PLAN"] = old
+
+
+@pytest.mark.parametrize("M", [1, 8, 32, 64])
+def test_splitk_equals_no_splitk_and_is_deterministic(M):
+    import torch
+    from w4a8_quantized_linear_amd import _lib, gemm_w4a8, quantize_act_per_token_i8
+    K, N = 4096, 4096
+    say("split-k equality M=%d" % M)
+    w = workloads.weights(1, K, N)
+    x = workloads.activations(1, M, K, N)
+    wq = gpu_weights(w)
+    qx, sa = quantize_act_per_token_i8(to_dev(x))
+    mt = 1 if M <= 16 else (2 if M <= 32 else 4)
+    results = []
+    for plan in ("%d,2,1" % mt, "%d,2,4" % mt, "%d,1,16" % mt, "%d,4,3" % mt, "%d,2,4" % mt):
+        def run():
+            acc = torch.empty((M, N), dtype=torch.int32, device=dev())
+            y = gemm_w4a8(qx, sa, wq["wpacked"], wq["s0"], N, acc_out=acc)
+            torch.cuda.synchronize()
+            return f16_bits(y), to_host(acc)
+        results.append(_with_plan(plan, run))
+    for y, acc in results[1:]:
+        assert np.array_equal(acc, results[0][1])
+        assert np.array_equal(y, results[0][0])
+    # the workspace is left zeroed
+    ws = _lib._ws_cache.get(torch.device(dev()))
+    if ws is not None:
+        assert int(ws.count_nonzero()) == 0
+
+
+def test_workspace_reuse_with_smaller_second_call():
+    import torch
+    from w4a8_quantized_linear_amd import _lib, gemm_w4a8, quantize_act_per_token_i8
+    K, N = 4096, 4096
+    w = workloads.weights(1, K, N)
+    wq = gpu_weights(w)
+    ref_w = orc.quantize_weights(w)
+    for M in (32, 1, 8):
+        say("workspace reuse M=%d" % M)
+        x = workloads.activations(1, M, K, N)
+        qx, sa = quantize_act_per_token_i8(to_dev(x))
+        acc = torch.empty((M, N), dtype=torch.int32, device=dev())
+        gemm_w4a8(qx, sa, wq["wpacked"], wq["s0"], N, acc_out=acc)
+        out = orc.linear(x, ref_w)
+        assert np.array_equal(to_host(acc), out["acc"])
+    ws = _lib._ws_cache.get(torch.device(dev()))
+    assert ws is None or int(ws.count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("plan", ["1,2,1", "1,4,2", "2,4,1", "4,2,3"])
+def test_gemm_n_tail_tiles(plan):
+    import torch
+    from w4a8_quantized_linear_amd import gemm_w4a8, quantize_act_per_token_i8
+    M, K, N = 20, 768, 48          # 3 n-tiles: the last workgroup's tile group is partial
+    say("gemm n-tail plan=%s" % plan)
+    rng = np.random.default_rng(99)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    wq = gpu_weights(w)
+    qx, sa = quantize_act_per_token_i8(to_dev(x))
+    acc = torch.zeros((M, N), dtype=torch.int32, device=dev())
+
+    def run():
+        y = gemm_w4a8(qx, sa, wq["wpacked"], wq["s0"], N, acc_out=acc)
+        torch.cuda.synchronize()
+        return y
+    y = _with_plan(plan, run)
+    out = orc.linear(x, orc.quantize_weights(w))
+    assert np.array_equal(to_host(acc), out["acc"])
+    assert_y_close(f16_bits(y), out["y"], "n-tail")

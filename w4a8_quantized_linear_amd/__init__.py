@@ -1,1 +1,25 @@
-"""MI355X-native W4A8 quantized linear layer (placeholder; binding added with the library)."""
+"""MI355X-native (gfx950) W4A8 quantized linear layer.
+
+The kernels live in libw4a8.so (HIP, built in-tree by
+``python -m w4a8_quantized_linear_amd.build``); this package is its ctypes
+binding.  The library is loaded on first use, so importing the package (or its
+``workloads`` / ``accounting`` helpers) does not need a GPU.
+"""
+from ._lib import (  # noqa: F401
+    W4A8Error,
+    gemm_w4a8,
+    gemm_w4a8_workspace_bytes,
+    linear,
+    quantize_act_per_token_i8,
+    quantize_weights_w4g128,
+    status_string,
+    version,
+    w4a8_packed_weight_bytes,
+    w4a8_unpack_weights,
+)
+
+__all__ = [
+    "W4A8Error", "gemm_w4a8", "gemm_w4a8_workspace_bytes", "linear", "quantize_act_per_token_i8",
+    "quantize_weights_w4g128", "status_string", "version", "w4a8_packed_weight_bytes",
+    "w4a8_unpack_weights",
+]

@@ -1,0 +1,193 @@
+"""ctypes binding of libw4a8 (include/w4a8.h), with the same entry-point names.
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the computation runs in the library's kernels.  If
+the library is not built the calls raise; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libw4a8.so")
+
+W4A8_OK = 0
+W4A8_E_NULL = -1
+W4A8_E_SHAPE = -2
+W4A8_E_ALIGN = -3
+W4A8_E_WORKSPACE = -4
+W4A8_E_HIP = -5
+
+# every symbol include/w4a8.h declares
+EXPORTS = (
+    "w4a8_status_string", "w4a8_version", "w4a8_packed_weight_bytes",
+    "quantize_weights_w4g128", "w4a8_unpack_weights", "quantize_act_per_token_i8",
+    "gemm_w4a8_workspace_bytes", "gemm_w4a8",
+)
+
+_lock = threading.Lock()
+_lib = None
+
+
+class W4A8Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (where, status_string(status), status))
+
+
+def load() -> ctypes.CDLL:
+    """Load libw4a8.so from the package directory (raises if it is not built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libw4a8.so is not built (run `python -m w4a8_quantized_linear_amd.build`): %s"
+                              % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I64, SZ, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+        lib.w4a8_status_string.argtypes = [I32]
+        lib.w4a8_status_string.restype = ctypes.c_char_p
+        lib.w4a8_version.argtypes = []
+        lib.w4a8_version.restype = ctypes.c_char_p
+        lib.w4a8_packed_weight_bytes.argtypes = [I64, I64]
+        lib.w4a8_packed_weight_bytes.restype = SZ
+        lib.quantize_weights_w4g128.argtypes = [P, I64, I64, P, P, P, P, P]
+        lib.quantize_weights_w4g128.restype = I32
+        lib.w4a8_unpack_weights.argtypes = [P, I64, I64, P, P, P, P]
+        lib.w4a8_unpack_weights.restype = I32
+        lib.quantize_act_per_token_i8.argtypes = [P, I64, I64, I64, P, P, P]
+        lib.quantize_act_per_token_i8.restype = I32
+        lib.gemm_w4a8_workspace_bytes.argtypes = [I64, I64, I64]
+        lib.gemm_w4a8_workspace_bytes.restype = SZ
+        lib.gemm_w4a8.argtypes = [P, P, P, P, I64, I64, I64, P, P, P, SZ, P]
+        lib.gemm_w4a8.restype = I32
+        _lib = lib
+        return lib
+
+
+def status_string(st: int) -> str:
+    return load().w4a8_status_string(int(st)).decode()
+
+
+def version() -> str:
+    return load().w4a8_version().decode()
+
+
+def _check(st: int, where: str):
+    if st != W4A8_OK:
+        raise W4A8Error(st, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# --------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# --------------------------------------------------------------------------
+def w4a8_packed_weight_bytes(N: int, K: int) -> int:
+    return int(load().w4a8_packed_weight_bytes(N, K))
+
+
+def gemm_w4a8_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(load().gemm_w4a8_workspace_bytes(M, N, K))
+
+
+def quantize_weights_w4g128(w, *, canonical: bool = True, stream=None):
+    """fp32 weights [N, K] on the GPU -> dict(wpacked uint8, s0 int16 (fp16 bits)[, s1, z uint8 [N, K/128]])."""
+    import torch
+    assert w.dtype == torch.float32 and w.dim() == 2 and w.is_contiguous()
+    N, K = w.shape
+    nbytes = w4a8_packed_weight_bytes(N, K)
+    if nbytes == 0:
+        _check(W4A8_E_SHAPE, "quantize_weights_w4g128")
+    dev = w.device
+    out = {"N": N, "K": K,
+           "wpacked": torch.empty(nbytes, dtype=torch.uint8, device=dev),
+           "s0": torch.empty(N, dtype=torch.int16, device=dev)}
+    if canonical:
+        out["s1"] = torch.empty((N, K // 128), dtype=torch.uint8, device=dev)
+        out["z"] = torch.empty((N, K // 128), dtype=torch.uint8, device=dev)
+    st = load().quantize_weights_w4g128(_ptr(w), N, K, _ptr(out["wpacked"]), _ptr(out.get("s1")),
+                                        _ptr(out.get("z")), _ptr(out["s0"]), _stream(stream))
+    _check(st, "quantize_weights_w4g128")
+    return out
+
+
+def w4a8_unpack_weights(wpacked, N: int, K: int, *, stream=None):
+    """Device weight stream -> (q4 canonical [N, K/2] uint8, s1 [N, K/128], z [N, K/128])."""
+    import torch
+    dev = wpacked.device
+    q4 = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    s1 = torch.empty((N, K // 128), dtype=torch.uint8, device=dev)
+    z = torch.empty((N, K // 128), dtype=torch.uint8, device=dev)
+    st = load().w4a8_unpack_weights(_ptr(wpacked), N, K, _ptr(q4), _ptr(s1), _ptr(z), _stream(stream))
+    _check(st, "w4a8_unpack_weights")
+    return q4, s1, z
+
+
+def quantize_act_per_token_i8(x, *, qx=None, s_a=None, stream=None):
+    """fp16 activations [M, K] (row stride x.stride(0)) -> (qx int8 [M, K], s_a fp32 [M])."""
+    import torch
+    assert x.dtype == torch.float16 and x.dim() == 2 and x.stride(1) == 1
+    M, K = x.shape
+    if qx is None:
+        qx = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if s_a is None:
+        s_a = torch.empty((M,), dtype=torch.float32, device=x.device)
+    st = load().quantize_act_per_token_i8(_ptr(x), M, K, x.stride(0), _ptr(qx), _ptr(s_a), _stream(stream))
+    _check(st, "quantize_act_per_token_i8")
+    return qx, s_a
+
+
+_ws_lock = threading.Lock()
+_ws_cache = {}
+
+
+def workspace(device, nbytes: int):
+    """A zeroed split-K workspace of at least nbytes on `device`, cached per device.
+
+    The kernels leave it zeroed after every call, so it is cleared only when
+    first allocated (or grown).  Calls that share it must be stream-ordered."""
+    import torch
+    if nbytes == 0:
+        return None
+    key = torch.device(device)
+    with _ws_lock:
+        buf = _ws_cache.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=key)
+            _ws_cache[key] = buf
+        return buf
+
+
+def gemm_w4a8(qx, s_a, wpacked, s0, N: int, *, y=None, acc_out=None, ws=None, stream=None):
+    """INT8 activations [M, K] x packed weights -> fp16 y [M, N] (and INT32 acc_out if given)."""
+    import torch
+    M, K = qx.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=qx.device)
+    need = gemm_w4a8_workspace_bytes(M, N, K)
+    if ws is None:
+        ws = workspace(qx.device, need)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    st = load().gemm_w4a8(_ptr(qx), _ptr(s_a), _ptr(wpacked), _ptr(s0), M, N, K, _ptr(y),
+                          _ptr(acc_out), _ptr(ws), wsb, _stream(stream))
+    _check(st, "gemm_w4a8")
+    return y
+
+
+def linear(x, wq: dict, *, acc_out=None, stream=None):
+    """The serving-time call: quantize the fp16 activations, then the W4A8 GEMM."""
+    qx, s_a = quantize_act_per_token_i8(x, stream=stream)
+    return gemm_w4a8(qx, s_a, wq["wpacked"], wq["s0"], wq["N"], acc_out=acc_out, stream=stream)

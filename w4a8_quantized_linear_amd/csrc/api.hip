@@ -1,0 +1,120 @@
+// api.hip -- the C ABI of libw4a8 (declared in include/w4a8.h): argument
+// checks on the host, then launches on the caller's stream.  Every argument
+// error is reported before anything is enqueued; nothing here allocates.
+#include <cstdint>
+
+#include "w4a8.h"
+#include "w4a8_internal.h"
+
+using namespace w4a8;
+
+namespace {
+
+constexpr int64_t kMaxM = (int64_t)65535 * 64;   // grid z limit of the GEMM (64 tokens per block)
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool weight_shape_ok(int64_t N, int64_t K)
+{
+    return N > 0 && K > 0 && K % kGroup == 0 && N % kTileN == 0 && N <= ((int64_t)1 << 31) &&
+           K <= ((int64_t)1 << 24);
+}
+
+w4a8_status hip_status(hipError_t e) { return e == hipSuccess ? W4A8_OK : W4A8_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *w4a8_status_string(w4a8_status st)
+{
+    switch (st) {
+    case W4A8_OK: return "ok";
+    case W4A8_E_NULL: return "a required pointer is NULL";
+    case W4A8_E_SHAPE: return "invalid shape (need M >= 0, N > 0, K > 0, K % 128 == 0, N % 16 == 0, ldx >= K, ldx % 8 == 0)";
+    case W4A8_E_ALIGN: return "a device pointer is not 16-byte aligned";
+    case W4A8_E_WORKSPACE: return "workspace missing or smaller than gemm_w4a8_workspace_bytes()";
+    case W4A8_E_HIP: return "HIP launch or runtime error";
+    }
+    return "unknown status";
+}
+
+const char *w4a8_version(void) { return "0.1.0"; }
+
+size_t w4a8_packed_weight_bytes(int64_t N, int64_t K)
+{
+    if (!weight_shape_ok(N, K))
+        return 0;
+    return (size_t)(code_bytes(N, K) + param_bytes(N, K));
+}
+
+w4a8_status quantize_weights_w4g128(const float *w, int64_t N, int64_t K, void *wpacked,
+                                    uint8_t *s1, uint8_t *z, uint16_t *s0_fp16,
+                                    hipStream_t stream)
+{
+    if (!w || !wpacked || !s0_fp16 || ((s1 == nullptr) != (z == nullptr)))
+        return W4A8_E_NULL;
+    if (!weight_shape_ok(N, K))
+        return W4A8_E_SHAPE;
+    if (!aligned16(w) || !aligned16(wpacked) || !aligned16(s0_fp16) ||
+        (s1 && (!aligned16(s1) || !aligned16(z))))
+        return W4A8_E_ALIGN;
+    return hip_status(launch_weight_quant(w, N, K, static_cast<uint8_t *>(wpacked), s1, z,
+                                          s0_fp16, stream));
+}
+
+w4a8_status w4a8_unpack_weights(const void *wpacked, int64_t N, int64_t K, uint8_t *q4_canon,
+                                uint8_t *s1, uint8_t *z, hipStream_t stream)
+{
+    if (!wpacked || !q4_canon || !s1 || !z)
+        return W4A8_E_NULL;
+    if (!weight_shape_ok(N, K))
+        return W4A8_E_SHAPE;
+    if (!aligned16(wpacked) || !aligned16(q4_canon) || !aligned16(s1) || !aligned16(z))
+        return W4A8_E_ALIGN;
+    return hip_status(launch_weight_unpack(static_cast<const uint8_t *>(wpacked), N, K, q4_canon,
+                                           s1, z, stream));
+}
+
+w4a8_status quantize_act_per_token_i8(const uint16_t *x_fp16, int64_t M, int64_t K, int64_t ldx,
+                                      int8_t *qx, float *s_a, hipStream_t stream)
+{
+    if (M < 0 || K <= 0 || K % kGroup != 0 || ldx < K || ldx % 8 != 0 || M > ((int64_t)1 << 31) - 1)
+        return W4A8_E_SHAPE;
+    if (M == 0)
+        return W4A8_OK;
+    if (!x_fp16 || !qx || !s_a)
+        return W4A8_E_NULL;
+    if (!aligned16(x_fp16) || !aligned16(qx) || !aligned16(s_a))
+        return W4A8_E_ALIGN;
+    return hip_status(launch_act_quant(x_fp16, M, K, ldx, qx, s_a, stream));
+}
+
+size_t gemm_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || M > kMaxM || !weight_shape_ok(N, K))
+        return 0;
+    return plan_gemm(M, N, K).ws_bytes;
+}
+
+w4a8_status gemm_w4a8(const int8_t *qx, const float *s_a, const void *wpacked,
+                      const uint16_t *s0_fp16, int64_t M, int64_t N, int64_t K, uint16_t *y_fp16,
+                      int32_t *acc_out, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (M < 0 || M > kMaxM || !weight_shape_ok(N, K))
+        return W4A8_E_SHAPE;
+    if (M == 0)
+        return W4A8_OK;
+    if (!qx || !s_a || !wpacked || !s0_fp16 || !y_fp16)
+        return W4A8_E_NULL;
+    if (!aligned16(qx) || !aligned16(s_a) || !aligned16(wpacked) || !aligned16(s0_fp16) ||
+        !aligned16(y_fp16) || (acc_out && !aligned16(acc_out)) || (ws && !aligned16(ws)))
+        return W4A8_E_ALIGN;
+    const GemmPlan p = plan_gemm(M, N, K);
+    if (p.ws_bytes > 0 && (ws == nullptr || ws_bytes < p.ws_bytes))
+        return W4A8_E_WORKSPACE;
+    return hip_status(launch_gemm(p, qx, s_a, static_cast<const uint8_t *>(wpacked), s0_fp16, M,
+                                  N, K, y_fp16, acc_out, ws, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// w4a8_internal.h -- layout constants and launcher declarations shared by the
+// HIP translation units of libw4a8 (private to the library).
+//
+// Device weight stream (written by quantize_weights_w4g128, read by the GEMM):
+//
+//   [ codes: N*K/2 bytes ][ group parameters: N * G4 bytes ]
+//
+// Codes.  The weight matrix is cut into tiles of 16 output channels x 128 k
+// (one quantization group), 1024 bytes each, stored n-tile major:
+//   tile (nt, g) at byte (nt * G + g) * 1024.
+// Inside a tile, lane l of a 64-wide wave owns bytes [16 l, 16 l + 16): the 32
+// codes of channel n = 16 nt + (l & 15) that the two 16x16x64 INT8 MFMA
+// fragments of that lane need, for k-block kb = l >> 4.  Byte b of dword d
+// holds, in its low nibble, the code of k = 128 g + 16 kb + 4 d + b (first
+// 64-k half of the group) and, in its high nibble, the code of
+// k = 128 g + 64 + 16 kb + 4 d + b (second half).  So one 16-byte load per
+// lane is one MFMA B-fragment pair, `x & 0x0F0F0F0F` is the first fragment's
+// dword and `(x >> 4) & 0x0F0F0F0F` the second's.  This is the
+// compute-aware reordering of the QServe talk summary ("Challenges and
+// Design Details of QServe GEMM Kernel") redone for the gfx950 MFMA operand
+// shape: the weights sit in HBM in exactly the order each lane consumes them.
+//
+// Group parameters.  One byte per (n, g): (s1 - 1) | (z << 4).  G is padded
+// to G4 = round_up(G, 4) and the bytes of four consecutive groups of one
+// channel form one dword:
+//   byte ((nt * (G4/4) + g/4) * 16 + (n & 15)) * 4 + (g & 3).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a8 {
+
+constexpr int kGroup = 128;
+constexpr int kTileN = 16;
+constexpr int kTileBytes = 1024;
+
+__host__ __device__ inline int64_t num_groups(int64_t K) { return K / kGroup; }
+__host__ __device__ inline int64_t groups_padded(int64_t K) { return (K / kGroup + 3) / 4 * 4; }
+__host__ __device__ inline int64_t code_bytes(int64_t N, int64_t K) { return N * K / 2; }
+__host__ __device__ inline int64_t param_bytes(int64_t N, int64_t K) { return N * groups_padded(K); }
+__host__ __device__ inline int64_t param_index(int64_t n, int64_t g, int64_t G4)
+{
+    return ((n / 16 * (G4 / 4) + g / 4) * 16 + (n & 15)) * 4 + (g & 3);
+}
+
+// ---- launchers (defined in the kernel translation units) ----------------
+hipError_t launch_act_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                            int8_t *qx, float *s_a, hipStream_t st);
+
+hipError_t launch_weight_quant(const float *w, int64_t N, int64_t K, uint8_t *stream_bytes,
+                               uint8_t *s1, uint8_t *z, uint16_t *s0, hipStream_t st);
+
+hipError_t launch_weight_unpack(const uint8_t *stream_bytes, int64_t N, int64_t K,
+                                uint8_t *q4_canon, uint8_t *s1, uint8_t *z, hipStream_t st);
+
+// GEMM plan: which kernel, its tile shape and the split-K factor.
+struct GemmPlan {
+    int kind;        // 0 = decode (weights streamed, split-K), 1 = prefill (LDS tiles)
+    int mt;          // 16-row m-tiles per workgroup (decode)
+    int nt;          // 16-column n-tiles per workgroup (decode)
+    int splitk;      // number of K slices (decode)
+    int64_t m_blocks;
+    int64_t n_blocks;
+    size_t ws_bytes; // workspace needed (0 if none)
+};
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
+
+hipError_t launch_gemm(const GemmPlan &p, const int8_t *qx, const float *s_a,
+                       const uint8_t *stream_bytes, const uint16_t *s0, int64_t M, int64_t N,
+                       int64_t K, uint16_t *y, int32_t *acc_out, void *ws, hipStream_t st);
+
+}  // namespace w4a8
