@@ -1,0 +1,210 @@
+"""Benchmark of the W4A8 linear layer on one MI355X.
+
+Workload: the 7B MLP projection K=4096 -> N=11008, swept over token counts
+M in {1, 8, 32, 256, 4096} (one decode token up to a 4096-token prefill).  One
+step = for every M, the per-token activation quantization followed by the W4A8
+GEMM, exactly what a serving engine runs per linear layer (the weights were
+quantized offline, once).  Inputs are seeded synthetic tensors resident in HBM
+before timing starts; every GEMM call reads a different copy of the packed
+weights, rotating through enough copies to exceed the 256 MB Infinity Cache,
+so weight bytes really come from HBM.
+
+Prints one JSON line: whole-step throughput (TOPS), the roofline of the
+dominant kernel (the M=4096 GEMM), per-M kernel figures, and the CPU oracle
+timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W4A8 GEMM TOPS + achieved HBM GB/s (% roofline), K=4096 N=11008 M=1..4096"
+K_DIM, N_DIM = 4096, 11008
+MS = (1, 8, 32, 256, 4096)
+FAMILY = 3          # weight / activation value distributions of the prefill family
+ROTATE_BYTES = 1 << 30
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=50, help="calls per per-M kernel timing loop")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="token rows per M in the oracle sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the path runs on a single MI355X); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from w4a8_quantized_linear_amd import _lib, accounting as A, workloads
+    from w4a8_quantized_linear_amd import (gemm_w4a8, quantize_act_per_token_i8,
+                                           quantize_weights_w4g128)
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    _lib.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs (host-generated, seeded), resident in HBM before timing ----
+    w_np = workloads.weights(FAMILY, K_DIM, N_DIM)
+    wq = quantize_weights_w4g128(torch.from_numpy(w_np).to(dev), canonical=False)
+    wbytes = wq["wpacked"].numel()
+    nrot = max(2, math.ceil(ROTATE_BYTES / wbytes))
+    wcopies = [wq["wpacked"]] + [wq["wpacked"].clone() for _ in range(nrot - 1)]
+    s0 = wq["s0"]
+    xs, qxs, sas, ys = {}, {}, {}, {}
+    for M in MS:
+        xs[M] = torch.from_numpy(workloads.activations(FAMILY, M, K_DIM, N_DIM)).to(dev)
+        qxs[M] = torch.empty((M, K_DIM), dtype=torch.int8, device=dev)
+        sas[M] = torch.empty((M,), dtype=torch.float32, device=dev)
+        ys[M] = torch.empty((M, N_DIM), dtype=torch.float16, device=dev)
+    ws = _lib.workspace(dev, max(_lib.gemm_w4a8_workspace_bytes(M, N_DIM, K_DIM) for M in MS))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    counter = [0]
+    dom_M = MS[-1]
+    ev_pairs = []
+
+    def step(record):
+        for M in MS:
+            quantize_act_per_token_i8(xs[M], qx=qxs[M], s_a=sas[M], stream=stream)
+            wp = wcopies[counter[0] % nrot]
+            counter[0] += 1
+            if record and M == dom_M:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                gemm_w4a8(qxs[M], sas[M], wp, s0, N_DIM, y=ys[M], ws=ws, stream=stream)
+                e1.record(stream)
+                ev_pairs.append((e0, e1))
+            else:
+                gemm_w4a8(qxs[M], sas[M], wp, s0, N_DIM, y=ys[M], ws=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps ------------------------------
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step(True)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    dom_us = 1e3 * sum(a.elapsed_time(b) for a, b in ev_pairs) / len(ev_pairs)
+
+    ops_step = sum(A.gemm_ops(M, N_DIM, K_DIM) for M in MS)
+    value = ops_step / (ms_per_step * 1e-3) / 1e12
+
+    # ---- per-M kernel figures: back-to-back calls, events on the stream ----
+    per_m = []
+    for M in MS:
+        rec = {"M": M}
+        for kind in ("act_quant", "gemm"):
+            reps = args.reps
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for r in range(reps):
+                if kind == "act_quant":
+                    quantize_act_per_token_i8(xs[M], qx=qxs[M], s_a=sas[M], stream=stream)
+                else:
+                    gemm_w4a8(qxs[M], sas[M], wcopies[r % nrot], s0, N_DIM, y=ys[M], ws=ws,
+                              stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = 1e3 * e0.elapsed_time(e1) / reps
+            if kind == "act_quant":
+                nbytes = A.act_quant_bytes(M, K_DIM)
+                rec["act_quant_us"] = round(us, 3)
+                rec["act_quant_GBps"] = round(nbytes / us * 1e-3, 1)
+            else:
+                nbytes = A.gemm_bytes(M, N_DIM, K_DIM)
+                ops = A.gemm_ops(M, N_DIM, K_DIM)
+                rec["gemm_us"] = round(us, 3)
+                rec["gemm_GBps"] = round(nbytes / us * 1e-3, 1)
+                rec["gemm_TOPS"] = round(ops / us * 1e-6, 2)
+                rec["hbm_frac"] = round(nbytes / us * 1e-3 / (A.MI355X_HBM_BYTES_PER_S / 1e9), 4)
+                rec["mfma_frac"] = round(ops / us * 1e-6 / (A.MI355X_INT8_OPS_PER_S / 1e12), 4)
+        per_m.append(rec)
+
+    # ---- roofline of the dominant kernel (M=4096 GEMM, MFMA-bound) ---------
+    dom_ops = A.gemm_ops(dom_M, N_DIM, K_DIM)
+    achieved = dom_ops / (dom_us * 1e-6) / 1e12
+    peak = A.MI355X_INT8_OPS_PER_S / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": "gemm_w4a8 M=%d N=%d K=%d" % (dom_M, N_DIM, K_DIM),
+                "avg_us": round(dom_us, 3), "ops_per_launch": dom_ops}
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "W4A8 linear K=4096 N=11008 (7B MLP projection), one step = "
+                               "act-quant + GEMM at each M in [1, 8, 32, 256, 4096]",
+                   "K": K_DIM, "N": N_DIM, "M": list(MS), "group": 128,
+                   "weight_copies": nrot, "wall_s": round(wall, 4)},
+        "roofline": roofline,
+        "per_m": per_m,
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w_np, args.cpu_rows)
+
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w_np, rows):
+    """The oracle, as it stands, on a bounded sample: every M of the sweep with at most `rows` token rows."""
+    import numpy as np
+
+    import oracle as orc
+    from w4a8_quantized_linear_amd import accounting as A, workloads
+    wq = orc.quantize_weights(w_np)
+    total_ops, total_s, threads, sample = 0, 0.0, 1, []
+    for M in MS:
+        m = min(M, rows)
+        x = workloads.activations(FAMILY, M, K_DIM, N_DIM)[:m]
+        bufs = orc.linear_timed_buffers(m, N_DIM, K_DIM)
+        t0 = time.perf_counter()
+        threads = orc.linear_into(x, wq, bufs)
+        total_s += time.perf_counter() - t0
+        total_ops += A.gemm_ops(m, N_DIM, K_DIM)
+        sample.append(m)
+    return {"value": round(total_ops / total_s / 1e12, 6), "unit": "TOPS", "cores": threads,
+            "kind": "oracle", "seconds": round(total_s, 3),
+            "sample": "oracle act-quant + dequant + int64 GEMM + epilogue, K=4096 N=11008, token rows %s "
+                      "(first rows of each M of the sweep)" % sample}
+
+
+if __name__ == "__main__":
+    main()

@@ -36,12 +36,14 @@ def f16_bits(t):
 
 
 def sample_rows(n, count, seed):
-    """Sorted sample of row indices that always includes the first and last 16 rows."""
+    """Sorted sample of `count` row indices that includes the first and last few rows."""
     if n <= count:
         return np.arange(n)
     rng = np.random.default_rng(seed)
-    pick = set(range(16)) | set(range(n - 16, n))
-    pick |= set(rng.choice(n, count - len(pick), replace=False).tolist())
+    edge = min(16, count // 4)
+    pick = set(range(edge)) | set(range(n - edge, n))
+    rest = np.setdiff1d(np.arange(n), np.array(sorted(pick), dtype=np.int64))
+    pick |= set(rng.choice(rest, count - len(pick), replace=False).tolist())
     return np.array(sorted(pick))
 
 

@@ -237,7 +237,11 @@ def test_splitk_equals_no_splitk_and_is_deterministic(M):
     qx, sa = quantize_act_per_token_i8(to_dev(x))
     mt = 1 if M <= 16 else (2 if M <= 32 else 4)
     results = []
-    for plan in ("%d,2,1" % mt, "%d,2,4" % mt, "%d,1,16" % mt, "%d,4,3" % mt, "%d,2,4" % mt):
+    plans = ["%d,2,1" % mt, "%d,2,4" % mt, "%d,1,16" % mt, "%d,4,3" % mt, "%d,2,4" % mt,
+             "%d,1,1,8,2" % mt, "%d,1,2,4,2" % mt]
+    if mt == 1:
+        plans += ["1,1,1,4,4,1", "1,2,1,4,2,1", "1,1,3,8,2,1", "1,2,2,4,4,1", "1,1,1,4,4,0"]
+    for plan in plans:
         def run():
             acc = torch.empty((M, N), dtype=torch.int32, device=dev())
             y = gemm_w4a8(qx, sa, wq["wpacked"], wq["s0"], N, acc_out=acc)
@@ -272,7 +276,7 @@ def test_workspace_reuse_with_smaller_second_call():
     assert ws is None or int(ws.count_nonzero()) == 0
 
 
-@pytest.mark.parametrize("plan", ["1,2,1", "1,4,2", "2,4,1", "4,2,3"])
+@pytest.mark.parametrize("plan", ["1,2,1", "1,4,2", "2,4,1", "4,2,3", "1,2,1,4,4,1", "1,2,2,8,2,1"])
 def test_gemm_n_tail_tiles(plan):
     import torch
     from w4a8_quantized_linear_amd import gemm_w4a8, quantize_act_per_token_i8

@@ -28,7 +28,7 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-fno-fast-math", "-ffp-contract=fast-honor-pragmas",
+    "-fno-fast-math", "-ffp-contract=off",
     "-Wall", "-Wno-unused-function",
     "-I", INCLUDE, "-I", CSRC,
 ]

@@ -14,10 +14,11 @@ constexpr int64_t kMaxM = (int64_t)65535 * 64;   // grid z limit of the GEMM (64
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The GEMM addresses the weight stream with 32-bit buffer offsets.
 bool weight_shape_ok(int64_t N, int64_t K)
 {
-    return N > 0 && K > 0 && K % kGroup == 0 && N % kTileN == 0 && N <= ((int64_t)1 << 31) &&
-           K <= ((int64_t)1 << 24);
+    return N > 0 && K > 0 && K % kGroup == 0 && N % kTileN == 0 && N <= ((int64_t)1 << 30) &&
+           K <= ((int64_t)1 << 24) && code_bytes(N, K) + param_bytes(N, K) <= 0x7FFFFFFF;
 }
 
 w4a8_status hip_status(hipError_t e) { return e == hipSuccess ? W4A8_OK : W4A8_E_HIP; }

@@ -3,16 +3,18 @@
 // The QFactory reading notes (6.1-6.2) make tile shapes compile-time template
 // parameters and pick an instantiation per shape; here the pick is a small
 // deterministic rule of (M, N, K), so the workspace size a caller queries and
-// the plan gemm_w4a8 launches always agree.  W4A8_DECODE_PLAN="mt,nt,splitk"
-// overrides the decode choice (for tuning sweeps).
-#include <cstdlib>
+// the plan gemm_w4a8 launches always agree.  W4A8_DECODE_PLAN=
+// "mt,nt,splitk[,waves[,depth[,xstage]]]" overrides the decode choice (for
+// tuning sweeps); an override that names no instantiated variant is ignored.
 #include <cstdio>
+#include <cstdlib>
 
 #include "w4a8_internal.h"
 
 namespace w4a8 {
 
-size_t decode_lds_bytes(int64_t M, int64_t K, int mt, int nt, int splitk);
+bool decode_variant_exists(int mt, int nt, int waves, int depth, bool xs);
+size_t decode_lds_bytes(const GemmPlan &p, int64_t M, int64_t K);
 hipError_t launch_gemm_decode(const GemmPlan &p, const int8_t *qx, const float *s_a,
                               const uint8_t *stream_bytes, const uint16_t *s0, int64_t M,
                               int64_t N, int64_t K, uint16_t *y, int32_t *acc_out, void *ws,
@@ -20,13 +22,18 @@ hipError_t launch_gemm_decode(const GemmPlan &p, const int8_t *qx, const float *
 
 namespace {
 
-constexpr int64_t kTargetBlocks = 1024;    // four 4-wave workgroups per CU
-
 size_t ws_size(int64_t M, int64_t N, int splitk, int64_t tiles)
 {
     if (splitk <= 1)
         return 0;
     return ((size_t)M * N * 4 + 255) / 256 * 256 + (size_t)tiles * 4;
+}
+
+bool launchable(const GemmPlan &p, int64_t M, int64_t K)
+{
+    const size_t lds = decode_lds_bytes(p, M, K);
+    return decode_variant_exists(p.mt, p.nt, p.waves, p.depth, p.xstage) && lds > 0 &&
+           lds <= 160 * 1024;
 }
 
 }  // namespace
@@ -37,28 +44,43 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     p.kind = 0;
     const int64_t ntiles = N / kTileN;
     const int64_t G = num_groups(K);
+    const int64_t P = (G + 1) / 2;
+    // Rule fitted to rocprofv3 sweeps of the 7B decode shapes on MI355X: one
+    // n-tile per workgroup for up to 16 tokens (the activation rows staged in
+    // LDS when they fit), wider n-blocks for 17..32 tokens so that each
+    // activation operand feeds more weight tiles.
     p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     p.m_blocks = (M + 16 * p.mt - 1) / (16 * p.mt);
-    p.nt = ntiles >= 512 ? 4 : (ntiles >= 128 ? 2 : 1);
+    p.nt = 1;
+    if (p.mt == 2)
+        p.nt = ntiles >= 512 ? 4 : (ntiles >= 384 ? 2 : 1);
     p.n_blocks = (ntiles + p.nt - 1) / p.nt;
-    int64_t blocks = p.n_blocks * p.m_blocks;
-    int64_t sk = (kTargetBlocks + blocks - 1) / blocks;
-    int64_t sk_max = G / 8 > 0 ? G / 8 : 1;          // at least one pair of groups per wave
-    if (sk > sk_max)
-        sk = sk_max;
-    if (sk < 1)
-        sk = 1;
-    p.splitk = (int)sk;
+    p.splitk = 1;
+    p.waves = 4;
+    p.depth = 2;
+    p.xstage = false;
+    if (p.mt == 1) {
+        GemmPlan q = p;
+        q.xstage = true;
+        if (launchable(q, M, K) && decode_lds_bytes(q, M, K) <= 64 * 1024)
+            p = q;
+    }
 
     if (const char *env = std::getenv("W4A8_DECODE_PLAN")) {
-        int mt = 0, nt = 0, s = 0;
-        if (std::sscanf(env, "%d,%d,%d", &mt, &nt, &s) == 3 && (mt == 1 || mt == 2 || mt == 4) &&
-            (nt == 1 || nt == 2 || nt == 4) && s >= 1 && s <= G) {
-            p.mt = mt;
-            p.nt = nt;
-            p.splitk = s;
-            p.m_blocks = (M + 16 * mt - 1) / (16 * mt);
-            p.n_blocks = (ntiles + nt - 1) / nt;
+        int mt = 0, nt = 0, s = 0, wv = 4, dp = 2, xs = 0;
+        int got = std::sscanf(env, "%d,%d,%d,%d,%d,%d", &mt, &nt, &s, &wv, &dp, &xs);
+        GemmPlan q = p;
+        q.mt = mt;
+        q.nt = nt;
+        q.splitk = s;
+        q.waves = wv;
+        q.depth = dp;
+        q.xstage = xs != 0;
+        if (got >= 3 && nt > 0 && s >= 1 && s <= P && (mt == 1 || mt == 2 || mt == 4)) {
+            q.m_blocks = (M + 16 * mt - 1) / (16 * mt);
+            q.n_blocks = (ntiles + nt - 1) / nt;
+            if (launchable(q, M, K))
+                p = q;
         }
     }
     p.ws_bytes = ws_size(M, N, p.splitk, p.m_blocks * p.n_blocks);
@@ -70,9 +92,12 @@ hipError_t launch_gemm(const GemmPlan &p, const int8_t *qx, const float *s_a,
                        int64_t K, uint16_t *y, int32_t *acc_out, void *ws, hipStream_t st)
 {
     if (std::getenv("W4A8_LOG"))
-        std::fprintf(stderr, "w4a8: gemm M=%lld N=%lld K=%lld kind=%d mt=%d nt=%d splitk=%d grid=%lldx%dx%lld\n",
+        std::fprintf(stderr,
+                     "w4a8: gemm M=%lld N=%lld K=%lld kind=%d mt=%d nt=%d splitk=%d waves=%d "
+                     "depth=%d xstage=%d grid=%lldx%dx%lld\n",
                      (long long)M, (long long)N, (long long)K, p.kind, p.mt, p.nt, p.splitk,
-                     (long long)p.n_blocks, p.splitk, (long long)p.m_blocks);
+                     p.waves, p.depth, (int)p.xstage, (long long)p.n_blocks, p.splitk,
+                     (long long)p.m_blocks);
     return launch_gemm_decode(p, qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, ws, st);
 }
 

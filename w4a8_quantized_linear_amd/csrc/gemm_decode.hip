@@ -9,22 +9,29 @@
 //   acc[m,n] = sum_k qx[m,k] * (q4[n,k] s1 - z s1)        (exact INT32)
 //   y[m,n]   = fp16((float(acc) * s_a[m]) * float(s0[n]))
 //
-// Work decomposition.  A 256-thread workgroup (4 waves) owns NT n-tiles of 16
-// channels, up to MT m-tiles of 16 tokens, and one K slice (split-K).  The
-// four waves split the slice into runs of group pairs.  Each wave streams its
-// weight tiles from HBM straight into registers with 16-byte non-temporal
-// loads, together with the matching activation fragments (tiny, L2-resident)
-// and the group-parameter dword, two groups per buffer, double buffered.
-// Every load is unconditional (addresses clamped at the edges) so the compiler
-// emits exact vmcnt waits and keeps both buffers in flight.  Each 16-byte lane
-// load is the fragment pair of two v_mfma_i32_16x16x64_i8 (the device layout
-// puts the codes in that order), so there is no shuffling: mask/shift, one
-// packed 16-bit multiply-add and one xor per 4 weights, then the MFMA with the
-// weights as the A operand (rows = channels) and the tokens as the B operand.
-// The four waves' partial accumulators are summed through LDS; with split-K
+// Work decomposition.  A workgroup of WAVES waves owns NT n-tiles of 16
+// channels, up to MT m-tiles of 16 tokens, and one K slice (split-K across
+// workgroups is optional).  The waves split the slice into runs of group
+// pairs.  At the start every thread issues its share of the small loads --
+// the slice's group-parameter bytes, the epilogue scales and, for few
+// tokens, the tokens' activation rows -- then the first DEPTH pairs of its
+// wave's weight tiles, and only then stores the small data into LDS: the
+// group parameters pre-decoded into the two 16-bit constants the rebuild
+// needs, and the activation rows.  So the weight stream starts at once and
+// its loads are the only vector-memory traffic of the main loop (activation
+// operands for more tokens are loaded with the weights instead).  Weight
+// tiles are read with 16-byte buffer loads (scalar base and offset, one
+// per-lane offset register) DEPTH pairs ahead of use; every load is
+// unconditional, so the compiler's vmcnt waits are exact.  Each 16-byte lane
+// load is the operand pair of two v_mfma_i32_16x16x64_i8 (the device layout
+// puts the codes in that order): mask/shift, one packed 16-bit multiply-add
+// and one xor per 4 weights, then the MFMA with the weights as the A operand
+// (rows = channels) and the tokens as the B operand (columns = tokens; columns
+// past M carry whatever row their lane loads and are never stored).  The
+// waves' partial accumulators meet in LDS through LDS atomics; with split-K
 // the workgroups of one tile add their partials into an INT32 workspace with
-// atomics (exact, so any arrival order gives the same bits) and the last to
-// arrive applies the epilogue and clears its part of the workspace.
+// device atomics (exact, so any arrival order gives the same bits) and the
+// last to arrive applies the epilogue and clears its part of the workspace.
 //
 // The packed rebuild.  For a dword holding four codes b in [0, 15], one per
 // byte, v_pk_mad_u16(x, s1, C) with C = 257 (128 - z s1) mod 2^16 computes in
@@ -35,6 +42,7 @@
 // the overflow hazard the QServe talk summary attributes to subtraction
 // before multiplication.
 #include <algorithm>
+
 #include "w4a8_internal.h"
 
 namespace w4a8 {
@@ -43,8 +51,8 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kBufFlags = 0x00020000;   // raw buffer resource, dword 3 (gfx9 family)
+constexpr int kLoadNT = 2;              // non-temporal (streaming) load policy
 
 __device__ inline uint32_t rebuild4(uint32_t nib, us2 S, us2 C)
 {
@@ -53,9 +61,20 @@ __device__ inline uint32_t rebuild4(uint32_t nib, us2 S, us2 C)
     return __builtin_bit_cast(uint32_t, v) ^ 0x80808080u;
 }
 
-__device__ inline v4i load_nt16(const uint8_t *p)
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *p, int64_t bytes)
 {
-    return __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
+    const int64_t lim = bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)lim, kBufFlags);
+}
+
+__device__ inline int sgpr(int64_t v) { return __builtin_amdgcn_readfirstlane((int)v); }
+
+// decoded constants of one group: s1 in the low half, 257 (128 - z s1) in the high half
+__device__ inline uint32_t decode_param(uint32_t p)
+{
+    const uint32_t s1 = (p & 15u) + 1u;
+    const uint32_t c16 = ((128u - (p >> 4) * s1) * 257u) & 0xFFFFu;
+    return s1 | (c16 << 16);
 }
 
 struct DecodeArgs {
@@ -72,60 +91,146 @@ struct DecodeArgs {
     uint32_t *ws_cnt;    // one counter per (m-block, n-block)
 };
 
-// One double-buffer slot: the loads of one pair of groups (2 x 128 k).
-template <int MT, int NT>
+// One ring slot: the loads of one pair of groups (2 x 128 k).
+template <int MT, int NT, bool XS>
 struct Chunk {
-    v4i w[NT][2];       // weight fragments: 16 B per lane per (n-tile, group)
-    uint32_t p[NT];     // group-parameter dword (four groups of this lane's channel)
-    v4i x[MT][2][2];    // activation fragments: (m-tile, group, 64-k half)
+    v4i w[NT][2];                    // weight operands: 16 B per lane per (n-tile, group)
+    v4i x[XS ? 1 : MT][2][2];        // activation operands when not staged in LDS
 };
 
-template <int MT, int NT>
-__global__ __launch_bounds__(kThreads) void gemm_decode_kernel(DecodeArgs a)
+template <int MT, int NT, int WAVES, int DEPTH, bool XS>
+__global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
 {
     extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int kThreads = 64 * WAVES;
 
     const int tid = threadIdx.x;
-    const int wv = tid >> 6;
     const int l = tid & 63;
-    const int c = l & 15;          // weight row (channel) fed / token column read by this lane
-    const int kb = l >> 4;         // 16-byte k-block within a 64-k MFMA step
+    const int c = l & 15;                    // channel row (A) / token column (B) of this lane
+    const int kb = l >> 4;                   // 16-byte k-block within a 64-k MFMA step
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    const int64_t G = num_groups(a.K);
-    const int64_t G4 = groups_padded(a.K);
-    const int64_t P = (G + 1) / 2;                 // pairs of groups
-    const int64_t ntiles_total = a.N / kTileN;
-    const int64_t nt0 = (int64_t)blockIdx.x * NT;
-    const int s = blockIdx.y;
+    // index arithmetic in 32 bits (shapes are validated on the host: K < 2^24,
+    // N < 2^30, weight stream < 2^31 bytes); 64-bit division would cost
+    // hundreds of instructions before the first load
+    const int K = (int)a.K;
+    const int G = K / kGroup;
+    const int G4 = (G + 3) / 4 * 4;
+    const int P = (G + 1) / 2;               // pairs of groups
+    const int ntiles = (int)(a.N / kTileN);
+    const int nt0 = (int)blockIdx.x * NT;
     const int64_t m0 = (int64_t)blockIdx.z * (16 * MT);
-    const int mrows = (int)min<int64_t>(16 * MT, a.M - m0);   // real token rows in this block
+    const int mrows = (int)min<int64_t>(16 * MT, a.M - m0);
 
-    // this workgroup's K slice and this wave's part of it, in pairs of groups
-    const int64_t ps0 = P * s / a.splitk;
-    const int64_t ps1 = P * (s + 1) / a.splitk;
-    const int64_t pw0 = ps0 + (ps1 - ps0) * wv / kWaves;
-    const int64_t pw1 = ps0 + (ps1 - ps0) * (wv + 1) / kWaves;
+    // K slice of this workgroup and this wave's pairs (all uniform)
+    const int ps0 = (int)((uint32_t)P * blockIdx.y / (uint32_t)a.splitk);
+    const int ps1 = (int)((uint32_t)P * (blockIdx.y + 1) / (uint32_t)a.splitk);
+    const int pw0 = ps0 + (ps1 - ps0) * wv / WAVES;
+    const int pw1 = ps0 + (ps1 - ps0) * (wv + 1) / WAVES;
+    const int gbase = 2 * ps0;                          // first group of the slice
+    const int span = min(2 * (ps1 - ps0), G - gbase);   // groups in the slice
 
-    // per-lane base pointers (tiles past N are clamped to a real tile and never stored)
-    const uint8_t *wbase[NT];
-    const uint32_t *pbase[NT];
-    bool tile_ok[NT];
-#pragma unroll
-    for (int t = 0; t < NT; t++) {
-        tile_ok[t] = (nt0 + t) < ntiles_total;
-        const int64_t tt = tile_ok[t] ? nt0 + t : ntiles_total - 1;
-        wbase[t] = a.codes + tt * G * kTileBytes + 16 * l;
-        pbase[t] = reinterpret_cast<const uint32_t *>(a.params) + (tt * (G4 / 4)) * 16 + c;
+    // LDS: reduction [NT*MT][4][64] int32 | decoded params [NT][span][16] u32 |
+    // raw parameter dwords [NT][nq][16] | activation rows [mrows][span*128 + 16]
+    // (the two staging areas are rounded up to whole copy chunks)
+    const int q0 = gbase / 4;
+    const int nq = max((gbase + span + 3) / 4 - q0, 1);
+    const int xstride = span * kGroup + 16;
+    int32_t *red = reinterpret_cast<int32_t *>(smem);
+    uint32_t *ptab = reinterpret_cast<uint32_t *>(smem + NT * MT * 1024);
+    uint8_t *praw = smem + NT * MT * 1024 + NT * span * 64;
+    const int praw_bytes = (NT * nq * 64 + 255) / 256 * 256;
+    int8_t *xlds = reinterpret_cast<int8_t *>(praw + praw_bytes);
+
+    const __amdgpu_buffer_rsrc_t rw = rsrc(a.codes, code_bytes(a.N, a.K));
+    const int8_t *xblk = a.qx + m0 * a.K;     // this block's first token row
+
+    // ---- 1. staging: parameter bytes and (few tokens) activation rows go
+    // straight from memory to LDS, exact counts, issued before the weights.
+    // The copies are asynchronous; the barrier below waits for them (and for
+    // the weight prologue issued meanwhile, which arrives at the same time).
+    for (int ch = wv; ch < praw_bytes / 256; ch += WAVES) {
+        const int o = ch * 256 + 4 * l;                   // byte offset in [NT][nq*64]
+        const int t = o / (nq * 64);
+        const int r = o - t * (nq * 64);
+        const int tt = min(nt0 + min(t, NT - 1), ntiles - 1);
+        const uint8_t *src = a.params + ((int64_t)tt * (G4 / 4) + q0) * 64 + (t < NT ? r : 0);
+        __builtin_amdgcn_global_load_lds(src, praw + ch * 256, 4, 0, 0);
     }
-    bool row_ok[MT];
-    const int8_t *xbase[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++) {
-        const int r = 16 * mt + c;
-        row_ok[mt] = r < mrows;
-        xbase[mt] = a.qx + (m0 + (row_ok[mt] ? r : mrows - 1)) * a.K + 16 * kb;
+    if constexpr (XS) {
+        const int xbytes = mrows * xstride;
+        for (int ch = wv; ch < (xbytes + 1023) / 1024; ch += WAVES) {
+            const int o = ch * 1024 + 16 * l;
+            const int row = o / xstride;
+            const int col = o - row * xstride;
+            const bool ok = row < mrows && col < span * kGroup;
+            const int8_t *src = xblk + (ok ? (int64_t)row * K + gbase * kGroup + col : 0);
+            __builtin_amdgcn_global_load_lds(src, xlds + ch * 1024, 16, 0, 0);
+        }
+    }
+    // epilogue scales of this wave's first output tile (waves without a tile skip them)
+    const int i0 = wv < NT * MT ? wv : 0;
+    const int t_e = i0 / MT, mt_e = i0 - (i0 / MT) * MT;
+    const int64_t m_e = min<int64_t>(m0 + 16 * mt_e + c, a.M - 1);
+    const int64_t n_e = (int64_t)min(nt0 + t_e, ntiles - 1) * kTileN + 4 * kb;
+    float sa_e = 0.0f;
+    uint2 s0_e = make_uint2(0, 0);
+    if (wv < NT * MT) {
+        sa_e = a.s_a[m_e];
+        s0_e = *reinterpret_cast<const uint2 *>(a.s0 + n_e);
     }
 
+    // ---- 2. the weight stream: DEPTH pairs in flight per wave -----------------
+    int vw[NT];                         // per-lane byte offset of each tile's stream
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+        vw[t] = min(nt0 + t, ntiles - 1) * G * kTileBytes + 16 * l;
+    const __amdgpu_buffer_rsrc_t rx = rsrc(xblk, (int64_t)mrows * a.K);
+    int vx[XS ? 1 : MT];                // per-lane offset of the activation operand row
+#pragma unroll
+    for (int mt = 0; mt < (XS ? 1 : MT); mt++)
+        vx[mt] = min(16 * mt + c, mrows - 1) * K + 16 * kb;
+
+    auto load = [&](Chunk<MT, NT, XS> &ch, int pr) {
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int g = sgpr(min(2 * pr + j, G - 1));
+#pragma unroll
+            for (int t = 0; t < NT; t++)
+                ch.w[t][j] = __builtin_amdgcn_raw_buffer_load_b128(rw, vw[t], g * kTileBytes, kLoadNT);
+            if constexpr (!XS) {
+#pragma unroll
+                for (int mt = 0; mt < MT; mt++) {
+                    ch.x[mt][j][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, vx[mt], g * kGroup, 0);
+                    ch.x[mt][j][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, vx[mt], g * kGroup + 64, 0);
+                }
+            }
+        }
+    };
+
+    // unconditional, even for a wave without pairs (the loads then re-read a
+    // real tile), so that the waits below are exact
+    const int npairs = pw1 - pw0;
+    Chunk<MT, NT, XS> ring[DEPTH];
+#pragma unroll
+    for (int u = 0; u < DEPTH; u++)
+        load(ring[u], pw0 + max(min(u, npairs - 1), 0));
+
+    // ---- 3. decode the group parameters, zero the reduction buffer -----------
+    for (int i = tid; i < NT * MT * 256; i += kThreads)
+        red[i] = 0;
+    __syncthreads();                    // staging copies have landed
+    for (int e = tid; e < NT * span * 16; e += kThreads) {
+        const int t = e / (span * 16);
+        const int rem = e - t * span * 16;
+        const int g = rem / 16 + gbase;                  // absolute group
+        const int cch = rem - (rem / 16) * 16;
+        const uint32_t dw = reinterpret_cast<const uint32_t *>(praw)[(t * nq + (g / 4 - q0)) * 16 + cch];
+        ptab[e] = decode_param((dw >> (8 * (g & 3))) & 0xFFu);
+    }
+    __syncthreads();
+
+    // ---- 4. main loop ----------------------------------------------------------
     v4i acc[NT][MT];
 #pragma unroll
     for (int t = 0; t < NT; t++)
@@ -133,48 +238,33 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_kernel(DecodeArgs a)
         for (int mt = 0; mt < MT; mt++)
             acc[t][mt] = v4i{0, 0, 0, 0};
 
-    // every load below is unconditional (addresses clamped), so the compiler
-    // can keep the whole double buffer in flight with exact vmcnt waits
-    auto load = [&](Chunk<MT, NT> &ch, int64_t pr) {
-#pragma unroll
-        for (int t = 0; t < NT; t++) {
-#pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const int64_t g = min<int64_t>(2 * pr + j, G - 1);
-                ch.w[t][j] = load_nt16(wbase[t] + g * kTileBytes);
-            }
-            ch.p[t] = pbase[t][(2 * pr / 4) * 16];
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const int64_t g = min<int64_t>(2 * pr + j, G - 1);
-                ch.x[mt][j][0] = *reinterpret_cast<const v4i *>(xbase[mt] + g * kGroup);
-                ch.x[mt][j][1] = *reinterpret_cast<const v4i *>(xbase[mt] + g * kGroup + 64);
-            }
-    };
+    const int8_t *xrow = xlds + (XS ? min(c, mrows - 1) : 0) * xstride + 16 * kb;
 
-    auto compute = [&](const Chunk<MT, NT> &ch, int64_t pr) {
+    auto compute = [&](const Chunk<MT, NT, XS> &ch, int pr) {
 #pragma unroll
         for (int j = 0; j < 2; j++) {
-            const int64_t g = 2 * pr + j;
+            const int g = 2 * pr + j;
             if (g >= G)          // odd group count: the pair's second half is padding
                 break;
+            const int gr = g - gbase;
             v4i xf[MT][2];
+            if constexpr (XS) {
+                xf[0][0] = *reinterpret_cast<const v4i *>(xrow + gr * kGroup);
+                xf[0][1] = *reinterpret_cast<const v4i *>(xrow + gr * kGroup + 64);
+            } else {
 #pragma unroll
-            for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-                for (int h = 0; h < 2; h++)
-                    xf[mt][h] = row_ok[mt] ? ch.x[mt][j][h] : v4i{0, 0, 0, 0};
+                for (int mt = 0; mt < MT; mt++) {
+                    xf[mt][0] = ch.x[mt][j][0];
+                    xf[mt][1] = ch.x[mt][j][1];
+                }
+            }
 #pragma unroll
             for (int t = 0; t < NT; t++) {
-                const uint32_t pb = (ch.p[t] >> (8 * (g & 3))) & 0xFFu;
-                const uint32_t s1 = (pb & 15u) + 1u;
-                const uint32_t zs = (pb >> 4) * s1;
-                const unsigned short cc16 = (unsigned short)((128u - zs) * 257u);
-                const us2 S = {(unsigned short)s1, (unsigned short)s1};
-                const us2 C = {cc16, cc16};
+                const uint32_t sc = ptab[(t * span + gr) * 16 + c];
+                const unsigned short s1 = (unsigned short)(sc & 0xFFFFu);
+                const unsigned short c16 = (unsigned short)(sc >> 16);
+                const us2 S = {s1, s1};
+                const us2 C = {c16, c16};
                 const v4i w = ch.w[t][j];
                 v4i f0, f1;
 #pragma unroll
@@ -192,53 +282,64 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_kernel(DecodeArgs a)
         }
     };
 
-    if (pw1 > pw0) {
-        Chunk<MT, NT> A, B;
-        load(A, pw0);
-        int64_t pr = pw0;
-        for (; pr + 2 < pw1; pr += 2) {
-            load(B, pr + 1);
-            compute(A, pr);
-            load(A, pr + 2);
-            compute(B, pr + 1);
+    // Loads in the steady-state loop are all real; the prologue and the last
+    // refill clamp to the wave's last pair (a re-read of data just fetched) so
+    // that no load is conditional.
+    if (npairs > 0) {
+        int pr = pw0;
+        for (; pr + 2 * DEPTH <= pw1; pr += DEPTH) {
+#pragma unroll
+            for (int u = 0; u < DEPTH; u++) {
+                compute(ring[u], pr + u);
+                load(ring[u], pr + u + DEPTH);
+            }
         }
-        if (pr + 1 < pw1) {
-            load(B, pr + 1);
-            compute(A, pr);
-            compute(B, pr + 1);
-        } else {
-            compute(A, pr);
+        int rem = pw1 - pr;
+        if (rem > DEPTH) {
+#pragma unroll
+            for (int u = 0; u < DEPTH; u++) {
+                compute(ring[u], pr + u);
+                load(ring[u], min(pr + u + DEPTH, pw1 - 1));
+            }
+            pr += DEPTH;
+            rem -= DEPTH;
         }
+#pragma unroll
+        for (int u = 0; u < DEPTH; u++)
+            if (u < rem)
+                compute(ring[u], pr + u);
     }
 
-    // ---- sum the four waves' partials through LDS ----------------------------
-    v4i *red = reinterpret_cast<v4i *>(smem);   // [kWaves][NT*MT][64]
+    // ---- 5. sum the waves' partials with LDS atomics ---------------------------
 #pragma unroll
     for (int t = 0; t < NT; t++)
 #pragma unroll
         for (int mt = 0; mt < MT; mt++)
-            red[(wv * NT * MT + t * MT + mt) * 64 + l] = acc[t][mt];
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                atomicAdd(red + ((t * MT + mt) * 4 + r) * 64 + l, acc[t][mt][r]);
     __syncthreads();
 
     const int64_t tile_id = (int64_t)blockIdx.z * gridDim.x + blockIdx.x;
-    for (int i = wv; i < NT * MT; i += kWaves) {
+    for (int i = wv; i < NT * MT; i += WAVES) {
         const int t = i / MT;
         const int mt = i - t * MT;
-        v4i sum = red[i * 64 + l];
+        v4i sum;
 #pragma unroll
-        for (int w = 1; w < kWaves; w++)
-            sum += red[(w * NT * MT + i) * 64 + l];
+        for (int r = 0; r < 4; r++)
+            sum[r] = red[(i * 4 + r) * 64 + l];
         const int64_t m = m0 + 16 * mt + c;
-        const int64_t n = (nt0 + t) * kTileN + 4 * kb;
-        if (!((nt0 + t) < ntiles_total) || m >= a.M)
+        const int64_t n = (int64_t)(nt0 + t) * kTileN + 4 * kb;
+        if (nt0 + t >= ntiles || m >= a.M)
             continue;
         if (a.splitk > 1) {
 #pragma unroll
             for (int r = 0; r < 4; r++)
-                atomicAdd(a.ws_acc + m * a.N + n + r, sum[r]);
+                __hip_atomic_fetch_add(a.ws_acc + m * a.N + n + r, sum[r], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
         } else {
-            const float sa = a.s_a[m];
-            const uint2 s0p = *reinterpret_cast<const uint2 *>(a.s0 + n);
+            const float sa = (i == i0) ? sa_e : a.s_a[m];
+            const uint2 s0p = (i == i0) ? s0_e : *reinterpret_cast<const uint2 *>(a.s0 + n);
             const uint32_t s0w[2] = {s0p.x, s0p.y};
             uint32_t out[2];
 #pragma unroll
@@ -257,29 +358,35 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_kernel(DecodeArgs a)
     if (a.splitk <= 1)
         return;
 
-    // ---- split-K: the last workgroup of the tile applies the epilogue --------
-    __threadfence();
+    // ---- 6. split-K: the last workgroup of the tile applies the epilogue -------
+    // Every value that crosses workgroups moves through device-scope atomics,
+    // which are performed at the memory-side coherence point, so no cache
+    // writeback or invalidate is needed (an agent-scope fence would write back
+    // and invalidate the whole L2 of the XCD in every workgroup).  Ordering:
+    // each wave waits until its partial-sum atomics are acknowledged before
+    // the barrier, the counter increment is issued after the barrier, and the
+    // last arriver's read-and-clear exchanges are issued after it has seen the
+    // final count.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     __shared__ uint32_t arrival;
     if (tid == 0)
-        arrival = atomicAdd(a.ws_cnt + tile_id, 1u);
+        arrival = __hip_atomic_fetch_add(a.ws_cnt + tile_id, 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (arrival != (uint32_t)(a.splitk - 1))
         return;
-    __threadfence();
-    const int ncols = (int)min<int64_t>(NT * kTileN, a.N - nt0 * kTileN);
+    const int ncols = (int)min<int64_t>(NT * kTileN, a.N - (int64_t)nt0 * kTileN);
     for (int i = tid; i < mrows * ncols / 4; i += kThreads) {
         const int r = i / (ncols / 4);
         const int q = i - r * (ncols / 4);
         const int64_t m = m0 + r;
-        const int64_t n = nt0 * kTileN + 4 * q;
+        const int64_t n = (int64_t)nt0 * kTileN + 4 * q;
         int32_t *wp = a.ws_acc + m * a.N + n;
         v4i sum;
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            sum[e] = __hip_atomic_load(wp + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(wp + e, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        for (int e = 0; e < 4; e++)
+            sum[e] = __hip_atomic_exchange(wp + e, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const float sa = a.s_a[m];
         const uint2 s0p = *reinterpret_cast<const uint2 *>(a.s0 + n);
         const uint32_t s0w[2] = {s0p.x, s0p.y};
@@ -300,23 +407,52 @@ __global__ __launch_bounds__(kThreads) void gemm_decode_kernel(DecodeArgs a)
         __hip_atomic_store(a.ws_cnt + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MT, int NT>
+template <int MT, int NT, int WAVES, int DEPTH, bool XS>
 hipError_t launch_decode_t(const GemmPlan &p, const DecodeArgs &a, size_t lds, hipStream_t st)
 {
     dim3 grid((unsigned)p.n_blocks, (unsigned)p.splitk, (unsigned)p.m_blocks);
-    hipLaunchKernelGGL((gemm_decode_kernel<MT, NT>), grid, dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((gemm_decode_kernel<MT, NT, WAVES, DEPTH, XS>), grid, dim3(64 * WAVES), lds,
+                       st, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// Dynamic LDS of one decode workgroup: the cross-wave reduction buffer.
-size_t decode_lds_bytes(int64_t M, int64_t K, int mt, int nt, int splitk)
+// Instantiated (mt, nt, waves, depth, staged activations) variants.
+#define W4A8_DECODE_VARIANTS(X)                                                                   \
+    X(1, 1, 4, 2, true) X(1, 1, 4, 4, true) X(1, 2, 4, 2, true) X(1, 2, 4, 4, true)              \
+    X(1, 1, 8, 2, true) X(1, 2, 8, 2, true) X(1, 1, 4, 2, false) X(1, 1, 4, 4, false)            \
+    X(1, 2, 4, 2, false) X(1, 4, 4, 2, false) X(1, 1, 8, 2, false) X(1, 2, 8, 2, false)          \
+    X(2, 1, 4, 2, false) X(2, 2, 4, 2, false) X(2, 4, 4, 2, false) X(2, 1, 8, 2, false)          \
+    X(4, 1, 4, 2, false) X(4, 2, 4, 2, false) X(4, 4, 4, 2, false) X(4, 1, 8, 2, false)
+
+bool decode_variant_exists(int mt, int nt, int waves, int depth, bool xs)
 {
-    (void)M;
-    (void)K;
-    (void)splitk;
-    return (size_t)kWaves * nt * mt * 64 * 16;
+#define W4A8_DECODE_HAS(MT_, NT_, WV_, D_, XS_) \
+    if (mt == MT_ && nt == NT_ && waves == WV_ && depth == D_ && xs == XS_) return true;
+    W4A8_DECODE_VARIANTS(W4A8_DECODE_HAS)
+#undef W4A8_DECODE_HAS
+    return false;
+}
+
+// Dynamic LDS of one decode workgroup (0 if the plan does not fit).
+size_t decode_lds_bytes(const GemmPlan &p, int64_t M, int64_t K)
+{
+    const int64_t G = num_groups(K);
+    const int64_t P = (G + 1) / 2;
+    int64_t span = 0, nq = 0;
+    for (int s = 0; s < p.splitk; s++) {
+        const int64_t ps0 = P * s / p.splitk, ps1 = P * (s + 1) / p.splitk;
+        const int64_t sp = std::min<int64_t>(2 * (ps1 - ps0), G - 2 * ps0);
+        span = std::max(span, sp);
+        nq = std::max<int64_t>(nq, std::max<int64_t>((2 * ps0 + sp + 3) / 4 - (2 * ps0) / 4, 1));
+    }
+    const int64_t rows = std::min<int64_t>(16 * p.mt, M);
+    int64_t bytes = (int64_t)p.nt * p.mt * 1024 + (int64_t)p.nt * span * 64 +
+                    ((int64_t)p.nt * nq * 64 + 255) / 256 * 256;
+    if (p.xstage)
+        bytes += (rows * (span * kGroup + 16) + 1023) / 1024 * 1024;
+    return (size_t)bytes;
 }
 
 hipError_t launch_gemm_decode(const GemmPlan &p, const int8_t *qx, const float *s_a,
@@ -343,18 +479,13 @@ hipError_t launch_gemm_decode(const GemmPlan &p, const int8_t *qx, const float *
         size_t acc_bytes = ((size_t)M * N * 4 + 255) / 256 * 256;
         a.ws_cnt = reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(ws) + acc_bytes);
     }
-    const size_t lds = decode_lds_bytes(M, K, p.mt, p.nt, p.splitk);
-#define W4A8_DECODE_CASE(MT_, NT_) \
-    if (p.mt == MT_ && p.nt == NT_) return launch_decode_t<MT_, NT_>(p, a, lds, st);
-    W4A8_DECODE_CASE(1, 1)
-    W4A8_DECODE_CASE(1, 2)
-    W4A8_DECODE_CASE(1, 4)
-    W4A8_DECODE_CASE(2, 1)
-    W4A8_DECODE_CASE(2, 2)
-    W4A8_DECODE_CASE(2, 4)
-    W4A8_DECODE_CASE(4, 1)
-    W4A8_DECODE_CASE(4, 2)
-    W4A8_DECODE_CASE(4, 4)
+    const size_t lds = decode_lds_bytes(p, M, K);
+    if (lds == 0 || lds > 160 * 1024)
+        return hipErrorInvalidValue;
+#define W4A8_DECODE_CASE(MT_, NT_, WV_, D_, XS_)                                           \
+    if (p.mt == MT_ && p.nt == NT_ && p.waves == WV_ && p.depth == D_ && p.xstage == XS_) \
+        return launch_decode_t<MT_, NT_, WV_, D_, XS_>(p, a, lds, st);
+    W4A8_DECODE_VARIANTS(W4A8_DECODE_CASE)
 #undef W4A8_DECODE_CASE
     return hipErrorInvalidValue;
 }

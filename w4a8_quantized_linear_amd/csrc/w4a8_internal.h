@@ -59,7 +59,10 @@ struct GemmPlan {
     int kind;        // 0 = decode (weights streamed, split-K), 1 = prefill (LDS tiles)
     int mt;          // 16-row m-tiles per workgroup (decode)
     int nt;          // 16-column n-tiles per workgroup (decode)
-    int splitk;      // number of K slices (decode)
+    int splitk;      // number of K slices across workgroups (decode)
+    int waves;       // waves per workgroup, splitting the slice (decode)
+    int depth;       // pairs of groups in flight per wave (decode)
+    bool xstage;     // activation rows staged in LDS (decode, few tokens)
     int64_t m_blocks;
     int64_t n_blocks;
     size_t ws_bytes; // workspace needed (0 if none)
