@@ -132,7 +132,7 @@ def test_act_quant_validation(lib):
 
 
 @needs_no_gpu
-def test_gemm_validation(lib):
+def test_gemm_validation(lib, monkeypatch):
     f = lib.gemm_w4a8
     ok = dict(qx=A, sa=A, w=A, s0=A, M=1, N=16, K=128, y=B, acc=NUL, ws=NUL, wsb=0)
 
@@ -154,8 +154,9 @@ def test_gemm_validation(lib):
     assert call(qx=MIS) == -3
     assert call(y=MIS) == -3
     assert call(acc=MIS) == -3
-    # a split-K shape without (or with too small) a workspace
+    # a split-K plan without (or with too small) a workspace
     from w4a8_quantized_linear_amd import _lib
+    monkeypatch.setenv("W4A8_DECODE_PLAN", "1,1,4")
     need = _lib.gemm_w4a8_workspace_bytes(1, 4096, 4096)
     assert need > 0
     assert call(N=4096, K=4096) == -4
