@@ -297,3 +297,39 @@ def test_gemm_n_tail_tiles(plan):
     out = orc.linear(x, orc.quantize_weights(w))
     assert np.array_equal(to_host(acc), out["acc"])
     assert_y_close(f16_bits(y), out["y"], "n-tail")
+
+
+def _with_env(name, value, fn):
+    old = os.environ.get(name)
+    os.environ[name] = value
+    try:
+        return fn()
+    finally:
+        if old is None:
+            del os.environ[name]
+        else:
+            os.environ[name] = old
+
+
+@pytest.mark.parametrize("tile", ["128,128", "256,128", "128,256", "256,256"])
+@pytest.mark.parametrize("M,K,N", [(300, 384, 272), (17, 256, 48), (512, 1024, 512)])
+def test_prefill_tiles_ragged(tile, M, K, N):
+    import torch
+    from w4a8_quantized_linear_amd import gemm_w4a8, quantize_act_per_token_i8
+    say("prefill tile=%s M=%d K=%d N=%d" % (tile, M, K, N))
+    rng = np.random.default_rng(M + 7 * K + 13 * N)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    x[M // 3] = 0
+    wq = gpu_weights(w)
+    qx, sa = quantize_act_per_token_i8(to_dev(x))
+    acc = torch.zeros((M, N), dtype=torch.int32, device=dev())
+
+    def run():
+        y = gemm_w4a8(qx, sa, wq["wpacked"], wq["s0"], N, acc_out=acc)
+        torch.cuda.synchronize()
+        return y
+    y = _with_env("W4A8_PREFILL_TILE", tile, run)
+    out = orc.linear(x, orc.quantize_weights(w))
+    assert np.array_equal(to_host(acc), out["acc"])
+    assert_y_close(f16_bits(y), out["y"], "prefill tile")

@@ -15,6 +15,9 @@ namespace w4a8 {
 
 bool decode_variant_exists(int mt, int nt, int waves, int depth, bool xs);
 size_t decode_lds_bytes(const GemmPlan &p, int64_t M, int64_t K);
+hipError_t launch_gemm_prefill(const GemmPlan &p, const int8_t *qx, const float *s_a,
+                               const uint8_t *stream_bytes, const uint16_t *s0, int64_t M,
+                               int64_t N, int64_t K, uint16_t *y, int32_t *acc_out, hipStream_t st);
 hipError_t launch_gemm_decode(const GemmPlan &p, const int8_t *qx, const float *s_a,
                               const uint8_t *stream_bytes, const uint16_t *s0, int64_t M,
                               int64_t N, int64_t K, uint16_t *y, int32_t *acc_out, void *ws,
@@ -66,6 +69,25 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
             p = q;
     }
 
+    // many tokens: the LDS-tiled matrix-core kernel (mt, nt = tile rows / 16, tile cols / 16)
+    const char *force = std::getenv("W4A8_PREFILL_TILE");
+    if (M > 64 || force) {
+        int bm = M >= 1024 ? 256 : 128, bn = M >= 1024 ? 256 : 128;
+        if (force)
+            std::sscanf(force, "%d,%d", &bm, &bn);
+        if ((bm == 128 || bm == 256) && (bn == 128 || bn == 256)) {
+            GemmPlan q{};
+            q.kind = 1;
+            q.mt = bm / 16;
+            q.nt = bn / 16;
+            q.splitk = 1;
+            q.m_blocks = (M + bm - 1) / bm;
+            q.n_blocks = (ntiles * kTileN + bn - 1) / bn;
+            q.ws_bytes = 0;
+            return q;
+        }
+    }
+
     if (const char *env = std::getenv("W4A8_DECODE_PLAN")) {
         int mt = 0, nt = 0, s = 0, wv = 4, dp = 2, xs = 0;
         int got = std::sscanf(env, "%d,%d,%d,%d,%d,%d", &mt, &nt, &s, &wv, &dp, &xs);
@@ -98,6 +120,8 @@ hipError_t launch_gemm(const GemmPlan &p, const int8_t *qx, const float *s_a,
                      (long long)M, (long long)N, (long long)K, p.kind, p.mt, p.nt, p.splitk,
                      p.waves, p.depth, (int)p.xstage, (long long)p.n_blocks, p.splitk,
                      (long long)p.m_blocks);
+    if (p.kind == 1)
+        return launch_gemm_prefill(p, qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, st);
     return launch_gemm_decode(p, qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, ws, st);
 }
 
