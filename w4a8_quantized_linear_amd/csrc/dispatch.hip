@@ -69,23 +69,17 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
             p = q;
     }
 
-    // many tokens: the LDS-tiled matrix-core kernel (mt, nt = tile rows / 16, tile cols / 16)
-    const char *force = std::getenv("W4A8_PREFILL_TILE");
-    if (M > 64 || force) {
-        int bm = M >= 1024 ? 256 : 128, bn = M >= 1024 ? 256 : 128;
-        if (force)
-            std::sscanf(force, "%d,%d", &bm, &bn);
-        if ((bm == 128 || bm == 256) && (bn == 128 || bn == 256)) {
-            GemmPlan q{};
-            q.kind = 1;
-            q.mt = bm / 16;
-            q.nt = bn / 16;
-            q.splitk = 1;
-            q.m_blocks = (M + bm - 1) / bm;
-            q.n_blocks = (ntiles * kTileN + bn - 1) / bn;
-            q.ws_bytes = 0;
-            return q;
-        }
+    // many tokens: the LDS-tiled matrix-core kernel (256 x 256 tiles)
+    if (M > 64 || std::getenv("W4A8_FORCE_PREFILL")) {
+        GemmPlan q{};
+        q.kind = 1;
+        q.mt = 16;
+        q.nt = 16;
+        q.splitk = 1;
+        q.m_blocks = (M + 255) / 256;
+        q.n_blocks = (ntiles * kTileN + 255) / 256;
+        q.ws_bytes = 0;
+        return q;
     }
 
     if (const char *env = std::getenv("W4A8_DECODE_PLAN")) {
