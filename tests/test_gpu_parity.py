@@ -311,16 +311,18 @@ def _with_env(name, value, fn):
             os.environ[name] = old
 
 
-# Shapes for the many-token kernel (256 x 256 workgroup tiles, four weight
-# groups in flight): ragged M and N tails, K with a group count below, at and
-# past the ring depth and not a multiple of it, and enough m-blocks to fill
-# more than one band of four.
+# Shapes for the many-token kernel (16 TM x 256 workgroup tiles, TM in
+# {4, 8, 16}; weight rings of 4 or 6 groups, unrolled by 4 or 12): ragged M
+# and N tails, K with a group count below, at and past the ring depth and the
+# unroll and not a multiple of them, and enough m-blocks to fill more than
+# one band of four.
+@pytest.mark.parametrize("tm", ["4", "8", "16"])
 @pytest.mark.parametrize("M,K,N", [(300, 384, 272), (17, 256, 48), (512, 1024, 512),
-                                   (1100, 640, 304), (257, 1152, 1040)])
-def test_prefill_ragged(M, K, N):
+                                   (1100, 640, 304), (257, 1152, 1040), (90, 1664, 256)])
+def test_prefill_ragged(tm, M, K, N):
     import torch
     from w4a8_quantized_linear_amd import gemm_w4a8, quantize_act_per_token_i8
-    say("prefill M=%d K=%d N=%d" % (M, K, N))
+    say("prefill TM=%s M=%d K=%d N=%d" % (tm, M, K, N))
     rng = np.random.default_rng(M + 7 * K + 13 * N)
     w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
     x = rng.standard_normal((M, K)).astype(np.float16)
@@ -333,7 +335,7 @@ def test_prefill_ragged(M, K, N):
         y = gemm_w4a8(qx, sa, wq["wpacked"], wq["s0"], N, acc_out=acc)
         torch.cuda.synchronize()
         return y
-    y = _with_env("W4A8_FORCE_PREFILL", "1", run)
+    y = _with_env("W4A8_PREFILL_TM", tm, run)
     out = orc.linear(x, orc.quantize_weights(w))
     assert np.array_equal(to_host(acc), out["acc"])
     assert_y_close(f16_bits(y), out["y"], "prefill")

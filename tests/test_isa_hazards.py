@@ -11,7 +11,8 @@ import isa_hazards
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "w4a8_quantized_linear_amd", "csrc", "gemm_prefill.hip")
-KERNEL = "_ZN4w4a812_GLOBAL__N_119gemm_prefill_kernelENS0_11PrefillArgsE"
+KERNELS = ["_ZN4w4a812_GLOBAL__N_119gemm_prefill_kernelILi%dEEEvNS0_11PrefillArgsE" % tm
+           for tm in (4, 8, 16)]
 
 
 @pytest.fixture(scope="module")
@@ -28,32 +29,45 @@ def listing(tmp_path_factory):
     return open(out).read()
 
 
-def test_mfma_accumulators_in_place(listing):
-    insts, _ = isa_hazards.parse_kernel(listing, KERNEL)
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_mfma_accumulators_in_place(listing, kernel):
+    insts, _ = isa_hazards.parse_kernel(listing, kernel)
     mfma = [ops for op, ops in insts if op.startswith("v_mfma")]
     assert len(mfma) >= 256
     for ops in mfma:
         assert ops[0].startswith("a[") and ops[0] == ops[3], ops
 
 
-def test_no_spills_or_accumulator_moves_beside_mfmas(listing):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_no_spills_or_accumulator_moves_beside_mfmas(listing, kernel):
     # basic blocks that issue MFMAs hold no scratch traffic and no moves of
-    # accumulation registers (the accumulators stay put between steps)
-    insts, labels = isa_hazards.parse_kernel(listing, KERNEL)
+    # the accumulation registers the MFMAs use (the accumulators stay put;
+    # other values parked in spare AGPRs are allowed)
+    insts, labels = isa_hazards.parse_kernel(listing, kernel)
+    acc_regs = set()
+    for op, ops in insts:
+        if op.startswith("v_mfma"):
+            acc_regs |= isa_hazards._regs(ops[0])
     starts = sorted(set(labels.values()) | {k + 1 for k, (op, _) in enumerate(insts)
                                              if op.startswith("s_cbranch") or op == "s_branch"})
     bounds = [0] + [s for s in starts if 0 < s < len(insts)] + [len(insts)]
     n_blocks = 0
     for a, b in zip(bounds, bounds[1:]):
-        ops = [op for op, _ in insts[a:b]]
-        if any(o.startswith("v_mfma") for o in ops):
-            n_blocks += 1
-            assert not any(o.startswith("scratch_") or o.startswith("v_accvgpr_") for o in ops), (a, b)
+        block = insts[a:b]
+        if not any(op.startswith("v_mfma") for op, _ in block):
+            continue
+        n_blocks += 1
+        for op, ops in block:
+            assert not op.startswith("scratch_"), (a, op, ops)
+            if op.startswith("v_accvgpr_"):
+                touched = set().union(*(isa_hazards._regs(o) for o in ops))
+                assert not (touched & acc_regs), (a, op, ops)
     assert n_blocks > 0
 
 
-def test_mfma_hazard_spacing(listing):
-    n, found = isa_hazards.check(listing, KERNEL, valu_mfma=4, mfma_other=19)
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_mfma_hazard_spacing(listing, kernel):
+    n, found = isa_hazards.check(listing, kernel, valu_mfma=4, mfma_other=19)
     assert n > 0
     assert not found, found[:5]
 

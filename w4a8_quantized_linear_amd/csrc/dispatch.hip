@@ -15,6 +15,7 @@ namespace w4a8 {
 
 bool decode_variant_exists(int mt, int nt, int waves, int depth, bool xs);
 size_t decode_lds_bytes(const GemmPlan &p, int64_t M, int64_t K);
+bool prefill_tm_supported(int tm);
 hipError_t launch_gemm_prefill(const GemmPlan &p, const int8_t *qx, const float *s_a,
                                const uint8_t *stream_bytes, const uint16_t *s0, int64_t M,
                                int64_t N, int64_t K, uint16_t *y, int32_t *acc_out, hipStream_t st);
@@ -30,6 +31,22 @@ size_t ws_size(int64_t M, int64_t N, int splitk, int64_t tiles)
     if (splitk <= 1)
         return 0;
     return ((size_t)M * N * 4 + 255) / 256 * 256 + (size_t)tiles * 4;
+}
+
+// compute units of the current device (cached per device)
+int64_t num_cus()
+{
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 bool launchable(const GemmPlan &p, int64_t M, int64_t K)
@@ -69,14 +86,36 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
             p = q;
     }
 
-    // many tokens: the LDS-tiled matrix-core kernel (256 x 256 tiles)
-    if (M > 64 || std::getenv("W4A8_FORCE_PREFILL")) {
+    // many tokens: the matrix-core kernel with (16 TM) x 256 workgroup tiles.
+    // TM is chosen by a cost model: workgroup rounds on the CUs x TM x the
+    // relative time per MFMA at that TM (smaller tiles rebuild each weight
+    // for fewer tokens and pay the per-group overheads more often), with the
+    // factors taken from rocprofv3 sweeps over M = 128..4096 on MI355X.
+    // W4A8_PREFILL_TM=4|8|16 forces this kernel and its TM (at any M).
+    int tm = 0;
+    if (const char *env = std::getenv("W4A8_PREFILL_TM"))
+        tm = std::atoi(env);
+    if (!prefill_tm_supported(tm) && M > 64) {
+        const int64_t cus = num_cus();
+        const int64_t nblk = (ntiles * kTileN + 255) / 256;
+        const struct { int tm; double rel; } cand[] = {{16, 1.0}, {8, 1.23}, {4, 1.75}};
+        double best = 0;
+        for (const auto &c : cand) {
+            const int64_t tiles = (M + 16 * c.tm - 1) / (16 * c.tm) * nblk;
+            const double cost = (double)((tiles + cus - 1) / cus) * c.tm * c.rel;
+            if (tm == 0 || cost < best) {
+                tm = c.tm;
+                best = cost;
+            }
+        }
+    }
+    if (prefill_tm_supported(tm)) {
         GemmPlan q{};
         q.kind = 1;
-        q.mt = 16;
+        q.mt = tm;
         q.nt = 16;
         q.splitk = 1;
-        q.m_blocks = (M + 255) / 256;
+        q.m_blocks = (M + 16 * tm - 1) / (16 * tm);
         q.n_blocks = (ntiles * kTileN + 255) / 256;
         q.ws_bytes = 0;
         return q;

@@ -61,17 +61,27 @@ constexpr int kBufFlags = 0x00020000;   // raw buffer resource, dword 3 (gfx9 fa
 constexpr int kXcds = 8;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int BM = 256, BN = 256;         // workgroup tile
-constexpr int TM = 16, TN = 4;            // 16x16 MFMA tiles per wave (256 x 64)
-constexpr int kAStage = BM * 128;         // bytes of one activation stage
+constexpr int TN = 4;                     // 16-channel tiles per wave
+constexpr int BN = kWaves * TN * 16;      // channels per workgroup
 constexpr int kAStages = 3;               // activation stages in LDS (ring)
-constexpr int kXChunks = kAStage / 16 / kThreads;   // 16-byte activation loads per thread per group
-constexpr int kBandM = 4;                 // m-blocks per band of the tile order
-constexpr int kBDepth = 4;                // weight groups in flight per wave (ring slots)
 constexpr int kAhead = 3;                 // activation operand reads in flight
-static_assert(TM == 4 * TN, "one B-operand dword is rebuilt per row step");
-static_assert(kXChunks + kXChunks / 2 + TN <= TM, "phase 1 has a row step for every transfer");
-static_assert(TM % (kAhead + 1) == 0, "the operand-read ring lines up with the phases");
+constexpr int kBandM = 4;                 // m-blocks per band of the tile order
+
+// Shape of one instantiation: TM 16-row tiles per wave (all waves share the
+// rows), so a workgroup tile is 16 TM tokens x 256 channels.
+template <int TM>
+struct Cfg {
+    static constexpr int BM = 16 * TM;
+    static constexpr int kAStage = BM * 128;                     // bytes of one activation stage
+    static constexpr int kXChunks = kAStage / 16 / kThreads;     // 16-byte activation loads per thread per group
+    static constexpr int kAPre = TM >= 16 ? 1 : 8 / kXChunks;   // groups of activations held in registers
+    static constexpr int kBDepth = TM >= 8 ? 4 : 6;             // weight groups in flight (ring slots)
+    static constexpr int kUnroll = TM >= 8 ? 4 : 12;            // groups per main-loop iteration
+    static_assert(kUnroll % kBDepth == 0 && kUnroll % kAPre == 0 && kUnroll % 4 == 0,
+                  "ring, register and parameter-byte indices are static in the unrolled loop");
+    static_assert(TM % (kAhead + 1) == 0 && TM > kAhead, "the operand-read ring lines up with the phases");
+    static_assert((BM / 2) * (BN * 2 + 16) <= kAStages * kAStage, "output half-tile fits in the stages");
+};
 
 __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *p, int64_t bytes)
 {
@@ -105,15 +115,20 @@ struct BSlot {
     uint32_t p[TN];    // group-parameter dword (four groups) of the lane's channel
 };
 
-// The accumulators, as two arrays of 32 tiles: kept under the size past which
-// the compiler leaves a private array in scratch memory.
+// The accumulators, as two arrays: each stays under the size past which the
+// compiler leaves a private array in scratch memory.
+template <int TM>
 struct Acc {
     v4i lo[TM / 2][TN], hi[TM / 2][TN];
     __device__ v4i &operator()(int i, int t) { return i < TM / 2 ? lo[i][t] : hi[i - TM / 2][t]; }
 };
 
+template <int TM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a)
 {
+    using C = Cfg<TM>;
+    constexpr int BM = C::BM, kAStage = C::kAStage, kXChunks = C::kXChunks, kAPre = C::kAPre,
+                  kBDepth = C::kBDepth, kUnroll = C::kUnroll;
     extern __shared__ __align__(16) uint8_t smem[];
     float *sa_lds = reinterpret_cast<float *>(smem + kAStages * kAStage);
 
@@ -155,28 +170,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
     for (int i = tid; i < BM; i += kThreads)
         sa_lds[i] = a.s_a[min<int64_t>(m0 + i, a.M - 1)];
 
-    v4i xr[kXChunks];
-    auto aload = [&](int g) {
+    v4i xr[kAPre][kXChunks];   // activations of the next kAPre groups to store
+    auto xload = [&](v4i &dst, int g, int j) {
         g = min(g, G - 1);                   // the last loads re-read a real group
-#pragma unroll
-        for (int j = 0; j < kXChunks; j++)
-            xr[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff, j * (kThreads / 8) * K + g * kGroup, 0);
+        dst = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff, j * (kThreads / 8) * K + g * kGroup, 0);
     };
-    auto astore = [&](int stage) {
-        uint8_t *As = smem + stage * kAStage;
-#pragma unroll
-        for (int j = 0; j < kXChunks; j++)
-            *reinterpret_cast<v4i *>(As + swz(j * (kThreads / 8) + xrow0, xch)) = xr[j];
+    auto xstore = [&](uint8_t *stage, const v4i &src, int j) {
+        *reinterpret_cast<v4i *>(stage + swz(j * (kThreads / 8) + xrow0, xch)) = src;
     };
-    auto bload = [&](BSlot &s, int g) {
+    auto bload_t = [&](BSlot &s, int g, int t) {
         g = min(g, G - 1);
-#pragma unroll
-        for (int t = 0; t < TN; t++) {
-            s.w[t] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff, (t * G + g) * kTileBytes, 2);
-            s.p[t] = __builtin_amdgcn_raw_buffer_load_b32(rp, poff, (t * (G4 / 4) + (g >> 2)) * 64, 0);
-        }
+        s.w[t] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff, (t * G + g) * kTileBytes, 2);
+        s.p[t] = __builtin_amdgcn_raw_buffer_load_b32(rp, poff, (t * (G4 / 4) + (g >> 2)) * 64, 0);
     };
-    Acc acc;
+
+    Acc<TM> acc;
 #pragma unroll
     for (int i = 0; i < TM; i++)
 #pragma unroll
@@ -191,103 +199,119 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
     int so_r = 0, so_n = kAStage, so_w = 2 * kAStage;
     static_assert(kAStages == 3, "three rotating stage offsets");
 
-    // Per-lane (s1, C) of the four tiles for the group being rebuilt:
+    // Per-lane (s1, C) of the four tiles, for groups of either parity:
     // s1 = (p & 15) + 1 and C = 257 (128 - z s1) mod 2^16 from the parameter
-    // byte p = (s1 - 1) | (z << 4).  Each group's pair is computed once, in
-    // two halves (sc_a, sc_b) placed in different row steps.
-    uint32_t S1[TN], C16[TN], sc_p = 0, sc_s1 = 0;
-    auto sc_a = [&](const BSlot &s, int g, int t) {
-        sc_p = (s.p[t] >> (8 * (g & 3))) & 0xFFu;
-        sc_s1 = (sc_p & 15u) + 1u;
-    };
-    auto sc_b = [&](int t) {
-        S1[t] = sc_s1;
-        C16[t] = ((128u - (sc_p >> 4) * sc_s1) * 257u) & 0xFFFFu;
-    };
+    // byte p = (s1 - 1) | (z << 4).  Group g + 1's pairs are computed during
+    // group g's first phase.
+    uint32_t S1[2][TN], C16[2][TN], sc_p = 0, sc_s1 = 0;
 
     v4i af[kAhead + 1];   // activation operands in flight (one per row step)
+    v4i f0[TN], f1[TN];   // B operands: current phase / next phase
+    uint32_t ru = 0;      // rebuild in progress: masked codes of one dword
+    us2 rv = {0, 0};      // ... after the packed multiply-add
 
-    // One phase: the MFMAs of k-half h of group g against B operands fc,
-    // interleaved one by one with the VALU rebuild of fn = the B operands of
-    // the next phase (k-half 1 of group g, then k-half 0 of group g + 1, from
-    // ring slot sb), the (s1, C) pairs of group g + 1 (from slot sn), and in
-    // phase 1 with the LDS stores of group g + 2's activations, the loads of
-    // group g + 3's and the loads of group g + kBDepth's weights into slot s.
-    // Rebuild of dword (t, d): mask, packed multiply-add, xor 0x80, i.e.
-    // (q4 s1 + 128 - z s1) ^ 0x80 per byte.  The operand reads run kAhead
-    // row steps ahead, across phase and group boundaries.  sched_barrier
-    // keeps the program order, so the matrix cores always have the next MFMA
-    // while the VALU works.
-    auto phase = [&](const int h, const v4i (&fc)[TN], v4i (&fn)[TN], const BSlot &sb,
-                     const BSlot &sn, int g, BSlot *refill) {
+    // One phase: the TM x TN MFMAs of k-half h of group g against B operands
+    // fc, with three instruction streams spread evenly over the MFMA slots
+    // (sched_barrier keeps the program order, so the matrix cores always have
+    // the next MFMA while the VALU and memory pipes work):
+    //   * rebuild of fn, the next phase's operands (k-half 1 of group g, then
+    //     k-half 0 of group g + 1), one dword in three steps: mask, packed
+    //     multiply-add, xor 0x80, i.e. (q4 s1 + 128 - z s1) ^ 0x80 per byte;
+    //   * phase 0: group g + 1's (s1, C) pairs, from ring slot sn;
+    //   * phase 1: LDS stores of group g + 2's activations, loads of group
+    //     g + 2 + kAPre's activations into the registers just stored, then
+    //     loads of group g + kBDepth's weights into slot s (loads leave in the
+    //     order they are waited for; vmcnt is in-order).
+    // The activation operand of row i + kAhead is read at the start of row
+    // step i, across phase and group boundaries.
+    auto phase = [&](const int h, const int u, const v4i (&fc)[TN], v4i (&fn)[TN], BSlot &s,
+                     const BSlot &sn, int g) {
+        constexpr int kSlots = TM * TN;
+        constexpr int kRebuild = 3 * 4 * TN;
+        constexpr int kSc = 2 * TN;
+        constexpr int kMem = 2 * kXChunks + TN;
         const uint8_t *As = smem + so_r + aoff[h];
         const uint8_t *An = h ? smem + so_n + aoff[0] : smem + so_r + aoff[1];
         uint8_t *Ad = smem + so_w;
+        // operands being rebuilt: half hn of group gr, from slot sb, with the
+        // pairs of parity pr
         const int hn = 1 - h;
+        const BSlot &sb = h ? sn : s;
+        const int pr = h ? (u + 1) & 1 : u & 1;
         // fc was last written by VALU before the previous phase boundary
         asm volatile("s_nop 4");
 #pragma unroll
-        for (int i = 0; i < TM; i++) {
-            const int t = i >> 2, d = i & 3;
-            const v4i &a = af[i % (kAhead + 1)];
-            mfma_acc(acc(i, 0), a, fc[0]);
-            {
+        for (int k = 0; k < kSlots; k++) {
+            const int i = k / TN, t = k % TN;
+            const v4i &av = af[i % (kAhead + 1)];
+            mfma_acc(acc(i, t), av, fc[t]);
+            if (t == 0) {
                 const int ir = i + kAhead;
                 af[ir % (kAhead + 1)] = *reinterpret_cast<const v4i *>(
                     ir < TM ? As + 2048 * ir : An + 2048 * (ir - TM));
             }
-            // (s1, C) of group g + 1: tile 0 at the end of phase 0, tile
-            // t + 1 during tile t's steps of phase 1
-            if (h == 0 && i == TM - 3)
-                sc_a(sn, g + 1, 0);
-            if (h == 1 && d == 1 && t + 1 < TN)
-                sc_a(sn, g + 1, t + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_acc(acc(i, 1), a, fc[1]);
-            const uint32_t u = ((uint32_t)sb.w[t][d] >> (4 * hn)) & 0x0F0F0F0Fu;
-            if (h == 0 && i == TM - 2)
-                sc_b(0);
-            if (h == 1 && d == 2 && t + 1 < TN)
-                sc_b(t + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_acc(acc(i, 2), a, fc[2]);
-            const us2 S = {(unsigned short)S1[t], (unsigned short)S1[t]};
-            const us2 C = {(unsigned short)C16[t], (unsigned short)C16[t]};
-            const us2 v = __builtin_bit_cast(us2, u) * S + C;
-            if (h == 1) {
-                if (i < kXChunks) {
-                    *reinterpret_cast<v4i *>(Ad + swz(i * (kThreads / 8) + xrow0, xch)) = xr[i];
-                } else if (i < kXChunks + kXChunks / 2) {
-                    const int j = 2 * (i - kXChunks);
-                    const int ga = min(g + 3, G - 1);
-                    xr[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff, j * (kThreads / 8) * K + ga * kGroup, 0);
-                    xr[j + 1] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff, (j + 1) * (kThreads / 8) * K + ga * kGroup, 0);
-                } else if (refill) {
-                    const int tb = i - (kXChunks + kXChunks / 2);
-                    if (tb < TN) {
-                        const int gb = min(g + kBDepth, G - 1);
-                        refill->w[tb] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff, (tb * G + gb) * kTileBytes, 2);
-                        refill->p[tb] = __builtin_amdgcn_raw_buffer_load_b32(rp, poff, (tb * (G4 / 4) + (gb >> 2)) * 64, 0);
+            // (slot k runs ops [k n / kSlots, (k + 1) n / kSlots) of a stream
+            // of n ops: at most ceil(n / kSlots) of them, a constant bound)
+#pragma unroll
+            for (int q = 0; q < (kRebuild + kSlots - 1) / kSlots; q++) {
+                const int o = k * kRebuild / kSlots + q;
+                if (o >= (k + 1) * kRebuild / kSlots)
+                    break;
+                const int j = o / 3, tt = j >> 2, d = j & 3;
+                if (o % 3 == 0) {
+                    ru = ((uint32_t)sb.w[tt][d] >> (4 * hn)) & 0x0F0F0F0Fu;
+                } else if (o % 3 == 1) {
+                    const us2 Sv = {(unsigned short)S1[pr][tt], (unsigned short)S1[pr][tt]};
+                    const us2 Cv = {(unsigned short)C16[pr][tt], (unsigned short)C16[pr][tt]};
+                    rv = __builtin_bit_cast(us2, ru) * Sv + Cv;
+                } else {
+                    fn[tt][d] = (int)(__builtin_bit_cast(uint32_t, rv) ^ 0x80808080u);
+                }
+            }
+            if (h == 0) {
+#pragma unroll
+                for (int q = 0; q < (kSc + kSlots - 1) / kSlots; q++) {
+                    const int o = k * kSc / kSlots + q;
+                    if (o >= (k + 1) * kSc / kSlots)
+                        break;
+                    const int tt = o >> 1;
+                    if ((o & 1) == 0) {
+                        sc_p = (sn.p[tt] >> (8 * ((u + 1) & 3))) & 0xFFu;
+                        sc_s1 = (sc_p & 15u) + 1u;
+                    } else {
+                        S1[(u + 1) & 1][tt] = sc_s1;
+                        C16[(u + 1) & 1][tt] = ((128u - (sc_p >> 4) * sc_s1) * 257u) & 0xFFFFu;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < (kMem + kSlots - 1) / kSlots; q++) {
+                    const int o = k * kMem / kSlots + q;
+                    if (o >= (k + 1) * kMem / kSlots)
+                        break;
+                    if (o < kXChunks) {
+                        xstore(Ad, xr[(u + 2) % kAPre][o], o);
+                    } else if (o < 2 * kXChunks) {
+                        xload(xr[(u + 2) % kAPre][o - kXChunks], g + 2 + kAPre, o - kXChunks);
+                    } else {
+                        bload_t(s, g + kBDepth, o - 2 * kXChunks);
                     }
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
-            mfma_acc(acc(i, 3), a, fc[3]);
-            fn[t][d] = (int)(__builtin_bit_cast(uint32_t, v) ^ 0x80808080u);
-            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // One group g on ring slot s (holding group g) and slot sn (group g + 1),
-    // then the barrier.  Before it, this wave's LDS stores must be complete
-    // (the oldest LDS operations: everything but the kAhead operand reads of
-    // the next group, which read a stage completed a group earlier).  The
-    // stores of group g land in stage (g + 2) % 3, first read at the end of
-    // group g + 1; the stage read in group g is rewritten in group g + 1.
-    v4i f0[TN], f1[TN];
-    auto group = [&](BSlot &s, const BSlot &sn, int g, bool refill) {
-        phase(0, f0, f1, s, sn, g, nullptr);
-        phase(1, f1, f0, sn, sn, g, refill ? &s : nullptr);
+    // One group g (position u in the unrolled loop) on ring slot s (holding
+    // group g) and slot sn (group g + 1), then the barrier.  Before it, this
+    // wave's LDS stores must be complete (the oldest LDS operations:
+    // everything but the kAhead operand reads of the next group, which read a
+    // stage completed a group earlier).  The stores of group g land in stage
+    // (g + 2) % 3, first read at the end of group g + 1; the stage read in
+    // group g is rewritten in group g + 1.
+    auto group = [&](const int u, BSlot &s, BSlot &sn, int g) {
+        phase(0, u, f0, f1, s, sn, g);
+        phase(1, u, f1, f0, s, sn, g);   // past the last group the rebuild is unused
         asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(kAhead) : "memory");
         const int so = so_r;
         so_r = so_n;
@@ -295,28 +319,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
         so_w = so;
     };
 
-    // prologue: groups 0 and 1's activations into LDS, group 2's in
-    // registers, the first kBDepth groups of weights in flight, group 0's
+    // prologue: groups 0 and 1's activations into LDS, groups 2 .. 1 + kAPre
+    // in registers, the first kBDepth groups of weights in flight, group 0's
     // (s1, C), first operands and first activation operand reads
     BSlot ring[kBDepth];
-    aload(0);
-    astore(0);
-    aload(1);
-    astore(1);
-    aload(2);
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+#pragma unroll
+        for (int j = 0; j < kXChunks; j++)
+            xload(xr[0][j], q, j);
+#pragma unroll
+        for (int j = 0; j < kXChunks; j++)
+            xstore(smem + q * kAStage, xr[0][j], j);
+    }
+#pragma unroll
+    for (int q = 2; q < 2 + kAPre; q++)
+#pragma unroll
+        for (int j = 0; j < kXChunks; j++)
+            xload(xr[q % kAPre][j], q, j);
 #pragma unroll
     for (int u = 0; u < kBDepth; u++)
-        bload(ring[u], u);
+#pragma unroll
+        for (int t = 0; t < TN; t++)
+            bload_t(ring[u], u, t);
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < TN; t++) {
-        sc_a(ring[0], 0, t);
-        sc_b(t);
-        const us2 S = {(unsigned short)S1[t], (unsigned short)S1[t]};
-        const us2 C = {(unsigned short)C16[t], (unsigned short)C16[t]};
+        const uint32_t p = ring[0].p[t] & 0xFFu;
+        S1[0][t] = (p & 15u) + 1u;
+        C16[0][t] = ((128u - (p >> 4) * S1[0][t]) * 257u) & 0xFFFFu;
+        const us2 Sv = {(unsigned short)S1[0][t], (unsigned short)S1[0][t]};
+        const us2 Cv = {(unsigned short)C16[0][t], (unsigned short)C16[0][t]};
 #pragma unroll
         for (int d = 0; d < 4; d++) {
-            const us2 v = __builtin_bit_cast(us2, (uint32_t)ring[0].w[t][d] & 0x0F0F0F0Fu) * S + C;
+            const us2 v = __builtin_bit_cast(us2, (uint32_t)ring[0].w[t][d] & 0x0F0F0F0Fu) * Sv + Cv;
             f0[t][d] = (int)(__builtin_bit_cast(uint32_t, v) ^ 0x80808080u);
         }
     }
@@ -324,18 +360,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
     for (int i = 0; i < kAhead; i++)
         af[i] = *reinterpret_cast<const v4i *>(smem + so_r + aoff[0] + 2048 * i);
 
-    // main loop, unrolled by the ring size so every slot index is static; the
-    // loads are unconditional (clamped at the end), so the waits are exact
+    // main loop, unrolled so every ring index is static; the loads are
+    // unconditional (clamped to the last group), also in the tail, whose
+    // groups may still need the weights refilled kBDepth groups back
     int g = 0;
-    for (; g + kBDepth <= G; g += kBDepth) {
+    for (; g + kUnroll <= G; g += kUnroll) {
 #pragma unroll
-        for (int u = 0; u < kBDepth; u++)
-            group(ring[u], ring[(u + 1) % kBDepth], g + u, true);
+        for (int u = 0; u < kUnroll; u++)
+            group(u, ring[u % kBDepth], ring[(u + 1) % kBDepth], g + u);
     }
 #pragma unroll
-    for (int u = 0; u < kBDepth - 1; u++) {
+    for (int u = 0; u < kUnroll - 1; u++) {
         if (g + u < G)
-            group(ring[u], ring[(u + 1) % kBDepth], g + u, false);
+            group(u, ring[u % kBDepth], ring[(u + 1) % kBDepth], g + u);
     }
     // the operand reads issued for group G (past the end) are never used
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -345,10 +382,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
 
     // ---- epilogue.  Lane l holds rows 16 i + 4 (l / 16) + r, column
     // 16 t + l % 16 of the wave's slice.  y = fp16((acc s_a) s0) goes through
-    // LDS, half a tile (128 rows) at a time, so that global stores are whole
-    // 16-byte pieces of output rows; the stages are free once every wave has
-    // passed the barrier.  The INT32 accumulators (an optional output) are
-    // stored directly.
+    // LDS, half a tile at a time, so that global stores are whole 16-byte
+    // pieces of output rows; the stages are free once every wave has passed
+    // the barrier.  The INT32 accumulators (an optional output) are stored
+    // directly.
     float s0f[TN];
 #pragma unroll
     for (int t = 0; t < TN; t++)
@@ -370,7 +407,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
     }
     constexpr int kYRow = BN * 2 + 16;    // padded LDS row of the fp16 tile (bytes)
     constexpr int kHalf = BM / 2;
-    static_assert(kHalf * kYRow <= kAStages * kAStage, "output half-tile fits in the stages");
     const int ncol0 = nb * BN;              // first output column of the tile
     __syncthreads();
 #pragma unroll
@@ -390,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
             }
         }
         __syncthreads();
-        // 128 rows x 32 pieces of 16 bytes; N is a multiple of 16, so a
+        // kHalf rows x 32 pieces of 16 bytes; N is a multiple of 16, so a
         // piece is wholly inside or wholly past the last column
 #pragma unroll 4
         for (int c = tid; c < kHalf * (BN / 8); c += kThreads) {
@@ -405,21 +441,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
     }
 }
 
-}  // namespace
-
-size_t prefill_lds_bytes() { return (size_t)kAStages * kAStage + BM * 4; }
+template <int TM>
+size_t lds_bytes()
+{
+    return (size_t)kAStages * Cfg<TM>::kAStage + Cfg<TM>::BM * 4;
+}
 
 // The kernel addresses activations with 32-bit buffer offsets, so M is cut
 // into launches of at most 2^31 activation bytes each.
-hipError_t launch_gemm_prefill(const GemmPlan &p, const int8_t *qx, const float *s_a,
-                               const uint8_t *stream_bytes, const uint16_t *s0, int64_t M,
-                               int64_t N, int64_t K, uint16_t *y, int32_t *acc_out, hipStream_t st)
+template <int TM>
+hipError_t launch_tm(const int8_t *qx, const float *s_a, const uint8_t *stream_bytes,
+                     const uint16_t *s0, int64_t M, int64_t N, int64_t K, uint16_t *y,
+                     int32_t *acc_out, hipStream_t st)
 {
-    (void)p;
+    constexpr int BM = Cfg<TM>::BM;
     static bool attr_set = false;
-    const size_t lds = prefill_lds_bytes();
+    const size_t lds = lds_bytes<TM>();
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_prefill_kernel),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_prefill_kernel<TM>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess)
             return e;
@@ -444,13 +483,29 @@ hipError_t launch_gemm_prefill(const GemmPlan &p, const int8_t *qx, const float 
         a.nblocks = (int)((N + BN - 1) / BN);
         const int tiles = a.mblocks * a.nblocks;
         a.per_xcd = (tiles + kXcds - 1) / kXcds;
-        hipLaunchKernelGGL(gemm_prefill_kernel, dim3((unsigned)(a.per_xcd * kXcds)),
+        hipLaunchKernelGGL(gemm_prefill_kernel<TM>, dim3((unsigned)(a.per_xcd * kXcds)),
                            dim3(kThreads), lds, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
     return hipSuccess;
+}
+
+}  // namespace
+
+bool prefill_tm_supported(int tm) { return tm == 4 || tm == 8 || tm == 16; }
+
+hipError_t launch_gemm_prefill(const GemmPlan &p, const int8_t *qx, const float *s_a,
+                               const uint8_t *stream_bytes, const uint16_t *s0, int64_t M,
+                               int64_t N, int64_t K, uint16_t *y, int32_t *acc_out, hipStream_t st)
+{
+    switch (p.mt) {
+    case 4: return launch_tm<4>(qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, st);
+    case 8: return launch_tm<8>(qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, st);
+    case 16: return launch_tm<16>(qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace w4a8
