@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--reps", type=int, default=50, help="calls per per-M kernel timing loop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512, help="token rows per M in the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="token rows per M in the oracle sample (default: every row, one whole step)")
     return ap.parse_args()
 
 
@@ -160,7 +161,7 @@ def main():
     achieved = dom_ops / (dom_us * 1e-6) / 1e12
     peak = A.MI355X_INT8_OPS_PER_S / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None,
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(),
                 "kernel": "gemm_w4a8 M=%d N=%d K=%d" % (dom_M, N_DIM, K_DIM),
                 "avg_us": round(dom_us, 3), "ops_per_launch": dom_ops}
 
@@ -181,6 +182,39 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w_np, args.cpu_rows)
 
     print(json.dumps(out), flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_w4a8_m4096_k4096_n11008.txt")
+TRAFFIC_SOURCES = ("w4a8_quantized_linear_amd/csrc/gemm_prefill.hip",
+                   "w4a8_quantized_linear_amd/csrc/dispatch.hip")
+
+
+def source_digest():
+    """sha256 over the sources that decide the dominant kernel's memory traffic."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None when the kernel sources changed
+    since those counters were taken."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("source_sha256") != source_digest():
+            return None
+        return int(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w_np, rows):
