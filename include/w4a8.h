@@ -55,7 +55,7 @@ typedef enum w4a8_status {
     W4A8_E_NULL = -1,       /* a required pointer is NULL                  */
     W4A8_E_SHAPE = -2,      /* M < 0, N <= 0, K <= 0, K % 128, N % 16, ld  */
     W4A8_E_ALIGN = -3,      /* a device pointer is not 16-byte aligned      */
-    W4A8_E_WORKSPACE = -4,  /* workspace missing or smaller than required   */
+    W4A8_E_WORKSPACE = -4,  /* workspace smaller than required              */
     W4A8_E_HIP = -5         /* a HIP launch or runtime call failed          */
 } w4a8_status;
 
@@ -127,10 +127,13 @@ w4a8_status quantize_act_per_token_i8(const uint16_t *x_fp16, int64_t M,
  * int32, row-major; when non-NULL the raw accumulators of the same main loop
  * are written too.
  * ws: workspace of at least gemm_w4a8_workspace_bytes(M, N, K) bytes, zeroed
- * by the caller once after allocation; every call leaves it zeroed again.
- * ws may be NULL only when that size is 0.  Calls that share one workspace
- * must be ordered (same stream, or synchronised): concurrent calls on one
- * workspace race.
+ * by the caller once after allocation; every call leaves its counters zeroed
+ * again.  It holds the split-K partial sums of decode shapes and the
+ * stream-K counters and partial tiles of prefill shapes.  ws may be NULL:
+ * the call then runs without splitting K (same results, slower for shapes
+ * whose tiles do not fill the GPU).  A non-NULL ws smaller than required is
+ * W4A8_E_WORKSPACE.  Calls that share one workspace must be ordered (same
+ * stream, or synchronised): concurrent calls on one workspace race.
  * ------------------------------------------------------------------------ */
 size_t gemm_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
 

@@ -69,9 +69,17 @@ def test_size_queries(lib):
         assert _lib.w4a8_packed_weight_bytes(N, K) == 0
     assert _lib.gemm_w4a8_workspace_bytes(0, 512, 512) == 0
     assert _lib.gemm_w4a8_workspace_bytes(1, 15, 512) == 0
-    for (M, N, K) in ((1, 4096, 4096), (32, 22016, 4096), (4096, 11008, 4096)):
-        ws = _lib.gemm_w4a8_workspace_bytes(M, N, K)
-        assert ws == 0 or ws >= M * N * 4
+    # decode plans (M <= 64) run unsplit by default
+    for (M, N, K) in ((1, 4096, 4096), (32, 22016, 4096)):
+        assert _lib.gemm_w4a8_workspace_bytes(M, N, K) == 0
+    if not _gpu_visible():   # the planner assumes 256 CUs when no device is present
+        # M=512, K=11008, N=4096: long K and 8 x 16 tiles of 64 x 256 fill half
+        # the CUs -> 256 stream-K ranges: the fixed 64 KB of counters, then two
+        # 64 x 256 INT32 partial slots per range
+        assert _lib.gemm_w4a8_workspace_bytes(512, 4096, 11008) == 65536 + 2 * 256 * 64 * 256 * 4
+        # K=4096 (32 groups): one workgroup per tile, no workspace
+        assert _lib.gemm_w4a8_workspace_bytes(4096, 11008, 4096) == 0
+        assert _lib.gemm_w4a8_workspace_bytes(256, 11008, 4096) == 0
 
 
 def _gpu_visible():
@@ -154,13 +162,19 @@ def test_gemm_validation(lib, monkeypatch):
     assert call(qx=MIS) == -3
     assert call(y=MIS) == -3
     assert call(acc=MIS) == -3
-    # a split-K plan without (or with too small) a workspace
+    # a split-K plan with too small a workspace (a NULL workspace is allowed:
+    # the call then runs unsplit)
     from w4a8_quantized_linear_amd import _lib
     monkeypatch.setenv("W4A8_DECODE_PLAN", "1,1,4")
     need = _lib.gemm_w4a8_workspace_bytes(1, 4096, 4096)
     assert need > 0
-    assert call(N=4096, K=4096) == -4
     assert call(N=4096, K=4096, ws=A, wsb=need - 1) == -4
+    # a stream-K prefill plan: the same rule
+    monkeypatch.delenv("W4A8_DECODE_PLAN")
+    monkeypatch.setenv("W4A8_PREFILL_P", "64")
+    need = _lib.gemm_w4a8_workspace_bytes(4096, 4096, 4096)
+    assert need > 64 * 2 * 256 * 256 * 4
+    assert call(M=4096, N=4096, K=4096, ws=A, wsb=need - 1) == -4
 
 
 def test_binding_raises_without_library(monkeypatch, tmp_path):

@@ -251,10 +251,10 @@ def test_splitk_equals_no_splitk_and_is_deterministic(M):
     for y, acc in results[1:]:
         assert np.array_equal(acc, results[0][1])
         assert np.array_equal(y, results[0][0])
-    # the workspace is left zeroed
+    # the workspace's counters are left zeroed (the partial slots are scratch)
     ws = _lib._ws_cache.get(torch.device(dev()))
     if ws is not None:
-        assert int(ws.count_nonzero()) == 0
+        assert int(ws[:65536].count_nonzero()) == 0
 
 
 def test_workspace_reuse_with_smaller_second_call():
@@ -273,7 +273,7 @@ def test_workspace_reuse_with_smaller_second_call():
         out = orc.linear(x, ref_w)
         assert np.array_equal(to_host(acc), out["acc"])
     ws = _lib._ws_cache.get(torch.device(dev()))
-    assert ws is None or int(ws.count_nonzero()) == 0
+    assert ws is None or int(ws[:65536].count_nonzero()) == 0
 
 
 @pytest.mark.parametrize("plan", ["1,2,1", "1,4,2", "2,4,1", "4,2,3", "1,2,1,4,4,1", "1,2,2,8,2,1"])
@@ -339,3 +339,94 @@ def test_prefill_ragged(tm, M, K, N):
     out = orc.linear(x, orc.quantize_weights(w))
     assert np.array_equal(to_host(acc), out["acc"])
     assert_y_close(f16_bits(y), out["y"], "prefill")
+
+
+# Stream-K: (tile, group) units split into P ranges, tiles finished by their
+# last contributor.  P from 1 (one workgroup does everything) to more ranges
+# than groups per tile (every tile split many ways); results are bit-exact
+# and deterministic, and the workspace counters are left at zero.
+@pytest.mark.parametrize("tm", ["4", "16"])
+@pytest.mark.parametrize("P", ["1", "5", "37", "256"])
+@pytest.mark.parametrize("M,K,N", [(300, 384, 272), (1100, 640, 304), (257, 1152, 1040)])
+def test_prefill_stream_k(tm, P, M, K, N):
+    import torch
+    from w4a8_quantized_linear_amd import _lib, gemm_w4a8, quantize_act_per_token_i8
+    say("prefill stream-K TM=%s P=%s M=%d K=%d N=%d" % (tm, P, M, K, N))
+    rng = np.random.default_rng(3 * M + 5 * K + N)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    wq = gpu_weights(w)
+    qx, sa = quantize_act_per_token_i8(to_dev(x))
+    out = orc.linear(x, orc.quantize_weights(w))
+    old = {k: os.environ.get(k) for k in ("W4A8_PREFILL_TM", "W4A8_PREFILL_P")}
+    os.environ["W4A8_PREFILL_TM"] = tm
+    os.environ["W4A8_PREFILL_P"] = P
+    try:
+        need = _lib.gemm_w4a8_workspace_bytes(M, N, K)
+        assert need > 0
+        ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+        accs = []
+        for rep in range(2):
+            acc = torch.full((M, N), 7, dtype=torch.int32, device=dev())
+            y = gemm_w4a8(qx, sa, wq["wpacked"], wq["s0"], N, acc_out=acc, ws=ws)
+            torch.cuda.synchronize()
+            accs.append(to_host(acc))
+            assert np.array_equal(accs[-1], out["acc"]), "rep %d" % rep
+            assert_y_close(f16_bits(y), out["y"], "stream-K")
+        assert int(to_host(ws[:65536]).astype(np.int64).sum()) == 0, "counters not reset"
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def test_workspace_shared_across_shapes_and_kernels():
+    """One workspace buffer serves calls of different shapes and both split
+    kernels in turn (stream-K prefill, split-K decode): the partial slots are
+    scratch, only the counters must stay zero, and every call is bit-exact."""
+    import torch
+    from w4a8_quantized_linear_amd import _lib, gemm_w4a8, quantize_act_per_token_i8
+    cases = [  # (M, K, N, env)
+        (1100, 640, 304, {"W4A8_PREFILL_TM": "4", "W4A8_PREFILL_P": "37"}),
+        (300, 1024, 2048, {"W4A8_PREFILL_TM": "16", "W4A8_PREFILL_P": "200"}),
+        (24, 1024, 2048, {"W4A8_DECODE_PLAN": "2,1,3"}),
+        (257, 1152, 1040, {"W4A8_PREFILL_TM": "8", "W4A8_PREFILL_P": "64"}),
+        (9, 1024, 512, {"W4A8_DECODE_PLAN": "1,2,4"}),
+        (1100, 640, 304, {"W4A8_PREFILL_TM": "4", "W4A8_PREFILL_P": "37"}),
+    ]
+    keys = ("W4A8_PREFILL_TM", "W4A8_PREFILL_P", "W4A8_DECODE_PLAN")
+    saved = {k: os.environ.get(k) for k in keys}
+    ws = None
+    try:
+        for (M, K, N, env) in cases:
+            say("shared workspace M=%d K=%d N=%d %s" % (M, K, N, env))
+            for k in keys:
+                os.environ.pop(k, None)
+            os.environ.update(env)
+            need = _lib.gemm_w4a8_workspace_bytes(M, N, K)
+            assert need > 0, env
+            if ws is None or ws.numel() < need:
+                old_ws = ws
+                ws = torch.zeros(max(need, 64 << 20), dtype=torch.uint8, device=dev())
+                if old_ws is not None:   # carry the scratch over: it must not matter
+                    ws[:old_ws.numel()] = old_ws
+            rng = np.random.default_rng(M + K + N)
+            w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+            x = rng.standard_normal((M, K)).astype(np.float16)
+            wq = gpu_weights(w)
+            qx, sa = quantize_act_per_token_i8(to_dev(x))
+            acc = torch.empty((M, N), dtype=torch.int32, device=dev())
+            y = gemm_w4a8(qx, sa, wq["wpacked"], wq["s0"], N, acc_out=acc, ws=ws)
+            torch.cuda.synchronize()
+            out = orc.linear(x, orc.quantize_weights(w))
+            assert np.array_equal(to_host(acc), out["acc"]), env
+            assert_y_close(f16_bits(y), out["y"], "shared workspace")
+            assert int(to_host(ws[:65536]).astype(np.int64).sum()) == 0, "counters not reset"
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v

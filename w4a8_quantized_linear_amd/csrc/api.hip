@@ -34,7 +34,7 @@ const char *w4a8_status_string(w4a8_status st)
     case W4A8_E_NULL: return "a required pointer is NULL";
     case W4A8_E_SHAPE: return "invalid shape (need M >= 0, N > 0, K > 0, K % 128 == 0, N % 16 == 0, ldx >= K, ldx % 8 == 0)";
     case W4A8_E_ALIGN: return "a device pointer is not 16-byte aligned";
-    case W4A8_E_WORKSPACE: return "workspace missing or smaller than gemm_w4a8_workspace_bytes()";
+    case W4A8_E_WORKSPACE: return "workspace smaller than gemm_w4a8_workspace_bytes()";
     case W4A8_E_HIP: return "HIP launch or runtime error";
     }
     return "unknown status";
@@ -111,8 +111,10 @@ w4a8_status gemm_w4a8(const int8_t *qx, const float *s_a, const void *wpacked,
     if (!aligned16(qx) || !aligned16(s_a) || !aligned16(wpacked) || !aligned16(s0_fp16) ||
         !aligned16(y_fp16) || (acc_out && !aligned16(acc_out)) || (ws && !aligned16(ws)))
         return W4A8_E_ALIGN;
-    const GemmPlan p = plan_gemm(M, N, K);
-    if (p.ws_bytes > 0 && (ws == nullptr || ws_bytes < p.ws_bytes))
+    GemmPlan p = plan_gemm(M, N, K);
+    if (p.ws_bytes > 0 && ws == nullptr)
+        p = plan_without_workspace(p);
+    if (p.ws_bytes > 0 && ws_bytes < p.ws_bytes)
         return W4A8_E_WORKSPACE;
     return hip_status(launch_gemm(p, qx, s_a, static_cast<const uint8_t *>(wpacked), s0_fp16, M,
                                   N, K, y_fp16, acc_out, ws, stream));

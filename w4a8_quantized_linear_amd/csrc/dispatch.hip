@@ -16,9 +16,11 @@ namespace w4a8 {
 bool decode_variant_exists(int mt, int nt, int waves, int depth, bool xs);
 size_t decode_lds_bytes(const GemmPlan &p, int64_t M, int64_t K);
 bool prefill_tm_supported(int tm);
+size_t prefill_ws_bytes(int tm, int P, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_prefill(const GemmPlan &p, const int8_t *qx, const float *s_a,
                                const uint8_t *stream_bytes, const uint16_t *s0, int64_t M,
-                               int64_t N, int64_t K, uint16_t *y, int32_t *acc_out, hipStream_t st);
+                               int64_t N, int64_t K, uint16_t *y, int32_t *acc_out, void *ws,
+                               hipStream_t st);
 hipError_t launch_gemm_decode(const GemmPlan &p, const int8_t *qx, const float *s_a,
                               const uint8_t *stream_bytes, const uint16_t *s0, int64_t M,
                               int64_t N, int64_t K, uint16_t *y, int32_t *acc_out, void *ws,
@@ -26,11 +28,13 @@ hipError_t launch_gemm_decode(const GemmPlan &p, const int8_t *qx, const float *
 
 namespace {
 
-size_t ws_size(int64_t M, int64_t N, int splitk, int64_t tiles)
+// decode split-K: the counters, then one 16 mt x 16 nt INT32 slot per (tile, split)
+size_t ws_size(const GemmPlan &p)
 {
-    if (splitk <= 1)
+    const int64_t tiles = p.m_blocks * p.n_blocks;
+    if (p.splitk <= 1 || tiles > kWsCounters)
         return 0;
-    return ((size_t)M * N * 4 + 255) / 256 * 256 + (size_t)tiles * 4;
+    return (size_t)kWsPartOffset + (size_t)tiles * p.splitk * 256 * p.mt * p.nt * 4;
 }
 
 // compute units of the current device (cached per device)
@@ -87,25 +91,42 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     }
 
     // many tokens: the matrix-core kernel with (16 TM) x 256 workgroup tiles.
-    // TM is chosen by a cost model: workgroup rounds on the CUs x TM x the
-    // relative time per MFMA at that TM (smaller tiles rebuild each weight
-    // for fewer tokens and pay the per-group overheads more often), with the
-    // factors taken from rocprofv3 sweeps over M = 128..4096 on MI355X.
-    // W4A8_PREFILL_TM=4|8|16 forces this kernel and its TM (at any M).
+    // Rules fitted to rocprofv3 sweeps (TM x stream-K on/off, M = 128..4096,
+    // the 7B and 70B shapes) on MI355X:
+    //  * long K (>= 64 groups) with few tiles: stream-K over all CUs, with the
+    //    largest-count tile (TM 4, else 8) that still leaves the CUs under
+    //    60% filled by whole tiles;
+    //  * otherwise one workgroup per tile, TM minimising workgroup rounds x
+    //    TM x the relative time per MFMA at that TM (1.0, 1.23, 1.75 for
+    //    TM 16, 8, 4: smaller tiles rebuild each weight for fewer tokens).
+    // W4A8_PREFILL_TM=4|8|16 forces this kernel and its TM (at any M);
+    // W4A8_PREFILL_P=n forces n stream-K ranges (0: one workgroup per tile).
+    const int64_t cus = num_cus();
+    const int64_t nblk = (ntiles * kTileN + 255) / 256;
+    auto tiles_of = [&](int t) { return (M + 16 * t - 1) / (16 * t) * nblk; };
     int tm = 0;
+    int64_t ranges = 0;
     if (const char *env = std::getenv("W4A8_PREFILL_TM"))
         tm = std::atoi(env);
-    if (!prefill_tm_supported(tm) && M > 64) {
-        const int64_t cus = num_cus();
-        const int64_t nblk = (ntiles * kTileN + 255) / 256;
-        const struct { int tm; double rel; } cand[] = {{16, 1.0}, {8, 1.23}, {4, 1.75}};
-        double best = 0;
-        for (const auto &c : cand) {
-            const int64_t tiles = (M + 16 * c.tm - 1) / (16 * c.tm) * nblk;
-            const double cost = (double)((tiles + cus - 1) / cus) * c.tm * c.rel;
-            if (tm == 0 || cost < best) {
-                tm = c.tm;
-                best = cost;
+    if (!prefill_tm_supported(tm)) {
+        tm = 0;
+        if (M > 64) {
+            if (G >= 64 && tiles_of(4) * 10 < cus * 6) {
+                tm = 4;
+                ranges = cus;
+            } else if (G >= 64 && tiles_of(8) * 10 < cus * 6) {
+                tm = 8;
+                ranges = cus;
+            } else {
+                const struct { int tm; double rel; } cand[] = {{16, 1.0}, {8, 1.23}, {4, 1.75}};
+                double best = 0;
+                for (const auto &c : cand) {
+                    const double cost = (double)((tiles_of(c.tm) + cus - 1) / cus) * c.tm * c.rel;
+                    if (tm == 0 || cost < best) {
+                        tm = c.tm;
+                        best = cost;
+                    }
+                }
             }
         }
     }
@@ -114,10 +135,12 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
         q.kind = 1;
         q.mt = tm;
         q.nt = 16;
-        q.splitk = 1;
         q.m_blocks = (M + 16 * tm - 1) / (16 * tm);
-        q.n_blocks = (ntiles * kTileN + 255) / 256;
-        q.ws_bytes = 0;
+        q.n_blocks = nblk;
+        if (const char *env = std::getenv("W4A8_PREFILL_P"))
+            ranges = std::max<int64_t>(0, std::min<int64_t>(std::atoll(env), tiles_of(tm) * G));
+        q.ws_bytes = prefill_ws_bytes(tm, (int)ranges, M, N, K);
+        q.splitk = q.ws_bytes > 0 ? (int)ranges : 0;
         return q;
     }
 
@@ -138,7 +161,16 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
                 p = q;
         }
     }
-    p.ws_bytes = ws_size(M, N, p.splitk, p.m_blocks * p.n_blocks);
+    if (p.splitk > 1 && p.m_blocks * p.n_blocks > kWsCounters)
+        p.splitk = 1;   // more tiles than counters: run unsplit
+    p.ws_bytes = ws_size(p);
+    return p;
+}
+
+GemmPlan plan_without_workspace(GemmPlan p)
+{
+    p.splitk = p.kind == 1 ? 0 : 1;
+    p.ws_bytes = 0;
     return p;
 }
 
@@ -154,7 +186,7 @@ hipError_t launch_gemm(const GemmPlan &p, const int8_t *qx, const float *s_a,
                      p.waves, p.depth, (int)p.xstage, (long long)p.n_blocks, p.splitk,
                      (long long)p.m_blocks);
     if (p.kind == 1)
-        return launch_gemm_prefill(p, qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, st);
+        return launch_gemm_prefill(p, qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, ws, st);
     return launch_gemm_decode(p, qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, ws, st);
 }
 

@@ -87,8 +87,8 @@ struct DecodeArgs {
     int splitk;
     uint16_t *y;
     int32_t *acc_out;
-    int32_t *ws_acc;     // [M, N] int32 (split-K only)
-    uint32_t *ws_cnt;    // one counter per (m-block, n-block)
+    int32_t *ws_part;    // split-K partial tiles: slot (tile, split) of 16 MT x 16 NT int32
+    uint32_t *ws_cnt;    // one arrival counter per (m-block, n-block)
 };
 
 // One ring slot: the loads of one pair of groups (2 x 128 k).
@@ -333,10 +333,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
         if (nt0 + t >= ntiles || m >= a.M)
             continue;
         if (a.splitk > 1) {
-#pragma unroll
-            for (int r = 0; r < 4; r++)
-                __hip_atomic_fetch_add(a.ws_acc + m * a.N + n + r, sum[r], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+            // this split's partial: row 16 mt + c, columns 16 t + 4 kb .. + 3
+            int32_t *slot = a.ws_part + (tile_id * a.splitk + blockIdx.y) * (256 * MT * NT);
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                slot, (short)0, 256 * MT * NT * 4, kBufFlags);
+            __builtin_amdgcn_raw_buffer_store_b128(sum, rs, ((16 * mt + c) * 16 * NT + 16 * t + 4 * kb) * 4, 0, 16);
         } else {
             const float sa = (i == i0) ? sa_e : a.s_a[m];
             const uint2 s0p = (i == i0) ? s0_e : *reinterpret_cast<const uint2 *>(a.s0 + n);
@@ -359,14 +360,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
         return;
 
     // ---- 6. split-K: the last workgroup of the tile applies the epilogue -------
-    // Every value that crosses workgroups moves through device-scope atomics,
-    // which are performed at the memory-side coherence point, so no cache
-    // writeback or invalidate is needed (an agent-scope fence would write back
-    // and invalidate the whole L2 of the XCD in every workgroup).  Ordering:
-    // each wave waits until its partial-sum atomics are acknowledged before
-    // the barrier, the counter increment is issued after the barrier, and the
-    // last arriver's read-and-clear exchanges are issued after it has seen the
-    // final count.
+    // Each split stores its partial tile into its own slot with agent-coherent
+    // (sc1) stores, which bypass the XCD's L2, so no cache writeback or
+    // invalidate is needed (an agent-scope fence would write back and
+    // invalidate the whole L2 of the XCD in every workgroup).  Ordering: each
+    // wave waits until its stores are acknowledged before the barrier, the
+    // counter increment is issued after the barrier, and the last arriver's
+    // sc1 loads of the other slots are issued after it has seen the final
+    // count.  It then resets the counter; the slots are scratch.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     __shared__ uint32_t arrival;
@@ -377,16 +378,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
     if (arrival != (uint32_t)(a.splitk - 1))
         return;
     const int ncols = (int)min<int64_t>(NT * kTileN, a.N - (int64_t)nt0 * kTileN);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        a.ws_part + tile_id * a.splitk * (256 * MT * NT), (short)0, a.splitk * 256 * MT * NT * 4, kBufFlags);
     for (int i = tid; i < mrows * ncols / 4; i += kThreads) {
         const int r = i / (ncols / 4);
         const int q = i - r * (ncols / 4);
         const int64_t m = m0 + r;
         const int64_t n = (int64_t)nt0 * kTileN + 4 * q;
-        int32_t *wp = a.ws_acc + m * a.N + n;
-        v4i sum;
-#pragma unroll
-        for (int e = 0; e < 4; e++)
-            sum[e] = __hip_atomic_exchange(wp + e, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v4i sum = {0, 0, 0, 0};
+        for (int sp = 0; sp < a.splitk; sp++)
+            sum += __builtin_amdgcn_raw_buffer_load_b128(rs, (r * 16 * NT + 4 * q) * 4,
+                                                        sp * (256 * MT * NT * 4), 16);
         const float sa = a.s_a[m];
         const uint2 s0p = *reinterpret_cast<const uint2 *>(a.s0 + n);
         const uint32_t s0w[2] = {s0p.x, s0p.y};
@@ -472,12 +474,11 @@ hipError_t launch_gemm_decode(const GemmPlan &p, const int8_t *qx, const float *
     a.splitk = p.splitk;
     a.y = y;
     a.acc_out = acc_out;
-    a.ws_acc = nullptr;
+    a.ws_part = nullptr;
     a.ws_cnt = nullptr;
     if (p.splitk > 1) {
-        a.ws_acc = reinterpret_cast<int32_t *>(ws);
-        size_t acc_bytes = ((size_t)M * N * 4 + 255) / 256 * 256;
-        a.ws_cnt = reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(ws) + acc_bytes);
+        a.ws_cnt = reinterpret_cast<uint32_t *>(ws);
+        a.ws_part = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(ws) + kWsPartOffset);
     }
     const size_t lds = decode_lds_bytes(p, M, K);
     if (lds == 0 || lds > 160 * 1024)

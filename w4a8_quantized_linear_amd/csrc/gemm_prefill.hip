@@ -105,9 +105,13 @@ struct PrefillArgs {
     const uint8_t *params;
     const uint16_t *s0;
     int64_t M, N, K;
-    int mblocks, nblocks, per_xcd;
+    int mblocks, nblocks;
+    int P;             // workgroups with work: each takes a balanced range of (tile, group) units
+    int per_xcd;       // launch grid / 8
     uint16_t *y;
     int32_t *acc_out;
+    uint32_t *cnt;     // one arrival counter per tile (zero between calls); null: P == tiles
+    int32_t *part;     // two partial-accumulator slots per workgroup
 };
 
 struct BSlot {
@@ -131,28 +135,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
                   kBDepth = C::kBDepth, kUnroll = C::kUnroll;
     extern __shared__ __align__(16) uint8_t smem[];
     float *sa_lds = reinterpret_cast<float *>(smem + kAStages * kAStage);
+    __shared__ uint32_t arrival;
 
     const int tid = threadIdx.x;
     const int l = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = l & 15, lk = l >> 4;      // operand row / 16-byte k-block of this lane
 
+    // Workgroup b runs on XCD b % 8; it takes range w of the P balanced
+    // ranges of (tile, group) units, so each XCD works through contiguous
+    // ranges.  With P equal to the tile count every range is one whole tile.
     const int b = blockIdx.x;
-    const int tile = (b % kXcds) * a.per_xcd + b / kXcds;
-    if (tile >= a.mblocks * a.nblocks)
+    const int w = (b % kXcds) * a.per_xcd + b / kXcds;
+    if (w >= a.P)
         return;
-    const int band = tile / (kBandM * a.nblocks);
-    const int bm0 = band * kBandM;
-    const int bh = min(kBandM, a.mblocks - bm0);
-    const int rt = tile - band * kBandM * a.nblocks;
-    const int nb = rt / bh;
-    const int mb = bm0 + (rt - nb * bh);
     const int K = (int)a.K;
     const int G = K / kGroup;
     const int G4 = (G + 3) / 4 * 4;
     const int ntiles = (int)(a.N / kTileN);
-    const int m0 = mb * BM;
-    const int nt0 = nb * (BN / 16) + wv * TN;   // first device tile of this wave
+    const int64_t units = (int64_t)a.mblocks * a.nblocks * G;
+    auto range_lo = [&](int64_t ww) { return ww * units / a.P; };
+    // workgroup whose range holds unit x: the largest ww with range_lo(ww) <= x
+    auto owner = [&](int64_t x) { return (int)(((x + 1) * a.P - 1) / units); };
+    const int64_t u_lo = range_lo(w), u_hi = range_lo(w + 1);
 
     // Rows past M and tiles past N fall outside the descriptors' ranges and
     // load as zeros; their outputs are never stored.
@@ -160,284 +165,346 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
     const __amdgpu_buffer_rsrc_t rw = rsrc(a.codes, code_bytes(a.N, a.K));
     const __amdgpu_buffer_rsrc_t rp = rsrc(a.params, param_bytes(a.N, a.K));
 
-    // activation tile loads: load j covers block row 32 j + tid / 8, chunk tid % 8
-    const int xrow0 = tid >> 3, xch = tid & 7;
-    const int xoff = (m0 + xrow0) * K + xch * 16;
-    // weight loads: tile nt0 + t, lane l; parameter dword of channel lr
-    const int woff = nt0 * G * kTileBytes + 16 * l;
-    const int poff = (nt0 * (G4 / 4) * 16 + lr) * 4;
+    // One segment per tile the range touches: groups [gs, ge) of the tile.
+    for (int64_t x = u_lo; x < u_hi;) {
+        const int tile = (int)(x / G);
+        const int gs = (int)(x - (int64_t)tile * G);
+        const int ge = (int)min<int64_t>(G, u_hi - (int64_t)tile * G);
+        x = (int64_t)tile * G + ge;
 
-    for (int i = tid; i < BM; i += kThreads)
-        sa_lds[i] = a.s_a[min<int64_t>(m0 + i, a.M - 1)];
+        const int band = tile / (kBandM * a.nblocks);
+        const int bm0 = band * kBandM;
+        const int bh = min(kBandM, a.mblocks - bm0);
+        const int rt = tile - band * kBandM * a.nblocks;
+        const int nb = rt / bh;
+        const int mb = bm0 + (rt - nb * bh);
+        const int m0 = mb * BM;
+        const int nt0 = nb * (BN / 16) + wv * TN;   // first device tile of this wave
+        const int glast = ge - 1;                    // loads past the segment re-read its last group
 
-    v4i xr[kAPre][kXChunks];   // activations of the next kAPre groups to store
-    auto xload = [&](v4i &dst, int g, int j) {
-        g = min(g, G - 1);                   // the last loads re-read a real group
-        dst = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff, j * (kThreads / 8) * K + g * kGroup, 0);
-    };
-    auto xstore = [&](uint8_t *stage, const v4i &src, int j) {
-        *reinterpret_cast<v4i *>(stage + swz(j * (kThreads / 8) + xrow0, xch)) = src;
-    };
-    auto bload_t = [&](BSlot &s, int g, int t) {
-        g = min(g, G - 1);
-        s.w[t] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff, (t * G + g) * kTileBytes, 2);
-        s.p[t] = __builtin_amdgcn_raw_buffer_load_b32(rp, poff, (t * (G4 / 4) + (g >> 2)) * 64, 0);
-    };
+        // activation tile loads: load j covers block row 32 j + tid / 8, chunk tid % 8
+        const int xrow0 = tid >> 3, xch = tid & 7;
+        const int xoff = (m0 + xrow0) * K + xch * 16;
+        // weight loads: tile nt0 + t, lane l; parameter dword of channel lr
+        const int woff = nt0 * G * kTileBytes + 16 * l;
+        const int poff = (nt0 * (G4 / 4) * 16 + lr) * 4;
 
-    Acc<TM> acc;
+        __syncthreads();   // the previous segment is done with the LDS
+        for (int i = tid; i < BM; i += kThreads)
+            sa_lds[i] = a.s_a[min<int64_t>(m0 + i, a.M - 1)];
+
+        v4i xr[kAPre][kXChunks];   // activations of the next kAPre groups to store
+        auto xload = [&](v4i &dst, int g, int j) {
+            g = min(g, glast);
+            dst = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff, j * (kThreads / 8) * K + g * kGroup, 0);
+        };
+        auto xstore = [&](uint8_t *stg, const v4i &src, int j) {
+            *reinterpret_cast<v4i *>(stg + swz(j * (kThreads / 8) + xrow0, xch)) = src;
+        };
+        auto bload_t = [&](BSlot &sl, int g, int t) {
+            g = min(g, glast);
+            sl.w[t] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff, (t * G + g) * kTileBytes, 2);
+            sl.p[t] = __builtin_amdgcn_raw_buffer_load_b32(rp, poff, (t * (G4 / 4) + (g >> 2)) * 64, 0);
+        };
+
+        Acc<TM> acc;
 #pragma unroll
-    for (int i = 0; i < TM; i++)
+        for (int i = 0; i < TM; i++)
 #pragma unroll
-        for (int t = 0; t < TN; t++)
-            acc(i, t) = v4i{0, 0, 0, 0};
+            for (int t = 0; t < TN; t++)
+                acc(i, t) = v4i{0, 0, 0, 0};
 
-    // lane's activation operand of row tile i, k-half h: row 16 i + lr, chunk
-    // 4 h + lk; the swizzle depends only on lr, so tile i is at + 2048 i
-    const int aoff[2] = {swz(lr, lk), swz(lr, 4 + lk)};
-    // byte offsets of the LDS stages read in this group, read next and
-    // written now; they rotate by one stage per group (uniform, in SGPRs)
-    int so_r = 0, so_n = kAStage, so_w = 2 * kAStage;
-    static_assert(kAStages == 3, "three rotating stage offsets");
+        // lane's activation operand of row tile i, k-half h: row 16 i + lr, chunk
+        // 4 h + lk; the swizzle depends only on lr, so tile i is at + 2048 i
+        const int aoff[2] = {swz(lr, lk), swz(lr, 4 + lk)};
+        // byte offsets of the LDS stages read in this group, read next and
+        // written now; they rotate by one stage per group (uniform, in SGPRs)
+        int so_r = 0, so_n = kAStage, so_w = 2 * kAStage;
+        static_assert(kAStages == 3, "three rotating stage offsets");
 
-    // Per-lane (s1, C) of the four tiles, for groups of either parity:
-    // s1 = (p & 15) + 1 and C = 257 (128 - z s1) mod 2^16 from the parameter
-    // byte p = (s1 - 1) | (z << 4).  Group g + 1's pairs are computed during
-    // group g's first phase.
-    uint32_t S1[2][TN], C16[2][TN], sc_p = 0, sc_s1 = 0;
+        // Per-lane (s1, C) of the four tiles, for groups of either parity:
+        // s1 = (p & 15) + 1 and C = 257 (128 - z s1) mod 2^16 from the
+        // parameter byte p = (s1 - 1) | (z << 4) (byte g % 4 of the dword).
+        // Group g + 1's pairs are computed during group g's first phase.
+        uint32_t S1[2][TN], C16[2][TN], sc_p = 0, sc_s1 = 0;
 
-    v4i af[kAhead + 1];   // activation operands in flight (one per row step)
-    v4i f0[TN], f1[TN];   // B operands: current phase / next phase
-    uint32_t ru = 0;      // rebuild in progress: masked codes of one dword
-    us2 rv = {0, 0};      // ... after the packed multiply-add
+        v4i af[kAhead + 1];   // activation operands in flight (one per row step)
+        v4i f0[TN], f1[TN];   // B operands: current phase / next phase
+        uint32_t ru = 0;      // rebuild in progress: masked codes of one dword
+        us2 rv = {0, 0};      // ... after the packed multiply-add
 
-    // One phase: the TM x TN MFMAs of k-half h of group g against B operands
-    // fc, with three instruction streams spread evenly over the MFMA slots
-    // (sched_barrier keeps the program order, so the matrix cores always have
-    // the next MFMA while the VALU and memory pipes work):
-    //   * rebuild of fn, the next phase's operands (k-half 1 of group g, then
-    //     k-half 0 of group g + 1), one dword in three steps: mask, packed
-    //     multiply-add, xor 0x80, i.e. (q4 s1 + 128 - z s1) ^ 0x80 per byte;
-    //   * phase 0: group g + 1's (s1, C) pairs, from ring slot sn;
-    //   * phase 1: LDS stores of group g + 2's activations, loads of group
-    //     g + 2 + kAPre's activations into the registers just stored, then
-    //     loads of group g + kBDepth's weights into slot s (loads leave in the
-    //     order they are waited for; vmcnt is in-order).
-    // The activation operand of row i + kAhead is read at the start of row
-    // step i, across phase and group boundaries.
-    auto phase = [&](const int h, const int u, const v4i (&fc)[TN], v4i (&fn)[TN], BSlot &s,
-                     const BSlot &sn, int g) {
-        constexpr int kSlots = TM * TN;
-        constexpr int kRebuild = 3 * 4 * TN;
-        constexpr int kSc = 2 * TN;
-        constexpr int kMem = 2 * kXChunks + TN;
-        const uint8_t *As = smem + so_r + aoff[h];
-        const uint8_t *An = h ? smem + so_n + aoff[0] : smem + so_r + aoff[1];
-        uint8_t *Ad = smem + so_w;
-        // operands being rebuilt: half hn of group gr, from slot sb, with the
-        // pairs of parity pr
-        const int hn = 1 - h;
-        const BSlot &sb = h ? sn : s;
-        const int pr = h ? (u + 1) & 1 : u & 1;
-        // fc was last written by VALU before the previous phase boundary
-        asm volatile("s_nop 4");
+        // One phase: the TM x TN MFMAs of k-half h of group g against B
+        // operands fc, with three instruction streams spread evenly over the
+        // MFMA slots (sched_barrier keeps the program order, so the matrix
+        // cores always have the next MFMA while the VALU and memory pipes work):
+        //   * rebuild of fn, the next phase's operands (k-half 1 of group g,
+        //     then k-half 0 of group g + 1), one dword in three steps: mask,
+        //     packed multiply-add, xor 0x80, i.e. (q4 s1 + 128 - z s1) ^ 0x80;
+        //   * phase 0: group g + 1's (s1, C) pairs, from ring slot sn;
+        //   * phase 1: LDS stores of group g + 2's activations, loads of group
+        //     g + 2 + kAPre's activations into the registers just stored,
+        //     then loads of group g + kBDepth's weights into slot s (loads
+        //     leave in the order they are waited for; vmcnt is in-order).
+        // The activation operand of row i + kAhead is read at the start of
+        // row step i, across phase and group boundaries.  u is the group's
+        // position in the unrolled loop; ring and register indices follow it.
+        auto phase = [&](const int h, const int u, const v4i (&fc)[TN], v4i (&fn)[TN], BSlot &s,
+                         const BSlot &sn, int g) {
+            constexpr int kSlots = TM * TN;
+            constexpr int kRebuild = 3 * 4 * TN;
+            constexpr int kSc = 2 * TN;
+            constexpr int kMem = 2 * kXChunks + TN;
+            const uint8_t *As = smem + so_r + aoff[h];
+            const uint8_t *An = h ? smem + so_n + aoff[0] : smem + so_r + aoff[1];
+            uint8_t *Ad = smem + so_w;
+            // operands being rebuilt: half hn, from slot sb, pairs of parity pr
+            const int hn = 1 - h;
+            const BSlot &sb = h ? sn : s;
+            const int pr = h ? (u + 1) & 1 : u & 1;
+            // fc was last written by VALU before the previous phase boundary
+            asm volatile("s_nop 4");
 #pragma unroll
-        for (int k = 0; k < kSlots; k++) {
-            const int i = k / TN, t = k % TN;
-            const v4i &av = af[i % (kAhead + 1)];
-            mfma_acc(acc(i, t), av, fc[t]);
-            if (t == 0) {
-                const int ir = i + kAhead;
-                af[ir % (kAhead + 1)] = *reinterpret_cast<const v4i *>(
-                    ir < TM ? As + 2048 * ir : An + 2048 * (ir - TM));
-            }
-            // (slot k runs ops [k n / kSlots, (k + 1) n / kSlots) of a stream
-            // of n ops: at most ceil(n / kSlots) of them, a constant bound)
+            for (int k = 0; k < kSlots; k++) {
+                const int i = k / TN, t = k % TN;
+                const v4i &av = af[i % (kAhead + 1)];
+                mfma_acc(acc(i, t), av, fc[t]);
+                if (t == 0) {
+                    const int ir = i + kAhead;
+                    af[ir % (kAhead + 1)] = *reinterpret_cast<const v4i *>(
+                        ir < TM ? As + 2048 * ir : An + 2048 * (ir - TM));
+                }
+                // (slot k runs ops [k n / kSlots, (k + 1) n / kSlots) of a
+                // stream of n ops: at most ceil(n / kSlots), a constant bound)
 #pragma unroll
-            for (int q = 0; q < (kRebuild + kSlots - 1) / kSlots; q++) {
-                const int o = k * kRebuild / kSlots + q;
-                if (o >= (k + 1) * kRebuild / kSlots)
-                    break;
-                const int j = o / 3, tt = j >> 2, d = j & 3;
-                if (o % 3 == 0) {
-                    ru = ((uint32_t)sb.w[tt][d] >> (4 * hn)) & 0x0F0F0F0Fu;
-                } else if (o % 3 == 1) {
-                    const us2 Sv = {(unsigned short)S1[pr][tt], (unsigned short)S1[pr][tt]};
-                    const us2 Cv = {(unsigned short)C16[pr][tt], (unsigned short)C16[pr][tt]};
-                    rv = __builtin_bit_cast(us2, ru) * Sv + Cv;
+                for (int q = 0; q < (kRebuild + kSlots - 1) / kSlots; q++) {
+                    const int o = k * kRebuild / kSlots + q;
+                    if (o >= (k + 1) * kRebuild / kSlots)
+                        break;
+                    const int j = o / 3, tt = j >> 2, d = j & 3;
+                    if (o % 3 == 0) {
+                        ru = ((uint32_t)sb.w[tt][d] >> (4 * hn)) & 0x0F0F0F0Fu;
+                    } else if (o % 3 == 1) {
+                        const us2 Sv = {(unsigned short)S1[pr][tt], (unsigned short)S1[pr][tt]};
+                        const us2 Cv = {(unsigned short)C16[pr][tt], (unsigned short)C16[pr][tt]};
+                        rv = __builtin_bit_cast(us2, ru) * Sv + Cv;
+                    } else {
+                        fn[tt][d] = (int)(__builtin_bit_cast(uint32_t, rv) ^ 0x80808080u);
+                    }
+                }
+                if (h == 0) {
+#pragma unroll
+                    for (int q = 0; q < (kSc + kSlots - 1) / kSlots; q++) {
+                        const int o = k * kSc / kSlots + q;
+                        if (o >= (k + 1) * kSc / kSlots)
+                            break;
+                        const int tt = o >> 1;
+                        if ((o & 1) == 0) {
+                            sc_p = (sn.p[tt] >> (8 * ((g + 1) & 3))) & 0xFFu;
+                            sc_s1 = (sc_p & 15u) + 1u;
+                        } else {
+                            S1[(u + 1) & 1][tt] = sc_s1;
+                            C16[(u + 1) & 1][tt] = ((128u - (sc_p >> 4) * sc_s1) * 257u) & 0xFFFFu;
+                        }
+                    }
                 } else {
-                    fn[tt][d] = (int)(__builtin_bit_cast(uint32_t, rv) ^ 0x80808080u);
-                }
-            }
-            if (h == 0) {
 #pragma unroll
-                for (int q = 0; q < (kSc + kSlots - 1) / kSlots; q++) {
-                    const int o = k * kSc / kSlots + q;
-                    if (o >= (k + 1) * kSc / kSlots)
-                        break;
-                    const int tt = o >> 1;
-                    if ((o & 1) == 0) {
-                        sc_p = (sn.p[tt] >> (8 * ((u + 1) & 3))) & 0xFFu;
-                        sc_s1 = (sc_p & 15u) + 1u;
-                    } else {
-                        S1[(u + 1) & 1][tt] = sc_s1;
-                        C16[(u + 1) & 1][tt] = ((128u - (sc_p >> 4) * sc_s1) * 257u) & 0xFFFFu;
+                    for (int q = 0; q < (kMem + kSlots - 1) / kSlots; q++) {
+                        const int o = k * kMem / kSlots + q;
+                        if (o >= (k + 1) * kMem / kSlots)
+                            break;
+                        if (o < kXChunks) {
+                            xstore(Ad, xr[(u + 2) % kAPre][o], o);
+                        } else if (o < 2 * kXChunks) {
+                            xload(xr[(u + 2) % kAPre][o - kXChunks], g + 2 + kAPre, o - kXChunks);
+                        } else {
+                            bload_t(s, g + kBDepth, o - 2 * kXChunks);
+                        }
                     }
                 }
-            } else {
-#pragma unroll
-                for (int q = 0; q < (kMem + kSlots - 1) / kSlots; q++) {
-                    const int o = k * kMem / kSlots + q;
-                    if (o >= (k + 1) * kMem / kSlots)
-                        break;
-                    if (o < kXChunks) {
-                        xstore(Ad, xr[(u + 2) % kAPre][o], o);
-                    } else if (o < 2 * kXChunks) {
-                        xload(xr[(u + 2) % kAPre][o - kXChunks], g + 2 + kAPre, o - kXChunks);
-                    } else {
-                        bload_t(s, g + kBDepth, o - 2 * kXChunks);
-                    }
-                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
+        };
+
+        // One group g (position u in the unrolled loop) on ring slot s
+        // (holding group g) and slot sn (group g + 1), then the barrier.
+        // Before it, this wave's LDS stores must be complete (the oldest LDS
+        // operations: everything but the kAhead operand reads of the next
+        // group, which read a stage completed a group earlier).  The stores
+        // of group g land in stage (g + 2) % 3, first read at the end of
+        // group g + 1; the stage read in group g is rewritten in group g + 1.
+        auto group = [&](const int u, BSlot &s, BSlot &sn, int g) {
+            phase(0, u, f0, f1, s, sn, g);
+            phase(1, u, f1, f0, s, sn, g);   // past the segment's end the rebuild is unused
+            asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(kAhead) : "memory");
+            const int so = so_r;
+            so_r = so_n;
+            so_n = so_w;
+            so_w = so;
+        };
+
+        // prologue: groups gs and gs + 1's activations into LDS, the next
+        // kAPre groups in registers, the first kBDepth groups of weights in
+        // flight, group gs's (s1, C), first operands and first operand reads
+        BSlot ring[kBDepth];
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+#pragma unroll
+            for (int j = 0; j < kXChunks; j++)
+                xload(xr[0][j], gs + q, j);
+#pragma unroll
+            for (int j = 0; j < kXChunks; j++)
+                xstore(smem + q * kAStage, xr[0][j], j);
         }
-    };
+#pragma unroll
+        for (int q = 2; q < 2 + kAPre; q++)
+#pragma unroll
+            for (int j = 0; j < kXChunks; j++)
+                xload(xr[q % kAPre][j], gs + q, j);
+#pragma unroll
+        for (int u = 0; u < kBDepth; u++)
+#pragma unroll
+            for (int t = 0; t < TN; t++)
+                bload_t(ring[u], gs + u, t);
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < TN; t++) {
+            const uint32_t p = (ring[0].p[t] >> (8 * (gs & 3))) & 0xFFu;
+            S1[0][t] = (p & 15u) + 1u;
+            C16[0][t] = ((128u - (p >> 4) * S1[0][t]) * 257u) & 0xFFFFu;
+            const us2 Sv = {(unsigned short)S1[0][t], (unsigned short)S1[0][t]};
+            const us2 Cv = {(unsigned short)C16[0][t], (unsigned short)C16[0][t]};
+#pragma unroll
+            for (int d = 0; d < 4; d++) {
+                const us2 v = __builtin_bit_cast(us2, (uint32_t)ring[0].w[t][d] & 0x0F0F0F0Fu) * Sv + Cv;
+                f0[t][d] = (int)(__builtin_bit_cast(uint32_t, v) ^ 0x80808080u);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kAhead; i++)
+            af[i] = *reinterpret_cast<const v4i *>(smem + so_r + aoff[0] + 2048 * i);
 
-    // One group g (position u in the unrolled loop) on ring slot s (holding
-    // group g) and slot sn (group g + 1), then the barrier.  Before it, this
-    // wave's LDS stores must be complete (the oldest LDS operations:
-    // everything but the kAhead operand reads of the next group, which read a
-    // stage completed a group earlier).  The stores of group g land in stage
-    // (g + 2) % 3, first read at the end of group g + 1; the stage read in
-    // group g is rewritten in group g + 1.
-    auto group = [&](const int u, BSlot &s, BSlot &sn, int g) {
-        phase(0, u, f0, f1, s, sn, g);
-        phase(1, u, f1, f0, s, sn, g);   // past the last group the rebuild is unused
-        asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(kAhead) : "memory");
-        const int so = so_r;
-        so_r = so_n;
-        so_n = so_w;
-        so_w = so;
-    };
+        // main loop, unrolled so every ring index is static; the loads are
+        // unconditional (clamped to the segment's last group), also in the
+        // tail, whose groups may still need weights refilled kBDepth back
+        int g = gs;
+        for (; g + kUnroll <= ge; g += kUnroll) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; u++)
+                group(u, ring[u % kBDepth], ring[(u + 1) % kBDepth], g + u);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll - 1; u++) {
+            if (g + u < ge)
+                group(u, ring[u % kBDepth], ring[(u + 1) % kBDepth], g + u);
+        }
+        // the operand reads issued past the segment's end are never used
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
-    // prologue: groups 0 and 1's activations into LDS, groups 2 .. 1 + kAPre
-    // in registers, the first kBDepth groups of weights in flight, group 0's
-    // (s1, C), first operands and first activation operand reads
-    BSlot ring[kBDepth];
+        // MFMA results are read by VALU below: cover the longest result latency
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+
+        // ---- a tile split over several ranges: every contributor stores its
+        // partial accumulators; the last to arrive adds the others' and runs
+        // the epilogue.  Partials move through agent-coherent (sc1) stores and
+        // loads; each wave waits for its stores before the barrier, the
+        // arrival count is taken after it, and the last arriver's loads are
+        // issued after it has seen the final count.  No workgroup waits on
+        // another.
+        const int c_lo = owner((int64_t)tile * G), c_hi = owner((int64_t)tile * G + G - 1);
+        if (c_lo != c_hi) {
+            constexpr int kSlotInts = TM * TN * kWaves * 64 * 4;
+            auto slot_of = [&](int ww) {
+                const int first = (int)(range_lo(ww) / G);
+                return a.part + (size_t)(2 * ww + (first == tile ? 0 : 1)) * kSlotInts;
+            };
+            const int pbase = ((wv * TM) * TN * 64 + l) * 16;   // lane's bytes in a slot
+            {
+                const __amdgpu_buffer_rsrc_t rs = rsrc(slot_of(w), (int64_t)kSlotInts * 4);
 #pragma unroll
-    for (int q = 0; q < 2; q++) {
+                for (int i = 0; i < TM; i++)
 #pragma unroll
-        for (int j = 0; j < kXChunks; j++)
-            xload(xr[0][j], q, j);
+                    for (int t = 0; t < TN; t++)
+                        __builtin_amdgcn_raw_buffer_store_b128(acc(i, t), rs, pbase, (i * TN + t) * 1024, 16);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (tid == 0)
+                arrival = __hip_atomic_fetch_add(a.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            if (arrival != (uint32_t)(c_hi - c_lo))
+                continue;
+            for (int ww = c_lo; ww <= c_hi; ww++) {
+                if (ww == w)
+                    continue;
+                const __amdgpu_buffer_rsrc_t rs = rsrc(slot_of(ww), (int64_t)kSlotInts * 4);
 #pragma unroll
-        for (int j = 0; j < kXChunks; j++)
-            xstore(smem + q * kAStage, xr[0][j], j);
-    }
+                for (int i = 0; i < TM; i++)
 #pragma unroll
-    for (int q = 2; q < 2 + kAPre; q++)
-#pragma unroll
-        for (int j = 0; j < kXChunks; j++)
-            xload(xr[q % kAPre][j], q, j);
-#pragma unroll
-    for (int u = 0; u < kBDepth; u++)
+                    for (int t = 0; t < TN; t++)
+                        acc(i, t) += __builtin_amdgcn_raw_buffer_load_b128(rs, pbase, (i * TN + t) * 1024, 16);
+            }
+            if (tid == 0)
+                __hip_atomic_store(a.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+
+        // ---- epilogue.  Lane l holds rows 16 i + 4 (l / 16) + r, column
+        // 16 t + l % 16 of the wave's slice.  y = fp16((acc s_a) s0) goes
+        // through LDS, half a tile at a time, so that global stores are whole
+        // 16-byte pieces of output rows.  The INT32 accumulators (an optional
+        // output) are stored directly.
+        float s0f[TN];
 #pragma unroll
         for (int t = 0; t < TN; t++)
-            bload_t(ring[u], u, t);
-    __syncthreads();
+            s0f[t] = (float)__builtin_bit_cast(_Float16, a.s0[min(nt0 + t, ntiles - 1) * 16 + lr]);
+        if (a.acc_out) {
 #pragma unroll
-    for (int t = 0; t < TN; t++) {
-        const uint32_t p = ring[0].p[t] & 0xFFu;
-        S1[0][t] = (p & 15u) + 1u;
-        C16[0][t] = ((128u - (p >> 4) * S1[0][t]) * 257u) & 0xFFFFu;
-        const us2 Sv = {(unsigned short)S1[0][t], (unsigned short)S1[0][t]};
-        const us2 Cv = {(unsigned short)C16[0][t], (unsigned short)C16[0][t]};
+            for (int i = 0; i < TM; i++) {
 #pragma unroll
-        for (int d = 0; d < 4; d++) {
-            const us2 v = __builtin_bit_cast(us2, (uint32_t)ring[0].w[t][d] & 0x0F0F0F0Fu) * Sv + Cv;
-            f0[t][d] = (int)(__builtin_bit_cast(uint32_t, v) ^ 0x80808080u);
-        }
-    }
+                for (int t = 0; t < TN; t++) {
+                    const int64_t n = (int64_t)(nt0 + t) * 16 + lr;
 #pragma unroll
-    for (int i = 0; i < kAhead; i++)
-        af[i] = *reinterpret_cast<const v4i *>(smem + so_r + aoff[0] + 2048 * i);
-
-    // main loop, unrolled so every ring index is static; the loads are
-    // unconditional (clamped to the last group), also in the tail, whose
-    // groups may still need the weights refilled kBDepth groups back
-    int g = 0;
-    for (; g + kUnroll <= G; g += kUnroll) {
-#pragma unroll
-        for (int u = 0; u < kUnroll; u++)
-            group(u, ring[u % kBDepth], ring[(u + 1) % kBDepth], g + u);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll - 1; u++) {
-        if (g + u < G)
-            group(u, ring[u % kBDepth], ring[(u + 1) % kBDepth], g + u);
-    }
-    // the operand reads issued for group G (past the end) are never used
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-
-    // MFMA results are read by VALU below: cover the longest result latency
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
-
-    // ---- epilogue.  Lane l holds rows 16 i + 4 (l / 16) + r, column
-    // 16 t + l % 16 of the wave's slice.  y = fp16((acc s_a) s0) goes through
-    // LDS, half a tile at a time, so that global stores are whole 16-byte
-    // pieces of output rows; the stages are free once every wave has passed
-    // the barrier.  The INT32 accumulators (an optional output) are stored
-    // directly.
-    float s0f[TN];
-#pragma unroll
-    for (int t = 0; t < TN; t++)
-        s0f[t] = (float)__builtin_bit_cast(_Float16, a.s0[min(nt0 + t, ntiles - 1) * 16 + lr]);
-    if (a.acc_out) {
-#pragma unroll
-        for (int i = 0; i < TM; i++) {
-#pragma unroll
-            for (int t = 0; t < TN; t++) {
-                const int64_t n = (int64_t)(nt0 + t) * 16 + lr;
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const int64_t m = (int64_t)m0 + 16 * i + 4 * lk + r;
-                    if (nt0 + t < ntiles && m < a.M)
-                        a.acc_out[m * a.N + n] = acc(i, t)[r];
+                    for (int r = 0; r < 4; r++) {
+                        const int64_t m = (int64_t)m0 + 16 * i + 4 * lk + r;
+                        if (nt0 + t < ntiles && m < a.M)
+                            a.acc_out[m * a.N + n] = acc(i, t)[r];
+                    }
                 }
             }
         }
-    }
-    constexpr int kYRow = BN * 2 + 16;    // padded LDS row of the fp16 tile (bytes)
-    constexpr int kHalf = BM / 2;
-    const int ncol0 = nb * BN;              // first output column of the tile
-    __syncthreads();
-#pragma unroll
-    for (int half = 0; half < 2; half++) {
-#pragma unroll
-        for (int ii = 0; ii < TM / 2; ii++) {
-            const int i = half * (TM / 2) + ii;
-#pragma unroll
-            for (int t = 0; t < TN; t++) {
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const int ml = 16 * i + 4 * lk + r;
-                    const float yv = ((float)acc(i, t)[r] * sa_lds[ml]) * s0f[t];
-                    *reinterpret_cast<_Float16 *>(smem + (ml - half * kHalf) * kYRow +
-                                                  (wv * 64 + 16 * t + lr) * 2) = (_Float16)yv;
-                }
-            }
-        }
+        constexpr int kYRow = BN * 2 + 16;    // padded LDS row of the fp16 tile (bytes)
+        constexpr int kHalf = BM / 2;
+        const int ncol0 = nb * BN;              // first output column of the tile
         __syncthreads();
-        // kHalf rows x 32 pieces of 16 bytes; N is a multiple of 16, so a
-        // piece is wholly inside or wholly past the last column
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+#pragma unroll
+            for (int ii = 0; ii < TM / 2; ii++) {
+                const int i = half * (TM / 2) + ii;
+#pragma unroll
+                for (int t = 0; t < TN; t++) {
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        const int ml = 16 * i + 4 * lk + r;
+                        const float yv = ((float)acc(i, t)[r] * sa_lds[ml]) * s0f[t];
+                        *reinterpret_cast<_Float16 *>(smem + (ml - half * kHalf) * kYRow +
+                                                      (wv * 64 + 16 * t + lr) * 2) = (_Float16)yv;
+                    }
+                }
+            }
+            __syncthreads();
+            // kHalf rows x 32 pieces of 16 bytes; N is a multiple of 16, so a
+            // piece is wholly inside or wholly past the last column
 #pragma unroll 4
-        for (int c = tid; c < kHalf * (BN / 8); c += kThreads) {
-            const int row = c / (BN / 8), pc = c % (BN / 8);
-            const int64_t m = (int64_t)m0 + half * kHalf + row;
-            const int64_t n = (int64_t)ncol0 + 8 * pc;
-            if (m < a.M && n < a.N)
-                *reinterpret_cast<v4i *>(a.y + m * a.N + n) =
-                    *reinterpret_cast<const v4i *>(smem + row * kYRow + 16 * pc);
+            for (int c = tid; c < kHalf * (BN / 8); c += kThreads) {
+                const int row = c / (BN / 8), pc = c % (BN / 8);
+                const int64_t m = (int64_t)m0 + half * kHalf + row;
+                const int64_t n = (int64_t)ncol0 + 8 * pc;
+                if (m < a.M && n < a.N)
+                    *reinterpret_cast<v4i *>(a.y + m * a.N + n) =
+                        *reinterpret_cast<const v4i *>(smem + row * kYRow + 16 * pc);
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
 }
 
@@ -448,11 +515,13 @@ size_t lds_bytes()
 }
 
 // The kernel addresses activations with 32-bit buffer offsets, so M is cut
-// into launches of at most 2^31 activation bytes each.
+// into launches of at most 2^31 activation bytes each.  P = 0 runs one
+// workgroup per tile; P > 0 splits the (tile, group) units into P balanced
+// ranges (stream-K), which needs the workspace laid out by prefill_ws_bytes.
 template <int TM>
-hipError_t launch_tm(const int8_t *qx, const float *s_a, const uint8_t *stream_bytes,
+hipError_t launch_tm(int P, const int8_t *qx, const float *s_a, const uint8_t *stream_bytes,
                      const uint16_t *s0, int64_t M, int64_t N, int64_t K, uint16_t *y,
-                     int32_t *acc_out, hipStream_t st)
+                     int32_t *acc_out, void *ws, hipStream_t st)
 {
     constexpr int BM = Cfg<TM>::BM;
     static bool attr_set = false;
@@ -481,8 +550,18 @@ hipError_t launch_tm(const int8_t *qx, const float *s_a, const uint8_t *stream_b
         a.acc_out = acc_out ? acc_out + r0 * N : nullptr;
         a.mblocks = (int)((mr + BM - 1) / BM);
         a.nblocks = (int)((N + BN - 1) / BN);
-        const int tiles = a.mblocks * a.nblocks;
-        a.per_xcd = (tiles + kXcds - 1) / kXcds;
+        const int64_t tiles = (int64_t)a.mblocks * a.nblocks;
+        const int64_t units = tiles * (K / kGroup);
+        if (P > 0 && ws != nullptr && tiles <= kWsCounters) {
+            a.P = (int)std::min<int64_t>(P, units);
+            a.cnt = reinterpret_cast<uint32_t *>(ws);
+            a.part = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(ws) + kWsPartOffset);
+        } else {
+            a.P = (int)tiles;
+            a.cnt = nullptr;
+            a.part = nullptr;
+        }
+        a.per_xcd = (a.P + kXcds - 1) / kXcds;
         hipLaunchKernelGGL(gemm_prefill_kernel<TM>, dim3((unsigned)(a.per_xcd * kXcds)),
                            dim3(kThreads), lds, st, a);
         hipError_t e = hipGetLastError();
@@ -496,14 +575,30 @@ hipError_t launch_tm(const int8_t *qx, const float *s_a, const uint8_t *stream_b
 
 bool prefill_tm_supported(int tm) { return tm == 4 || tm == 8 || tm == 16; }
 
+// Stream-K workspace: the counters (one per tile; at most kWsCounters tiles
+// per launch), then two partial-accumulator slots of 16 TM x 256 INT32 per range.
+size_t prefill_ws_bytes(int tm, int P, int64_t M, int64_t N, int64_t K)
+{
+    if (P <= 0 || !prefill_tm_supported(tm))
+        return 0;
+    const int64_t bm = 16 * tm;
+    const int64_t rows_max = (0x7FFFFFFF / K - bm) / bm * bm;
+    const int64_t tiles = (std::min<int64_t>(M, rows_max) + bm - 1) / bm * ((N + BN - 1) / BN);
+    if (tiles > kWsCounters)
+        return 0;
+    return (size_t)kWsPartOffset + (size_t)2 * P * bm * BN * 4;
+}
+
 hipError_t launch_gemm_prefill(const GemmPlan &p, const int8_t *qx, const float *s_a,
                                const uint8_t *stream_bytes, const uint16_t *s0, int64_t M,
-                               int64_t N, int64_t K, uint16_t *y, int32_t *acc_out, hipStream_t st)
+                               int64_t N, int64_t K, uint16_t *y, int32_t *acc_out, void *ws,
+                               hipStream_t st)
 {
+    const int P = p.splitk > 1 ? p.splitk : 0;
     switch (p.mt) {
-    case 4: return launch_tm<4>(qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, st);
-    case 8: return launch_tm<8>(qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, st);
-    case 16: return launch_tm<16>(qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, st);
+    case 4: return launch_tm<4>(P, qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, ws, st);
+    case 8: return launch_tm<8>(P, qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, ws, st);
+    case 16: return launch_tm<16>(P, qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, ws, st);
     }
     return hipErrorInvalidValue;
 }

@@ -54,12 +54,23 @@ hipError_t launch_weight_quant(const float *w, int64_t N, int64_t K, uint8_t *st
 hipError_t launch_weight_unpack(const uint8_t *stream_bytes, int64_t N, int64_t K,
                                 uint8_t *q4_canon, uint8_t *s1, uint8_t *z, hipStream_t st);
 
+// GEMM workspace (split-K of decode shapes, stream-K of prefill shapes).  One
+// fixed layout for every call, so that calls of different shapes may share a
+// buffer: kWsCounters arrival counters at the front (the only part that must
+// be zero between calls; every call leaves them zero), then partial-sum
+// slots from kWsPartOffset on, which are scratch (written before they are
+// read, never assumed zero).  Plans with more output tiles than counters run
+// unsplit.
+constexpr int64_t kWsCounters = 16384;
+constexpr int64_t kWsPartOffset = kWsCounters * 4;
+
 // GEMM plan: which kernel, its tile shape and the split-K factor.
 struct GemmPlan {
-    int kind;        // 0 = decode (weights streamed, split-K), 1 = prefill (LDS tiles)
-    int mt;          // 16-row m-tiles per workgroup (decode)
+    int kind;        // 0 = decode (weights streamed, split-K), 1 = prefill (matrix-core tiles)
+    int mt;          // 16-row m-tiles per workgroup (decode); TM, 16-row tiles per wave (prefill)
     int nt;          // 16-column n-tiles per workgroup (decode)
-    int splitk;      // number of K slices across workgroups (decode)
+    int splitk;      // decode: K slices across workgroups; prefill: stream-K ranges (0: one
+                     // workgroup per tile)
     int waves;       // waves per workgroup, splitting the slice (decode)
     int depth;       // pairs of groups in flight per wave (decode)
     bool xstage;     // activation rows staged in LDS (decode, few tokens)
@@ -69,6 +80,9 @@ struct GemmPlan {
 };
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
+
+// The same computation without a workspace (no split-K, no stream-K).
+GemmPlan plan_without_workspace(GemmPlan p);
 
 hipError_t launch_gemm(const GemmPlan &p, const int8_t *qx, const float *s_a,
                        const uint8_t *stream_bytes, const uint16_t *s0, int64_t M, int64_t N,
