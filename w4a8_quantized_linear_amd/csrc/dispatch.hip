@@ -69,21 +69,47 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     const int64_t ntiles = N / kTileN;
     const int64_t G = num_groups(K);
     const int64_t P = (G + 1) / 2;
-    // Rule fitted to rocprofv3 sweeps of the 7B decode shapes on MI355X: one
-    // n-tile per workgroup for up to 16 tokens (the activation rows staged in
-    // LDS when they fit), wider n-blocks for 17..32 tokens so that each
-    // activation operand feeds more weight tiles.
-    p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    p.m_blocks = (M + 16 * p.mt - 1) / (16 * p.mt);
-    p.nt = 1;
-    if (p.mt == 2)
-        p.nt = ntiles >= 512 ? 4 : (ntiles >= 384 ? 2 : 1);
-    p.n_blocks = (ntiles + p.nt - 1) / p.nt;
+    // Rules fitted to rocprofv3 sweeps of the decode plans over the 7B and 70B
+    // shapes (M = 1..64) on MI355X.  Few tokens: one n-tile per workgroup,
+    // the activation rows staged in LDS when they fit.  Large weight streams
+    // (>= 512 n-tiles, or >= 100 MB at 2..8 tokens): two n-tiles per workgroup
+    // and a 2-way K split, which doubles the weight bytes in flight per CU.
+    // 17..32 tokens: two m-tiles, wide n-blocks (each activation operand
+    // feeds more weight tiles) and a 4-way K split for long K.  33..64
+    // tokens: four m-tiles and four n-tiles for long K and wide N, else two
+    // m-blocks of two m-tiles; the widest N goes to the matrix-core kernel.
+    const double wbytes = (double)N * K / 2;
     p.splitk = 1;
     p.waves = 4;
     p.depth = 2;
     p.xstage = false;
-    if (p.mt == 1) {
+    if (M <= 16) {
+        p.mt = 1;
+        p.nt = 1;
+        if (M > 1 && ((M > 8 && ntiles >= 512) || (M <= 8 && wbytes >= 100e6))) {
+            p.nt = 2;
+            p.splitk = 2;
+        }
+    } else if (M <= 32) {
+        p.mt = 2;
+        p.nt = ntiles >= 512 ? 4 : (ntiles >= 384 ? 2 : 1);
+        if (G >= 86) {
+            p.nt = 4;
+            p.splitk = 4;
+        }
+    } else if (K >= 8192 && N >= 8192) {
+        p.mt = 4;
+        p.nt = 4;
+        p.splitk = K >= 16384 ? 2 : 1;
+    } else {
+        p.mt = 2;
+        p.nt = 4;
+        p.splitk = ntiles <= 256 ? 2 : 1;
+    }
+    p.splitk = (int)std::min<int64_t>(p.splitk, P);
+    p.m_blocks = (M + 16 * p.mt - 1) / (16 * p.mt);
+    p.n_blocks = (ntiles + p.nt - 1) / p.nt;
+    if (p.mt == 1 && p.splitk == 1) {
         GemmPlan q = p;
         q.xstage = true;
         if (launchable(q, M, K) && decode_lds_bytes(q, M, K) <= 64 * 1024)
@@ -110,7 +136,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
         tm = std::atoi(env);
     if (!prefill_tm_supported(tm)) {
         tm = 0;
-        if (M > 64) {
+        if (M > 32 && M <= 64 && N >= 32768)
+            tm = 4;   // 33..64 tokens on the widest N: activations shared through LDS
+        else if (M > 64) {
             if (G >= 64 && tiles_of(4) * 10 < cus * 6) {
                 tm = 4;
                 ranges = cus;

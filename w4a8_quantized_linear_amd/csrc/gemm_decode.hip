@@ -426,7 +426,9 @@ hipError_t launch_decode_t(const GemmPlan &p, const DecodeArgs &a, size_t lds, h
     X(1, 1, 8, 2, true) X(1, 2, 8, 2, true) X(1, 1, 4, 2, false) X(1, 1, 4, 4, false)            \
     X(1, 2, 4, 2, false) X(1, 4, 4, 2, false) X(1, 1, 8, 2, false) X(1, 2, 8, 2, false)          \
     X(2, 1, 4, 2, false) X(2, 2, 4, 2, false) X(2, 4, 4, 2, false) X(2, 1, 8, 2, false)          \
-    X(4, 1, 4, 2, false) X(4, 2, 4, 2, false) X(4, 4, 4, 2, false) X(4, 1, 8, 2, false)
+    X(4, 1, 4, 2, false) X(4, 2, 4, 2, false) X(4, 4, 4, 2, false) X(4, 1, 8, 2, false)          \
+    X(1, 1, 4, 8, true) X(1, 1, 4, 8, false) X(1, 2, 4, 4, false) X(1, 2, 4, 8, false)           \
+    X(1, 4, 4, 4, false) X(2, 2, 4, 4, false) X(2, 4, 4, 4, false) X(4, 4, 4, 4, false)
 
 bool decode_variant_exists(int mt, int nt, int waves, int depth, bool xs)
 {
