@@ -84,6 +84,32 @@ def test_act_quant_edges_and_row_stride():
     quantize_act_per_token_i8(e)
 
 
+@pytest.mark.parametrize("M", [64, 1100])
+def test_act_quant_every_half_value(M):
+    """Each row holds every finite fp16 value up to its absmax (the rest 0),
+    under scales that make exact ties (absmax 127, 63.5, 254: s_a = 1, 0.5, 2)
+    and random ones: every quotient the division can meet for that scale,
+    including those within rounding distance of a half-integer.  M spans the
+    four-waves-per-token and one-wave-per-token layouts."""
+    from w4a8_quantized_linear_amd import quantize_act_per_token_i8
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = bits.view(np.float16)
+    vals = vals[np.isfinite(vals)]
+    K = vals.size                                    # 63488 = 496 groups of 128
+    assert K % 128 == 0
+    rng = np.random.default_rng(20261202 + M)
+    amax = rng.uniform(-24, 15.99, size=M)
+    amax = np.exp2(amax).astype(np.float16)
+    amax[:6] = [127, 63.5, 254, 65504, 2.0 ** -24, 1]
+    x = np.where(np.abs(vals)[None, :] <= amax[:, None], vals[None, :], np.float16(0))
+    x = np.ascontiguousarray(x.astype(np.float16))
+    say("act quant every fp16 value M=%d K=%d" % (M, K))
+    qx, sa = quantize_act_per_token_i8(to_dev(x))
+    qx_ref, sa_ref = orc.quantize_act(x)
+    assert np.array_equal(to_host(sa).view(np.uint32), sa_ref.view(np.uint32))
+    assert np.array_equal(to_host(qx), qx_ref)
+
+
 # ---------------------------------------------------------------------------
 # weight quantizer + packing (read back through the unpack entry point)
 # ---------------------------------------------------------------------------

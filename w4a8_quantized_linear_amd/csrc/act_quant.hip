@@ -5,105 +5,226 @@
 //   s_a[m]  = max_k |x[m,k]| / 127            (IEEE fp32 division)
 //   qx[m,k] = clamp(rint(x[m,k] / s_a[m]), -127, 127)   (0 when s_a == 0)
 //
-// One 256-thread workgroup per token.  The row is read once from HBM with
-// 16-byte loads and held in registers (up to 32768 elements per row; longer
-// rows re-read their tail), reduced to the absmax in-wave with cross-lane
-// moves and across the four waves through LDS, then quantized from the
-// registers and written with 8-byte stores.  Memory bound: 3 bytes per
-// element (+4 per token).
+// Layout: W waves per token (W = 4 while few tokens leave waves idle, else
+// W = 1), four waves per workgroup.  Each lane keeps R 16-byte chunks of its
+// row in registers, so a row of up to 512 R W elements is read from HBM once
+// (longer rows re-read their tail from cache); loads are all issued before
+// the first use.  The absmax is reduced as 15-bit fp16 magnitudes with
+// packed integer max (for finite halves, magnitude bits order like values),
+// across lanes with cross-lane moves and across the W waves through LDS.
+//
+// Division: x / s_a needs one correctly rounded fp32 quotient per element
+// (the scale is a/127 by IEEE division, so 1/s_a is not exact).  Every
+// element takes t = x * fl(1/s_a), which is within 3 units in the last place
+// of the quotient (|t - x/s| <= |x/s| (3u + u^2), u = 2^-24, |x/s| <= 127 +
+// 2^-16), i.e. within 2.3e-5 of it.  rint(t) and rint(fl(x/s)) can only
+// differ when a half-integer lies between them, so a chunk whose t are all
+// farther than 2^-14 from a half-integer is quantized from t; otherwise the
+// whole chunk is recomputed with the IEEE division (a chunk takes that path
+// with probability ~1e-3 on smooth data, every time on exact ties).
+// Memory bound: 3 bytes per element (+4 per token).
 #include "w4a8_internal.h"
 
 namespace w4a8 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRegChunks = 16;   // 16-byte chunks (8 halves) kept per thread
+constexpr int64_t kMaxBlocks = 1 << 22;  // workgroups per launch (slots loop over the rest)
+constexpr float kNearTie = 1.0f / 16384; // 2^-14 > the 2.3e-5 bound above
+
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 __device__ inline float h2f(uint32_t bits16)
 {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
-__device__ inline float chunk_absmax(const uint4 &c, float a)
+// running max of the two 15-bit magnitudes held in each half of a dword
+__device__ inline uint32_t chunk_absmax(const uint4 &c, uint32_t a)
 {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    us2 m = __builtin_bit_cast(us2, a);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        a = fmaxf(a, fabsf(h2f(w[i] & 0xFFFFu)));
-        a = fmaxf(a, fabsf(h2f(w[i] >> 16)));
-    }
-    return a;
+    for (int i = 0; i < 4; i++)
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, w[i] & 0x7FFF7FFFu));
+    return __builtin_bit_cast(uint32_t, m);
 }
 
-__device__ inline int quant1(float x, float s, bool zero)
+// low bytes of four dwords -> one dword
+__device__ inline uint32_t pack4(uint32_t q0, uint32_t q1, uint32_t q2, uint32_t q3)
 {
-    if (zero)
-        return 0;
-    float q = __builtin_rintf(x / s);
-    q = fminf(fmaxf(q, -127.0f), 127.0f);
-    return (int)q;
+    const uint32_t lo = __builtin_amdgcn_perm(q1, q0, 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(q3, q2, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-__device__ inline uint2 chunk_quant(const uint4 &c, float s, bool zero)
+// Round-to-nearest-even to an integer by adding 1.5 * 2^23: for |v| < 2^22
+// the sum's ulp is 1, so the sum is rint(v) + 1.5 * 2^23 exactly and its low
+// byte is rint(v) as a two's-complement int8.
+constexpr float kRoundC = 12582912.0f;
+
+// quantize 8 halves; inv = fl(1/s) (0 for an all-zero row, whose s is 0).
+// No clamp: |x| <= a and s = fl(a/127) >= (a/127)(1 - 2^-24) bound both
+// quotients by 127 + 2^-16, so their rint is within [-127, 127].
+__device__ inline uint2 chunk_quant(const uint4 &c, float s, float inv)
 {
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    uint32_t out[2] = {0, 0};
+    float x[8], r[8];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        uint32_t lo = (uint32_t)(quant1(h2f(w[i] & 0xFFFFu), s, zero)) & 0xFFu;
-        uint32_t hi = (uint32_t)(quant1(h2f(w[i] >> 16), s, zero)) & 0xFFu;
-        out[i / 2] |= (lo | (hi << 8)) << (16 * (i & 1));
+        x[2 * i] = h2f(w[i] & 0xFFFFu);
+        x[2 * i + 1] = h2f(w[i] >> 16);
     }
-    return make_uint2(out[0], out[1]);
+    // the largest distance of t to its nearest integer (t - rint(t) is exact)
+    float dmax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        // x * inv as one mixed-precision fma straight from the half (the +0
+        // addend changes no rounding and keeps the fma from folding to a mul)
+        const float t = __builtin_fmaf(x[i], inv, 0.0f);
+        r[i] = t + kRoundC;
+        dmax = fmaxf(dmax, fabsf(t - (r[i] - kRoundC)));
+    }
+    if (__builtin_expect(dmax >= 0.5f - kNearTie, 0)) {
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            r[i] = x[i] / s + kRoundC;
+    }
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        b[i] = __builtin_bit_cast(uint32_t, r[i]);
+    return make_uint2(pack4(b[0], b[1], b[2], b[3]), pack4(b[4], b[5], b[6], b[7]));
 }
 
+// W waves per token, R register chunks per lane.  Token slots (a wave, or a
+// workgroup when W = 4) walk the tokens with a stride of the slot count;
+// the next token's row is loaded before the current one is quantized, so
+// loads, arithmetic and stores of successive tokens overlap.  Every load is
+// unconditional, so the waits for one row never include the next row's
+// loads: a lane index past the row is clamped to its last chunk (a repeated
+// chunk leaves the absmax unchanged; only its store is skipped), and the
+// prefetch after a slot's last token re-reads that token's row from cache.
+// Exact: the row is exactly R chunks per lane (no clamping, no tail).
+template <int W, int R, bool Exact>
 __global__ __launch_bounds__(kThreads) void act_quant_kernel(const uint16_t *__restrict__ x,
-                                                             int64_t K, int64_t ldx,
+                                                             int64_t M, int64_t K, int64_t ldx,
                                                              int8_t *__restrict__ qx,
                                                              float *__restrict__ s_a)
 {
-    __shared__ float red[kThreads / 64];
-    const int64_t m = blockIdx.x;
-    const int tid = threadIdx.x;
-    const uint4 *row = reinterpret_cast<const uint4 *>(x + m * ldx);
+    constexpr int L = 64 * W;               // lanes per token
+    constexpr int kTok = kThreads / L;      // token slots per workgroup
+    const int lane = threadIdx.x % L;
+    const int64_t slots = (int64_t)gridDim.x * kTok;
+    int64_t m = (int64_t)blockIdx.x * kTok + threadIdx.x / L;
+    if (m >= M)
+        return;                              // whole slots only (W = 1)
     const int64_t nchunks = K / 8;
+    __shared__ uint32_t red[kThreads / 64];
 
-    uint4 buf[kRegChunks];
-    float a = 0.0f;
+    auto chunk = [&](int i) -> int64_t {
+        const int64_t c = lane + (int64_t)L * i;
+        return Exact ? c : std::min<int64_t>(c, nchunks - 1);
+    };
+    auto load = [&](uint4(&b)[R], int64_t t) {
+        const uint4 *row = reinterpret_cast<const uint4 *>(x + t * ldx);
 #pragma unroll
-    for (int i = 0; i < kRegChunks; i++) {
-        int64_t c = tid + (int64_t)i * kThreads;
-        if (c < nchunks) {
-            buf[i] = row[c];
-            a = chunk_absmax(buf[i], a);
+        for (int i = 0; i < R; i++)
+            b[i] = row[chunk(i)];
+        __builtin_amdgcn_sched_barrier(0);   // issue the row's loads before what follows
+    };
+    auto quantize = [&](const uint4(&b)[R], int64_t t) {
+        const uint4 *row = reinterpret_cast<const uint4 *>(x + t * ldx);
+        uint32_t am = 0;
+#pragma unroll
+        for (int i = 0; i < R; i++)
+            am = chunk_absmax(b[i], am);
+        if (!Exact)
+            for (int64_t c = lane + (int64_t)L * R; c < nchunks; c += L)
+                am = chunk_absmax(row[c], am);
+        am = max(am & 0xFFFFu, am >> 16);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            am = max(am, (uint32_t)__shfl_xor((int)am, off, 64));
+        if (W > 1) {
+            if ((threadIdx.x & 63) == 0)
+                red[threadIdx.x >> 6] = am;
+            __syncthreads();
+#pragma unroll
+            for (int v = 0; v < W; v++)
+                am = max(am, red[(threadIdx.x / L) * W + v]);
+            __syncthreads();                 // red is rewritten for the next token
         }
-    }
-    for (int64_t c = tid + (int64_t)kRegChunks * kThreads; c < nchunks; c += kThreads)
-        a = chunk_absmax(row[c], a);
-
-    // in-wave reduction, then across the waves
+        const float a = h2f(am);
+        const float s = a / 127.0f;
+        const float inv = a == 0.0f ? 0.0f : 1.0f / s;
+        if (lane == 0)
+            s_a[t] = s;
+        uint2 *out = reinterpret_cast<uint2 *>(qx + t * K);
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        a = fmaxf(a, __shfl_xor(a, off, 64));
-    if ((tid & 63) == 0)
-        red[tid >> 6] = a;
-    __syncthreads();
-    a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        for (int i = 0; i < R; i++) {
+            const int64_t c = lane + (int64_t)L * i;
+            const uint2 v = chunk_quant(b[i], s, inv);
+            if (Exact || c < nchunks)
+                out[c] = v;
+        }
+        if (!Exact)
+            for (int64_t c = lane + (int64_t)L * R; c < nchunks; c += L)
+                out[c] = chunk_quant(row[c], s, inv);
+    };
 
-    const float s = a / 127.0f;
-    const bool zero = (a == 0.0f);
-    if (tid == 0)
-        s_a[m] = s;
-
-    uint2 *out = reinterpret_cast<uint2 *>(qx + m * K);
-#pragma unroll
-    for (int i = 0; i < kRegChunks; i++) {
-        int64_t c = tid + (int64_t)i * kThreads;
-        if (c < nchunks)
-            out[c] = chunk_quant(buf[i], s, zero);
+    uint4 A[R], B[R];
+    load(A, m);
+    while (true) {
+        const int64_t m1 = m + slots;
+        load(B, m1 < M ? m1 : m);
+        quantize(A, m);
+        if (m1 >= M)
+            break;
+        const int64_t m2 = m1 + slots;
+        load(A, m2 < M ? m2 : m1);
+        quantize(B, m1);
+        if (m2 >= M)
+            break;
+        m = m2;
     }
-    for (int64_t c = tid + (int64_t)kRegChunks * kThreads; c < nchunks; c += kThreads)
-        out[c] = chunk_quant(row[c], s, zero);
+}
+
+template <int W, int R>
+hipError_t launch_wr(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int8_t *qx,
+                     float *s_a, int64_t slots, hipStream_t st)
+{
+    const int64_t tok = kThreads / (64 * W);
+    const int64_t blocks = std::min<int64_t>((slots + tok - 1) / tok, kMaxBlocks);
+    const bool exact = K / 8 == (int64_t)64 * W * R;
+    hipLaunchKernelGGL((exact ? act_quant_kernel<W, R, true> : act_quant_kernel<W, R, false>),
+                       dim3((unsigned)blocks), dim3(kThreads), 0, st, x, M, K, ldx, qx, s_a);
+    return hipGetLastError();
+}
+
+// register chunks per lane for a row of K halves over W waves (24 at most;
+// longer rows read the rest in a second pass from cache)
+int regs_for(int64_t K, int W)
+{
+    const int64_t per_lane = (K / 8 + 64 * W - 1) / (64 * W);
+    for (int r : {2, 4, 8, 12, 16})
+        if (per_lane <= r)
+            return r;
+    return 24;
+}
+
+template <int W>
+hipError_t launch_w(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int8_t *qx, float *s_a,
+                    int64_t slots, hipStream_t st)
+{
+    switch (regs_for(K, W)) {
+    case 2: return launch_wr<W, 2>(x, M, K, ldx, qx, s_a, slots, st);
+    case 4: return launch_wr<W, 4>(x, M, K, ldx, qx, s_a, slots, st);
+    case 8: return launch_wr<W, 8>(x, M, K, ldx, qx, s_a, slots, st);
+    case 12: return launch_wr<W, 12>(x, M, K, ldx, qx, s_a, slots, st);
+    case 16: return launch_wr<W, 16>(x, M, K, ldx, qx, s_a, slots, st);
+    default: return launch_wr<W, 24>(x, M, K, ldx, qx, s_a, slots, st);
+    }
 }
 
 }  // namespace
@@ -113,9 +234,27 @@ hipError_t launch_act_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx
 {
     if (M == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(act_quant_kernel, dim3((unsigned)M), dim3(kThreads), 0, st, x, K, ldx, qx,
-                       s_a);
-    return hipGetLastError();
+    // Few tokens, or rows too long for one wave's registers: four waves per
+    // token.  Otherwise one wave per token.  From four tokens per slot on,
+    // each slot walks its tokens with the row prefetch (two slots per SIMD,
+    // one if the two row buffers take more than half its registers); below
+    // that every token gets a slot of its own (timed faster on MI355X at
+    // 4096 tokens of 4096).  W4A8_ACT_SLOTS=n overrides the slot count.
+    int64_t slots = 0;
+    if (const char *env = std::getenv("W4A8_ACT_SLOTS"))
+        slots = std::atoll(env);
+    const int64_t cus = num_cus();
+    const bool wide = (K / 8 + 63) / 64 > 24;
+    if (M < 1024 || wide) {
+        if (slots <= 0)
+            slots = M >= 4 * cus ? 2 * cus : M;
+        return launch_w<4>(x, M, K, ldx, qx, s_a, std::min(slots, M), st);
+    }
+    if (slots <= 0) {
+        const int64_t per_simd = regs_for(K, 1) <= 16 ? 2 : 1;
+        slots = M >= 4 * per_simd * 4 * cus ? per_simd * 4 * cus : M;
+    }
+    return launch_w<1>(x, M, K, ldx, qx, s_a, std::min(slots, M), st);
 }
 
 }  // namespace w4a8

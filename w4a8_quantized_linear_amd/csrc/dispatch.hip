@@ -26,17 +26,6 @@ hipError_t launch_gemm_decode(const GemmPlan &p, const int8_t *qx, const float *
                               int64_t N, int64_t K, uint16_t *y, int32_t *acc_out, void *ws,
                               hipStream_t st);
 
-namespace {
-
-// decode split-K: the counters, then one 16 mt x 16 nt INT32 slot per (tile, split)
-size_t ws_size(const GemmPlan &p)
-{
-    const int64_t tiles = p.m_blocks * p.n_blocks;
-    if (p.splitk <= 1 || tiles > kWsCounters)
-        return 0;
-    return (size_t)kWsPartOffset + (size_t)tiles * p.splitk * 256 * p.mt * p.nt * 4;
-}
-
 // compute units of the current device (cached per device)
 int64_t num_cus()
 {
@@ -51,6 +40,17 @@ int64_t num_cus()
         cached[dev] = n;
     }
     return cached[dev];
+}
+
+namespace {
+
+// decode split-K: the counters, then one 16 mt x 16 nt INT32 slot per (tile, split)
+size_t ws_size(const GemmPlan &p)
+{
+    const int64_t tiles = p.m_blocks * p.n_blocks;
+    if (p.splitk <= 1 || tiles > kWsCounters)
+        return 0;
+    return (size_t)kWsPartOffset + (size_t)tiles * p.splitk * 256 * p.mt * p.nt * 4;
 }
 
 bool launchable(const GemmPlan &p, int64_t M, int64_t K)

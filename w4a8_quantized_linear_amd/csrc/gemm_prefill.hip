@@ -137,10 +137,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
     float *sa_lds = reinterpret_cast<float *>(smem + kAStages * kAStage);
     __shared__ uint32_t arrival;
 
-    const int tid = threadIdx.x;
-    const int l = tid & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lr = l & 15, lk = l >> 4;      // operand row / 16-byte k-block of this lane
+    const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
 
     // Workgroup b runs on XCD b % 8; it takes range w of the P balanced
     // ranges of (tile, group) units, so each XCD works through contiguous
@@ -181,6 +178,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
         const int m0 = mb * BM;
         const int nt0 = nb * (BN / 16) + wv * TN;   // first device tile of this wave
         const int glast = ge - 1;                    // loads past the segment re-read its last group
+
+        // Lane indices, made opaque per segment so that the compiler derives
+        // the per-lane offsets inside the loop instead of keeping dozens of
+        // them live (and spilled) across all segments.
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int l = tid & 63;
+        const int lr = l & 15, lk = l >> 4;      // operand row / 16-byte k-block of this lane
 
         // activation tile loads: load j covers block row 32 j + tid / 8, chunk tid % 8
         const int xrow0 = tid >> 3, xch = tid & 7;

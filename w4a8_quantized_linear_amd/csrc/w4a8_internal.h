@@ -81,6 +81,9 @@ struct GemmPlan {
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
 
+// compute units of the current device (256 when it cannot be queried)
+int64_t num_cus();
+
 // The same computation without a workspace (no split-K, no stream-K).
 GemmPlan plan_without_workspace(GemmPlan p);
 
