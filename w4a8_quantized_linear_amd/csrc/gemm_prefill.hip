@@ -21,12 +21,15 @@
 //     xor: the QServe talk summary's register-level rebuild with subtraction
 //     after multiplication).  Every weight byte is read once per workgroup.
 //   * Activations go through LDS: the 256 x 128 INT8 tile of group g + 3 is
-//     loaded into registers during group g and stored during group g + 1
-//     into a three-stage LDS ring, so the stage group g + 1 reads is complete
-//     a whole group before it is needed and its first operand reads can be
-//     issued before the barrier that ends group g.  Rows are 128 bytes whose
-//     eight 16-byte chunks are XOR-swizzled with (row / 2) so the rows one
-//     operand load touches spread over the banks.
+//     loaded during group g by buffer loads whose destination is the LDS
+//     (no registers, no LDS store instructions) into a four-stage ring, and
+//     waited for by counted vmcnt at the end of group g + 1, so the stage
+//     group g + 2 reads is complete a whole group before it is needed and its
+//     first operand reads can be issued before the barrier that ends group
+//     g + 1.  Rows are 128 bytes whose eight 16-byte chunks are XOR-swizzled
+//     with (row / 2) so the rows one operand load touches spread over the
+//     banks; each lane of a load fetches the chunk the swizzle puts at its
+//     fixed LDS position.
 //   * A group is two phases, one per 64-k half, of 16 row steps each.  A row
 //     step issues the LDS read of the activation operand three steps ahead,
 //     four MFMAs, and the VALU rebuild of one dword of the next phase's B
@@ -63,7 +66,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int TN = 4;                     // 16-channel tiles per wave
 constexpr int BN = kWaves * TN * 16;      // channels per workgroup
-constexpr int kAStages = 3;               // activation stages in LDS (ring)
+constexpr int kAStages = 4;               // activation stages in LDS (ring)
 constexpr int kAhead = 3;                 // activation operand reads in flight
 constexpr int kBandM = 4;                 // m-blocks per band of the tile order
 
@@ -73,13 +76,14 @@ template <int TM>
 struct Cfg {
     static constexpr int BM = 16 * TM;
     static constexpr int kAStage = BM * 128;                     // bytes of one activation stage
-    static constexpr int kXChunks = kAStage / 16 / kThreads;     // 16-byte activation loads per thread per group
-    static constexpr int kAPre = TM >= 16 ? 1 : 8 / kXChunks;   // groups of activations held in registers
+    static constexpr int kXChunks = kAStage / 1024 / kWaves;     // 1 KB LDS loads per wave per group
     static constexpr int kBDepth = TM >= 8 ? 4 : 6;             // weight groups in flight (ring slots)
     static constexpr int kUnroll = TM >= 8 ? 4 : 12;            // groups per main-loop iteration
-    static_assert(kUnroll % kBDepth == 0 && kUnroll % kAPre == 0 && kUnroll % 4 == 0,
+    static_assert(kUnroll % kBDepth == 0 && kUnroll % 4 == 0,
                   "ring, register and parameter-byte indices are static in the unrolled loop");
+    static_assert(kXChunks % 2 == 0, "a wave's first LDS load starts an even 8-row block");
     static_assert(TM % (kAhead + 1) == 0 && TM > kAhead, "the operand-read ring lines up with the phases");
+    static_assert(BM <= kThreads, "one token scale per thread");
     static_assert((BM / 2) * (BN * 2 + 16) <= kAStages * kAStage, "output half-tile fits in the stages");
 };
 
@@ -131,10 +135,11 @@ template <int TM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a)
 {
     using C = Cfg<TM>;
-    constexpr int BM = C::BM, kAStage = C::kAStage, kXChunks = C::kXChunks, kAPre = C::kAPre,
+    constexpr int BM = C::BM, kAStage = C::kAStage, kXChunks = C::kXChunks,
                   kBDepth = C::kBDepth, kUnroll = C::kUnroll;
     extern __shared__ __align__(16) uint8_t smem[];
-    float *sa_lds = reinterpret_cast<float *>(smem + kAStages * kAStage);
+    float *sa_lds = reinterpret_cast<float *>(smem + kAStages * kAStage);   // [BM] token scales
+    constexpr int kDummy = kAStages * kAStage + BM * 4;                      // 1 KB never read
     __shared__ uint32_t arrival;
 
     const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -187,24 +192,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
         const int l = tid & 63;
         const int lr = l & 15, lk = l >> 4;      // operand row / 16-byte k-block of this lane
 
-        // activation tile loads: load j covers block row 32 j + tid / 8, chunk tid % 8
-        const int xrow0 = tid >> 3, xch = tid & 7;
-        const int xoff = (m0 + xrow0) * K + xch * 16;
+        // Activation tiles go from HBM straight into LDS (buffer loads with
+        // the LDS as destination: no registers, no LDS store instructions).
+        // Load j of wave wv fills rows 8 J .. 8 J + 7 of a stage (J = kXChunks
+        // wv + j), lane l writing position l % 8 of row 8 J + l / 8, so it
+        // fetches the chunk the swizzle puts there: (l % 8) ^ ((row / 2) % 8),
+        // which depends on J only through its parity.
+        const int xq = l >> 3, xp = l & 7;
+        const int xoff[2] = {(m0 + xq) * K + 16 * (xp ^ (xq >> 1)),
+                             (m0 + xq) * K + 16 * (xp ^ (4 + (xq >> 1)))};
         // weight loads: tile nt0 + t, lane l; parameter dword of channel lr
         const int woff = nt0 * G * kTileBytes + 16 * l;
         const int poff = (nt0 * (G4 / 4) * 16 + lr) * 4;
 
         __syncthreads();   // the previous segment is done with the LDS
-        for (int i = tid; i < BM; i += kThreads)
-            sa_lds[i] = a.s_a[min<int64_t>(m0 + i, a.M - 1)];
+        // this thread's token scale (stored to LDS after the loads below)
+        const float sa_t = a.s_a[min<int64_t>(m0 + min(tid, BM - 1), a.M - 1)];
 
-        v4i xr[kAPre][kXChunks];   // activations of the next kAPre groups to store
-        auto xload = [&](v4i &dst, int g, int j) {
-            g = min(g, glast);
-            dst = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff, j * (kThreads / 8) * K + g * kGroup, 0);
-        };
-        auto xstore = [&](uint8_t *stg, const v4i &src, int j) {
-            *reinterpret_cast<v4i *>(stg + swz(j * (kThreads / 8) + xrow0, xch)) = src;
+        // Loads of groups past the segment are still issued (so that every
+        // group issues the same number of loads and no branch splits the
+        // main loop), from the last group into a 1 KB scratch area that
+        // nothing reads.
+        auto xdma = [&](int stage, bool live, int g, int j) {
+            const int J = wv * kXChunks + j;
+            const int dst = live ? stage + 1024 * J : kDummy;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rx, (__attribute__((address_space(3))) void *)(smem + dst), 16, xoff[j & 1],
+                8 * J * K + min(g, glast) * kGroup, 0, 0);
         };
         auto bload_t = [&](BSlot &sl, int g, int t) {
             g = min(g, glast);
@@ -222,10 +236,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
         // lane's activation operand of row tile i, k-half h: row 16 i + lr, chunk
         // 4 h + lk; the swizzle depends only on lr, so tile i is at + 2048 i
         const int aoff[2] = {swz(lr, lk), swz(lr, 4 + lk)};
-        // byte offsets of the LDS stages read in this group, read next and
-        // written now; they rotate by one stage per group (uniform, in SGPRs)
-        int so_r = 0, so_n = kAStage, so_w = 2 * kAStage;
-        static_assert(kAStages == 3, "three rotating stage offsets");
+        // byte offsets of the LDS stages of groups g .. g + 3 (read now, read
+        // next, in flight, being loaded); they rotate by one stage per group
+        // (uniform, in SGPRs)
+        int so_r = 0, so_n = kAStage, so_2 = 2 * kAStage, so_w = 3 * kAStage;
+        static_assert(kAStages == 4, "four rotating stage offsets");
 
         // Per-lane (s1, C) of the four tiles, for groups of either parity:
         // s1 = (p & 15) + 1 and C = 257 (128 - z s1) mod 2^16 from the
@@ -245,10 +260,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
         //   * rebuild of fn, the next phase's operands (k-half 1 of group g,
         //     then k-half 0 of group g + 1), one dword in three steps: mask,
         //     packed multiply-add, xor 0x80, i.e. (q4 s1 + 128 - z s1) ^ 0x80;
-        //   * phase 0: group g + 1's (s1, C) pairs, from ring slot sn;
-        //   * phase 1: LDS stores of group g + 2's activations, loads of group
-        //     g + 2 + kAPre's activations into the registers just stored,
-        //     then loads of group g + kBDepth's weights into slot s (loads
+        //   * phase 0: the LDS loads of group g + 3's activations, then group
+        //     g + 1's (s1, C) pairs, from ring slot sn;
+        //   * phase 1: loads of group g + kBDepth's weights into slot s (loads
         //     leave in the order they are waited for; vmcnt is in-order).
         // The activation operand of row i + kAhead is read at the start of
         // row step i, across phase and group boundaries.  u is the group's
@@ -257,16 +271,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
                          const BSlot &sn, int g) {
             constexpr int kSlots = TM * TN;
             constexpr int kRebuild = 3 * 4 * TN;
-            constexpr int kSc = 2 * TN;
-            constexpr int kMem = 2 * kXChunks + TN;
+            constexpr int kSc = kXChunks + 2 * TN;
+            constexpr int kMem = TN;
             const uint8_t *As = smem + so_r + aoff[h];
             const uint8_t *An = h ? smem + so_n + aoff[0] : smem + so_r + aoff[1];
-            uint8_t *Ad = smem + so_w;
+            const bool dma = g + 3 < ge;   // group g + 3 is inside the segment
             // operands being rebuilt: half hn, from slot sb, pairs of parity pr
             const int hn = 1 - h;
             const BSlot &sb = h ? sn : s;
             const int pr = h ? (u + 1) & 1 : u & 1;
             // fc was last written by VALU before the previous phase boundary
+            // (or in the prologue: nothing before this point may sink past it)
+            __builtin_amdgcn_sched_barrier(0);
             asm volatile("s_nop 4");
 #pragma unroll
             for (int k = 0; k < kSlots; k++) {
@@ -302,8 +318,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
                         const int o = k * kSc / kSlots + q;
                         if (o >= (k + 1) * kSc / kSlots)
                             break;
-                        const int tt = o >> 1;
-                        if ((o & 1) == 0) {
+                        if (o < kXChunks) {
+                            xdma(so_w, dma, g + 3, o);
+                            continue;
+                        }
+                        const int tt = (o - kXChunks) >> 1;
+                        if (((o - kXChunks) & 1) == 0) {
                             sc_p = (sn.p[tt] >> (8 * ((g + 1) & 3))) & 0xFFu;
                             sc_s1 = (sc_p & 15u) + 1u;
                         } else {
@@ -317,13 +337,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
                         const int o = k * kMem / kSlots + q;
                         if (o >= (k + 1) * kMem / kSlots)
                             break;
-                        if (o < kXChunks) {
-                            xstore(Ad, xr[(u + 2) % kAPre][o], o);
-                        } else if (o < 2 * kXChunks) {
-                            xload(xr[(u + 2) % kAPre][o - kXChunks], g + 2 + kAPre, o - kXChunks);
-                        } else {
-                            bload_t(s, g + kBDepth, o - 2 * kXChunks);
-                        }
+                        bload_t(s, g + kBDepth, o);
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -332,45 +346,48 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
 
         // One group g (position u in the unrolled loop) on ring slot s
         // (holding group g) and slot sn (group g + 1), then the barrier.
-        // Before it, this wave's LDS stores must be complete (the oldest LDS
-        // operations: everything but the kAhead operand reads of the next
-        // group, which read a stage completed a group earlier).  The stores
-        // of group g land in stage (g + 2) % 3, first read at the end of
-        // group g + 1; the stage read in group g is rewritten in group g + 1.
+        // Before it, this wave's LDS loads of group g + 2 (issued in group
+        // g - 1, first read at the end of group g + 1) must be complete:
+        // vmcnt retires in order, and after them this wave issued group g -
+        // 1's weight loads (2 TN), group g + 3's LDS loads (kXChunks) and
+        // group g's weight loads (2 TN), so waiting until at most that many
+        // remain suffices (more in flight, e.g. right after the
+        // prologue, only makes the wait stricter).  Its LDS reads must be
+        // complete too, except the kAhead operand reads of the next group,
+        // which read a stage completed a group earlier.  The stage read in
+        // group g is reloaded in group g + 1, after this barrier.
         auto group = [&](const int u, BSlot &s, BSlot &sn, int g) {
             phase(0, u, f0, f1, s, sn, g);
             phase(1, u, f1, f0, s, sn, g);   // past the segment's end the rebuild is unused
-            asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(kAhead) : "memory");
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(%1)\n\ts_barrier" ::"n"(kXChunks + 4 * TN), "n"(kAhead)
+                         : "memory");
             const int so = so_r;
             so_r = so_n;
-            so_n = so_w;
+            so_n = so_2;
+            so_2 = so_w;
             so_w = so;
         };
 
-        // prologue: groups gs and gs + 1's activations into LDS, the next
-        // kAPre groups in registers, the first kBDepth groups of weights in
-        // flight, group gs's (s1, C), first operands and first operand reads
+        // prologue: groups gs .. gs + 2's activations into LDS, the first
+        // kBDepth groups of weights in flight, group gs's (s1, C), first
+        // operands and first operand reads
         BSlot ring[kBDepth];
 #pragma unroll
-        for (int q = 0; q < 2; q++) {
+        for (int q = 0; q < 3; q++)
 #pragma unroll
             for (int j = 0; j < kXChunks; j++)
-                xload(xr[0][j], gs + q, j);
-#pragma unroll
-            for (int j = 0; j < kXChunks; j++)
-                xstore(smem + q * kAStage, xr[0][j], j);
-        }
-#pragma unroll
-        for (int q = 2; q < 2 + kAPre; q++)
-#pragma unroll
-            for (int j = 0; j < kXChunks; j++)
-                xload(xr[q % kAPre][j], gs + q, j);
+                xdma(q * kAStage, gs + q < ge, gs + q, j);
 #pragma unroll
         for (int u = 0; u < kBDepth; u++)
 #pragma unroll
             for (int t = 0; t < TN; t++)
                 bload_t(ring[u], gs + u, t);
-        __syncthreads();
+        if (tid < BM)
+            sa_lds[tid] = sa_t;
+        // groups gs and gs + 1 in LDS (group gs + 2's LDS loads and the 2 TN
+        // kBDepth weight loads may still be in flight); the token scales
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kXChunks + 2 * TN * kBDepth)
+                     : "memory");
 #pragma unroll
         for (int t = 0; t < TN; t++) {
             const uint32_t p = (ring[0].p[t] >> (8 * (gs & 3))) & 0xFFu;
@@ -516,7 +533,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
 template <int TM>
 size_t lds_bytes()
 {
-    return (size_t)kAStages * Cfg<TM>::kAStage + Cfg<TM>::BM * 4;
+    return (size_t)kAStages * Cfg<TM>::kAStage + Cfg<TM>::BM * 4 + 1024;
 }
 
 // The kernel addresses activations with 32-bit buffer offsets, so M is cut
