@@ -60,6 +60,9 @@ def _load():
         lib.orc_rne_div.restype = I64
         lib.orc_quantize_act.argtypes = [P, I64, I64, I64, P, P]
         lib.orc_quantize_act.restype = None
+        lib.orc_norm_quantize_act.argtypes = [P, I64, I64, I64, P, P, ctypes.c_float, ctypes.c_int,
+                                              P, P, P, P, P]
+        lib.orc_norm_quantize_act.restype = None
         lib.orc_weights_level1.argtypes = [P, I64, I64, P, P]
         lib.orc_weights_level1.restype = None
         lib.orc_weights_level2.argtypes = [P, I64, I64, P, P, P]
@@ -128,6 +131,44 @@ def quantize_act(x_f16: np.ndarray):
     sa = np.empty((M,), np.float32)
     _load().orc_quantize_act(_p(x), M, K, K, _p(qx), _p(sa))
     return qx, sa
+
+
+def norm_quantize_act(x_f16: np.ndarray, gamma_f16: np.ndarray, beta_f16=None,
+                      eps: float = 1e-5, rms: bool = False):
+    """LayerNorm (or RMSNorm) fused with the per-token INT8 quantizer.
+
+    x: fp16 [M, K]; gamma, beta: fp16 [K] (beta may be None).  Returns a dict
+    with qx int8 [M,K], s_a fp32 [M], h (the normalized fp16 row, as uint16
+    bits [M,K]), mean and r (double [M]: the statistics before rounding to fp32).
+    """
+    x = _as(x_f16, np.float16)
+    M, K = x.shape
+    g = _as(gamma_f16, np.float16)
+    b = None if beta_f16 is None else _as(beta_f16, np.float16)
+    assert g.shape == (K,) and (b is None or b.shape == (K,))
+    out = {"qx": np.empty((M, K), np.int8), "s_a": np.empty((M,), np.float32),
+           "h": np.empty((M, K), np.uint16), "mean": np.empty((M,), np.float64),
+           "r": np.empty((M,), np.float64)}
+    _load().orc_norm_quantize_act(_p(x), M, K, K, _p(g), None if b is None else _p(b),
+                                  float(np.float32(eps)), int(bool(rms)), _p(out["qx"]),
+                                  _p(out["s_a"]), _p(out["h"]), _p(out["mean"]), _p(out["r"]))
+    return out
+
+
+def rstd_near_midpoint(r: np.ndarray, rel: float = 2.0 ** -36) -> np.ndarray:
+    """Tokens whose double r lies within rel * r of a midpoint between two
+    adjacent floats: another order of the sum of squares may round r to the
+    other float there (see the C oracle's note).  False where r is infinite."""
+    r = np.asarray(r, np.float64)
+    out = np.zeros(r.shape, bool)
+    fin = np.isfinite(r) & (r > 0)
+    f = r[fin].astype(np.float32)
+    lo = np.nextafter(f, np.float32(0)).astype(np.float64)
+    hi = np.nextafter(f, np.float32(np.inf)).astype(np.float64)
+    fd = f.astype(np.float64)
+    d = np.minimum(np.abs(r[fin] - (fd + lo) / 2), np.abs(r[fin] - (fd + hi) / 2))
+    out[fin] = d <= rel * r[fin]
+    return out
 
 
 def weights_level1(w: np.ndarray):
@@ -233,7 +274,8 @@ def linear_into(x_f16: np.ndarray, wq: dict, bufs: dict) -> int:
 
 __all__ = [
     "GROUP", "PROTECT", "build", "f32_to_f16_bits", "f16_bits_to_f32", "f32_to_f16_bits_array",
-    "rne_div", "num_threads", "quantize_act", "weights_level1", "weights_level2", "pack_q4",
+    "rne_div", "num_threads", "quantize_act", "norm_quantize_act", "rstd_near_midpoint",
+    "weights_level1", "weights_level2", "pack_q4",
     "dequant_i8", "gemm_acc", "epilogue", "quantize_weights", "linear",
     "linear_timed_buffers", "linear_into",
 ]

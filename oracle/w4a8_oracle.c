@@ -161,6 +161,77 @@ void orc_quantize_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Normalization fused with the activation quantizer.  The QServe talk      */
+/* summary ("Precision Data Flow and Activation Quantization Fusion") has   */
+/* the layer before a linear layer -- its example is LayerNorm -- emit the  */
+/* 8-bit activations directly.  Per token m, over its K features:           */
+/*   LayerNorm (rms == 0): h = (x - mean) / sqrt(var + eps) * gamma + beta  */
+/*   RMSNorm   (rms != 0): h = x / sqrt(mean(x^2) + eps) * gamma (+ beta)   */
+/* and the fp16 row h is quantized by orc_quantize_act's rule.  The pages   */
+/* give no precision for the statistics; the readings:                      */
+/*   - mean is exact up to one rounding: an fp16 value is an integer       */
+/*     multiple of 2^-24, so the row sum is an exact integer S and          */
+/*     mean = (double(S) * 2^-24) / K (IEEE double; 0 for RMSNorm);         */
+/*   - var = (sum over k, in order, of (double(x) - mean)^2) / K in double, */
+/*     each product and sum rounded (x^2 for RMSNorm);                      */
+/*   - r = 1 / sqrt(var + eps) in double (IEEE sqrt and division); the fp32 */
+/*     factors are mean32 = float(mean) and rstd = float(r), with rstd = 0  */
+/*     when var + eps is 0;                                                  */
+/*   - h = fp16( ((float(x) - mean32) * rstd) * float(gamma) + float(beta)) */
+/*     in fp32 in that order (no beta: no addition).                         */
+/* The sum of squares is the one step whose rounding depends on the order   */
+/* of the additions; an implementation that adds in another order gets a    */
+/* double r within about K * 2^-53 of this one, and the same rstd unless r  */
+/* lies that close to a midpoint between two floats.                        */
+/* mean_out and r_out (double [M]) may be NULL; h (fp16 bits [M, K]) may be  */
+/* NULL.  K <= 2^20 keeps S inside int64.                                    */
+/* ------------------------------------------------------------------------ */
+void orc_norm_quantize_act(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                           const uint16_t *gamma, const uint16_t *beta, float eps, int rms,
+                           int8_t *qx, float *s_a, uint16_t *h, double *mean_out,
+                           double *r_out)
+{
+    uint16_t *row = (uint16_t *)malloc((size_t)K * sizeof(uint16_t));
+    for (int64_t m = 0; m < M; m++) {
+        const uint16_t *xm = x + m * ldx;
+        double mean = 0.0;
+        if (!rms) {
+            int64_t S = 0;
+            for (int64_t k = 0; k < K; k++)
+                S += (int64_t)ldexp((double)orc_f16_to_f32(xm[k]), 24);   /* exact integer */
+            mean = ldexp((double)S, -24) / (double)K;
+        }
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            double d = (double)orc_f16_to_f32(xm[k]) - mean;
+            double sq = d * d;
+            ss = ss + sq;
+        }
+        double var = ss / (double)K;
+        double ve = var + (double)eps;
+        double r = ve == 0.0 ? INFINITY : 1.0 / sqrt(ve);
+        float rstd = ve == 0.0 ? 0.0f : (float)r;
+        float mean32 = (float)mean;
+        if (mean_out)
+            mean_out[m] = mean;
+        if (r_out)
+            r_out[m] = r;
+        for (int64_t k = 0; k < K; k++) {
+            float t = orc_f16_to_f32(xm[k]) - mean32;
+            t = t * rstd;
+            t = t * orc_f16_to_f32(gamma[k]);
+            if (beta)
+                t = t + orc_f16_to_f32(beta[k]);
+            row[k] = orc_f32_to_f16(t);
+        }
+        if (h)
+            memcpy(h + m * K, row, (size_t)K * sizeof(uint16_t));
+        orc_quantize_act(row, 1, K, K, qx + m * K, s_a + m);
+    }
+    free(row);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Weights, level 1: per output channel, symmetric INT8 inside the          */
 /* protective range [-119, 119], with an fp16 scale (QServe talk summary,   */
 /* "Progressive Group Quantization for W4A8 GEMM"; Lecture 15 notes, 15.6,  */

@@ -2,7 +2,7 @@
 
 Each case plants one mistake in a copy of the oracle's C source (a wrong tie
 rule, a dropped factor, a transposed index, a wrong constant, ...), builds it
-on the CPU, and runs the pin suite against that build.  Every mutant must make
+on the CPU, and runs the pin suites against that build.  Every mutant must make
 at least one pin fail.  Nothing here touches a GPU.
 """
 import os
@@ -31,7 +31,19 @@ MUTANTS = [
      "int64_t s = s1[n * G + (k + 1) / ORC_GROUP % G];"),
     ("fp16 rounding truncates", "double n = rint(ldexp(a, 10 - e));", "double n = floor(ldexp(a, 10 - e));"),
     ("level-1 codes unclamped sign flip", "q8[n * K + k] = (int8_t)q;", "q8[n * K + k] = (int8_t)(-q);"),
+    ("norm variance divisor K - 1", "double var = ss / (double)K;", "double var = ss / (double)(K - 1);"),
+    ("norm eps dropped", "double ve = var + (double)eps;", "double ve = var;"),
+    ("layernorm mean not subtracted", "float t = orc_f16_to_f32(xm[k]) - mean32;",
+     "float t = orc_f16_to_f32(xm[k]);"),
+    ("norm beta dropped", "t = t + orc_f16_to_f32(beta[k]);", "t = t + 0.0f;"),
+    ("norm gamma index shifted", "t = t * orc_f16_to_f32(gamma[k]);",
+     "t = t * orc_f16_to_f32(gamma[(k + 1) % K]);"),
+    ("norm mean in single precision", "mean = ldexp((double)S, -24) / (double)K;",
+     "mean = (double)(float)(ldexp((double)S, -24) / (double)K);"),
+    ("norm rsqrt in single precision", "double r = ve == 0.0 ? INFINITY : 1.0 / sqrt(ve);",
+     "double r = ve == 0.0 ? INFINITY : 1.0 / (double)sqrtf((float)ve);"),
 ]
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_norm_pins.py"]
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
@@ -44,7 +56,7 @@ def test_pins_reject_mutant(tmp_path, name, old, new):
     subprocess.run(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
                     "-o", str(lib), str(mutant), "-lm"], check=True)
     env = dict(os.environ, W4A8_ORACLE_LIB=str(lib))
-    res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                          os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+    res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider"]
+                         + [os.path.join(ROOT, "tests", f) for f in PIN_FILES],
                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert res.returncode != 0, "mutant '%s' passed every pin:\n%s" % (name, res.stdout[-2000:])
