@@ -11,7 +11,10 @@ so weight bytes really come from HBM.
 
 Prints one JSON line: whole-step throughput (TOPS), the roofline of the
 dominant kernel (the M=4096 GEMM), per-M kernel figures, and the CPU oracle
-timed on a bounded sample of the same workload.
+timed on a bounded sample of the same workload.  A separate "norm_quant"
+object measures the fused LayerNorm + INT8 producer (norm_quantize_act_i8) on
+the same activations, against the HBM roofline, with its oracle beside it;
+it is not part of the step or of `value`.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5]
 """
@@ -58,8 +61,8 @@ def main():
     import torch
 
     from w4a8_quantized_linear_amd import _lib, accounting as A, workloads
-    from w4a8_quantized_linear_amd import (gemm_w4a8, quantize_act_per_token_i8,
-                                           quantize_weights_w4g128)
+    from w4a8_quantized_linear_amd import (gemm_w4a8, norm_quantize_act_i8,
+                                           quantize_act_per_token_i8, quantize_weights_w4g128)
     if not os.path.exists(_lib.LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
@@ -165,6 +168,33 @@ def main():
                 "kernel": "gemm_w4a8 M=%d N=%d K=%d" % (dom_M, N_DIM, K_DIM),
                 "avg_us": round(dom_us, 3), "ops_per_launch": dom_ops}
 
+    # ---- fused normalization + quantizer (not part of the step) -----------
+    gam = torch.from_numpy(workloads.norm_affine(K_DIM)[0]).to(dev)
+    bet = torch.from_numpy(workloads.norm_affine(K_DIM)[1]).to(dev)
+    nq = []
+    for M in MS:
+        reps = args.reps
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for r in range(reps):
+            norm_quantize_act_i8(xs[M], gam, bet, eps=1e-5, qx=qxs[M], s_a=sas[M], stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / reps
+        nbytes = A.norm_quant_bytes(M, K_DIM)
+        nq.append({"M": M, "us": round(us, 3), "GBps": round(nbytes / us * 1e-3, 1),
+                   "hbm_frac": round(nbytes / us * 1e-3 / (A.MI355X_HBM_BYTES_PER_S / 1e9), 4)})
+    big = nq[-1]
+    norm_quant = {
+        "kernel": "norm_quantize_act_i8 (LayerNorm, gamma + beta) K=%d" % K_DIM,
+        "per_m": nq,
+        "roofline": {"bound": "hbm", "achieved": big["GBps"], "peak": A.MI355X_HBM_BYTES_PER_S / 1e9,
+                     "unit": "GB/s", "frac": big["hbm_frac"], "traffic": None,
+                     "bytes_per_launch": A.norm_quant_bytes(MS[-1], K_DIM), "M": MS[-1]},
+        "unfused_bytes_per_launch": A.unfused_norm_quant_bytes(MS[-1], K_DIM),
+    }
+
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
@@ -176,10 +206,12 @@ def main():
                    "weight_copies": nrot, "wall_s": round(wall, 4)},
         "roofline": roofline,
         "per_m": per_m,
+        "norm_quant": norm_quant,
     }
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w_np, args.cpu_rows)
+        norm_quant["cpu_baseline"] = cpu_baseline_norm_quant()
 
     print(json.dumps(out), flush=True)
 
@@ -238,6 +270,20 @@ def cpu_baseline(w_np, rows):
             "kind": "oracle", "seconds": round(total_s, 3),
             "sample": "oracle act-quant + dequant + int64 GEMM + epilogue, K=4096 N=11008, token rows %s "
                       "(first rows of each M of the sweep)" % sample}
+
+
+def cpu_baseline_norm_quant(rows: int = 1024):
+    """The fused producer's oracle on a bounded sample: the first `rows` tokens of the M=4096 activations."""
+    import oracle as orc
+    from w4a8_quantized_linear_amd import accounting as A, workloads
+    x = workloads.activations(FAMILY, MS[-1], K_DIM, N_DIM)[:rows]
+    g, b = workloads.norm_affine(K_DIM)
+    t0 = time.perf_counter()
+    orc.norm_quantize_act(x, g, b, eps=1e-5)
+    s = time.perf_counter() - t0
+    return {"value": round(A.norm_quant_bytes(rows, K_DIM) / s / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds": round(s, 3),
+            "sample": "oracle LayerNorm + per-token INT8, K=%d, the first %d tokens of M=%d" % (K_DIM, rows, MS[-1])}
 
 
 if __name__ == "__main__":

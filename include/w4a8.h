@@ -115,6 +115,34 @@ w4a8_status quantize_act_per_token_i8(const uint16_t *x_fp16, int64_t M,
                                       float *s_a, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Normalization fused with the per-token INT8 quantization (QServe talk
+ * summary, "Precision Data Flow and Activation Quantization Fusion": the
+ * quantization is folded into the preceding layer, e.g. LayerNorm, which
+ * then writes the 8-bit activations directly).  Per token m:
+ *   LayerNorm (rms == 0): mean = exact row sum (in units of 2^-24) * 2^-24 / K
+ *                         (double); RMSNorm (rms == 1): mean = 0
+ *   var  = sum_k (double(x[m,k]) - mean)^2 / K          (double)
+ *   rstd = float(1 / sqrt(var + eps))   (0 when var + eps == 0)
+ *   h[k] = fp16_rne(((float(x) - float(mean)) * rstd) * float(gamma[k])
+ *                   + float(beta[k]))    (fp32, in that order; no beta: no add)
+ * then qx[m,:] and s_a[m] from h exactly as quantize_act_per_token_i8 would
+ * compute them from an fp16 row h.  The second moment is summed in double in
+ * a tree over lanes, so rstd may differ from a sequential sum's only when the
+ * double 1/sqrt lies within about K * 2^-53 (relative) of a midpoint between
+ * two floats.
+ * x_fp16: [M, K] fp16 bit patterns, row stride ldx >= K (multiple of 8).
+ * gamma_fp16: [K] fp16, required.  beta_fp16: [K] fp16 or NULL (no shift).
+ * eps: finite, >= 0.  rms: 0 or 1.  qx: [M, K] int8, row stride K; s_a: [M]
+ * fp32.  K <= 2^20 (W4A8_E_SHAPE otherwise) keeps the exact row sum in 64
+ * bits.  The normalized values must be finite in fp16 (larger results are
+ * unspecified, as for non-finite inputs).
+ * ------------------------------------------------------------------------ */
+w4a8_status norm_quantize_act_i8(const uint16_t *x_fp16, int64_t M, int64_t K,
+                                 int64_t ldx, const uint16_t *gamma_fp16,
+                                 const uint16_t *beta_fp16, float eps, int rms,
+                                 int8_t *qx, float *s_a, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * W4A8 GEMM (QServe talk summary, "Quantized Matrix Multiplication (GEMM)
  * Kernel on GPUs" and "Challenges and Design Details of QServe GEMM Kernel";
  * Lecture 15 notes, 15.5-15.6).

@@ -140,6 +140,33 @@ def test_act_quant_validation(lib):
 
 
 @needs_no_gpu
+def test_norm_quant_validation(lib):
+    f = lib.norm_quantize_act_i8
+
+    def call(x=A, M=4, K=128, ldx=128, g=A, b=NUL, eps=1e-5, rms=0, qx=A, sa=B):
+        return f(x, M, K, ldx, g, b, eps, rms, qx, sa, S)
+
+    assert call(M=0) == 0 and call(M=0, x=NUL, g=NUL, qx=NUL, sa=NUL) == 0
+    assert call(M=-1) == -2
+    assert call(K=100, ldx=100) == -2
+    assert call(ldx=64) == -2
+    assert call(ldx=130) == -2
+    assert call(K=(1 << 20) + 128, ldx=(1 << 20) + 128) == -2     # exact row sum would leave 64 bits
+    assert call(eps=-1.0) == -2
+    assert call(eps=float("nan")) == -2
+    assert call(eps=float("inf")) == -2
+    assert call(rms=2) == -2
+    assert call(x=NUL) == -1
+    assert call(g=NUL) == -1
+    assert call(qx=NUL) == -1
+    assert call(sa=NUL) == -1
+    assert call(x=MIS) == -3
+    assert call(g=MIS) == -3
+    assert call(b=MIS) == -3
+    assert call(sa=MIS) == -3
+
+
+@needs_no_gpu
 def test_gemm_validation(lib, monkeypatch):
     f = lib.gemm_w4a8
     ok = dict(qx=A, sa=A, w=A, s0=A, M=1, N=16, K=128, y=B, acc=NUL, ws=NUL, wsb=0)

@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     gemm_w4a8,
     gemm_w4a8_workspace_bytes,
     linear,
+    norm_quantize_act_i8,
     quantize_act_per_token_i8,
     quantize_weights_w4g128,
     status_string,
@@ -19,7 +20,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "W4A8Error", "gemm_w4a8", "gemm_w4a8_workspace_bytes", "linear", "quantize_act_per_token_i8",
+    "W4A8Error", "gemm_w4a8", "gemm_w4a8_workspace_bytes", "linear", "norm_quantize_act_i8",
+    "quantize_act_per_token_i8",
     "quantize_weights_w4g128", "status_string", "version", "w4a8_packed_weight_bytes",
     "w4a8_unpack_weights",
 ]

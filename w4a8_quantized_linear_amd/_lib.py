@@ -24,7 +24,7 @@ W4A8_E_HIP = -5
 EXPORTS = (
     "w4a8_status_string", "w4a8_version", "w4a8_packed_weight_bytes",
     "quantize_weights_w4g128", "w4a8_unpack_weights", "quantize_act_per_token_i8",
-    "gemm_w4a8_workspace_bytes", "gemm_w4a8",
+    "norm_quantize_act_i8", "gemm_w4a8_workspace_bytes", "gemm_w4a8",
 )
 
 _lock = threading.Lock()
@@ -60,6 +60,8 @@ def load() -> ctypes.CDLL:
         lib.w4a8_unpack_weights.restype = I32
         lib.quantize_act_per_token_i8.argtypes = [P, I64, I64, I64, P, P, P]
         lib.quantize_act_per_token_i8.restype = I32
+        lib.norm_quantize_act_i8.argtypes = [P, I64, I64, I64, P, P, ctypes.c_float, I32, P, P, P]
+        lib.norm_quantize_act_i8.restype = I32
         lib.gemm_w4a8_workspace_bytes.argtypes = [I64, I64, I64]
         lib.gemm_w4a8_workspace_bytes.restype = SZ
         lib.gemm_w4a8.argtypes = [P, P, P, P, I64, I64, I64, P, P, P, SZ, P]
@@ -147,6 +149,25 @@ def quantize_act_per_token_i8(x, *, qx=None, s_a=None, stream=None):
         s_a = torch.empty((M,), dtype=torch.float32, device=x.device)
     st = load().quantize_act_per_token_i8(_ptr(x), M, K, x.stride(0), _ptr(qx), _ptr(s_a), _stream(stream))
     _check(st, "quantize_act_per_token_i8")
+    return qx, s_a
+
+
+def norm_quantize_act_i8(x, gamma, beta=None, *, eps: float = 1e-5, rms: bool = False, qx=None,
+                         s_a=None, stream=None):
+    """LayerNorm (rms=False) or RMSNorm (rms=True) of fp16 rows [M, K] with fp16 gamma [K]
+    (and optional beta [K]), quantized per token -> (qx int8 [M, K], s_a fp32 [M])."""
+    import torch
+    assert x.dtype == torch.float16 and x.dim() == 2 and x.stride(1) == 1
+    M, K = x.shape
+    assert gamma.dtype == torch.float16 and gamma.shape == (K,) and gamma.is_contiguous()
+    assert beta is None or (beta.dtype == torch.float16 and beta.shape == (K,) and beta.is_contiguous())
+    if qx is None:
+        qx = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if s_a is None:
+        s_a = torch.empty((M,), dtype=torch.float32, device=x.device)
+    st = load().norm_quantize_act_i8(_ptr(x), M, K, x.stride(0), _ptr(gamma), _ptr(beta), float(eps),
+                                     int(bool(rms)), _ptr(qx), _ptr(s_a), _stream(stream))
+    _check(st, "norm_quantize_act_i8")
     return qx, s_a
 
 

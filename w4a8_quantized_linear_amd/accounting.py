@@ -80,6 +80,16 @@ def act_quant_bytes(M: int, K: int) -> int:
     return 2 * M * K + M * K + 4 * M
 
 
+def norm_quant_bytes(M: int, K: int, beta: bool = True) -> int:
+    """norm_quantize_act_i8: fp16 rows in once, int8 + fp32 out, plus the fp16 gamma (and beta) rows."""
+    return 2 * M * K + M * K + 4 * M + 2 * K * (2 if beta else 1)
+
+
+def unfused_norm_quant_bytes(M: int, K: int, beta: bool = True) -> int:
+    """The same result without the fusion: a normalization pass that writes fp16 rows, then the quantizer."""
+    return 2 * M * K + 2 * M * K + 2 * K * (2 if beta else 1) + act_quant_bytes(M, K)
+
+
 def gemm_ops(M: int, N: int, K: int) -> int:
     return 2 * M * N * K
 

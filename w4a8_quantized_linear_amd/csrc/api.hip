@@ -91,6 +91,24 @@ w4a8_status quantize_act_per_token_i8(const uint16_t *x_fp16, int64_t M, int64_t
     return hip_status(launch_act_quant(x_fp16, M, K, ldx, qx, s_a, stream));
 }
 
+w4a8_status norm_quantize_act_i8(const uint16_t *x_fp16, int64_t M, int64_t K, int64_t ldx,
+                                 const uint16_t *gamma_fp16, const uint16_t *beta_fp16, float eps,
+                                 int rms, int8_t *qx, float *s_a, hipStream_t stream)
+{
+    if (M < 0 || K <= 0 || K % kGroup != 0 || K > ((int64_t)1 << 20) || ldx < K || ldx % 8 != 0 ||
+        M > ((int64_t)1 << 31) - 1 || !(eps >= 0.0f && eps <= 3.4e38f) || (rms != 0 && rms != 1))
+        return W4A8_E_SHAPE;
+    if (M == 0)
+        return W4A8_OK;
+    if (!x_fp16 || !gamma_fp16 || !qx || !s_a)
+        return W4A8_E_NULL;
+    if (!aligned16(x_fp16) || !aligned16(gamma_fp16) || (beta_fp16 && !aligned16(beta_fp16)) ||
+        !aligned16(qx) || !aligned16(s_a))
+        return W4A8_E_ALIGN;
+    return hip_status(launch_norm_quant(x_fp16, M, K, ldx, gamma_fp16, beta_fp16, eps, rms, qx, s_a,
+                                        stream));
+}
+
 size_t gemm_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M <= 0 || M > kMaxM || !weight_shape_ok(N, K))

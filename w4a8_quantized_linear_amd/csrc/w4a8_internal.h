@@ -47,6 +47,9 @@ __host__ __device__ inline int64_t param_index(int64_t n, int64_t g, int64_t G4)
 // ---- launchers (defined in the kernel translation units) ----------------
 hipError_t launch_act_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                             int8_t *qx, float *s_a, hipStream_t st);
+hipError_t launch_norm_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                             const uint16_t *gamma, const uint16_t *beta, float eps, int rms,
+                             int8_t *qx, float *s_a, hipStream_t st);
 
 hipError_t launch_weight_quant(const float *w, int64_t N, int64_t K, uint8_t *stream_bytes,
                                uint8_t *s1, uint8_t *z, uint16_t *s0, hipStream_t st);

@@ -6,7 +6,8 @@ their inputs from it.
 
 Recipe (one per workload family; every draw is seeded):
   * generator: numpy PCG64 seeded by SeedSequence([0x57A8, family, K, N, tensor_id(, M)])
-    with tensor_id 0 = weights, 1 = activations (M appended), 2 = outlier channels;
+    with tensor_id 0 = weights, 1 = activations (M appended), 2 = outlier channels,
+    3 = the normalization's gamma and beta rows (family and N are 0 there);
   * weights: fp32, N(0, 0.02) -- or, for the heavy-tailed family, Student-t with
     nu = 4 scaled to the same std (divide by the population std sqrt(2));
   * activations: fp32 N(0, 1) with a fixed set of outlier channels (the same
@@ -15,6 +16,9 @@ Recipe (one per workload family; every draw is seeded):
 The outlier structure follows the pages' description of LLM activations: a
 small fraction of feature channels, fixed across tokens, tens to hundreds of
 times larger than the rest.
+  * normalization rows (the fused LayerNorm/RMSNorm producer): gamma =
+    fp16(1 + 0.1 N(0, 1)), beta = fp16(0.05 N(0, 1)), stand-ins for trained
+    affine parameters (no checkpoint is used).
 """
 from __future__ import annotations
 
@@ -88,6 +92,14 @@ def activations(family: int, M: int, K: int, N: int) -> np.ndarray:
     cols = outlier_channels(family, K, N)
     x[:, cols] *= np.float32(fam.outlier_scale)
     return x.astype(np.float16)
+
+
+def norm_affine(K: int) -> Tuple[np.ndarray, np.ndarray]:
+    """fp16 gamma [K] and beta [K] of the normalization in front of the quantizer."""
+    rng = _rng(0, K, 0, 3)
+    g = (1 + 0.1 * rng.standard_normal(K)).astype(np.float16)
+    b = (0.05 * rng.standard_normal(K)).astype(np.float16)
+    return g, b
 
 
 def all_cases():
