@@ -73,6 +73,8 @@ def _load():
         lib.orc_dequant_i8.restype = I64
         lib.orc_gemm_acc.argtypes = [P, P, I64, I64, I64, P]
         lib.orc_gemm_acc.restype = I64
+        lib.orc_gemm_w4a16.argtypes = [P, I64, I64, P, P, I64, P, P]
+        lib.orc_gemm_w4a16.restype = None
         lib.orc_epilogue.argtypes = [P, P, P, I64, I64, P]
         lib.orc_epilogue.restype = None
         lib.orc_linear.argtypes = [P, I64, I64, P, P, P, P, I64, P, P, P, P, P]
@@ -237,6 +239,22 @@ def epilogue(acc: np.ndarray, s_a: np.ndarray, s0: np.ndarray) -> np.ndarray:
     return y
 
 
+def gemm_w4a16(x_f16: np.ndarray, r: np.ndarray, s0: np.ndarray):
+    """W4A16: ref[m,n] = sum_k x[m,k] r[n,k] s0[n] in double, and the sum of the |terms|.
+
+    x: fp16 [M, K]; r: int8 [N, K] (from dequant_i8); s0: fp16 bits [N].  -> (ref, absref), double [M, N]."""
+    x = _as(x_f16, np.float16)
+    r = _as(r, np.int8)
+    s0 = _as(s0, np.uint16)
+    M, K = x.shape
+    N = r.shape[0]
+    assert r.shape == (N, K) and s0.shape == (N,)
+    ref = np.empty((M, N), np.float64)
+    absref = np.empty((M, N), np.float64)
+    _load().orc_gemm_w4a16(_p(x), M, K, _p(r), _p(s0), N, _p(ref), _p(absref))
+    return ref, absref
+
+
 def quantize_weights(w: np.ndarray) -> dict:
     """Both levels of the progressive weight quantization."""
     q8, s0 = weights_level1(w)
@@ -276,6 +294,6 @@ __all__ = [
     "GROUP", "PROTECT", "build", "f32_to_f16_bits", "f16_bits_to_f32", "f32_to_f16_bits_array",
     "rne_div", "num_threads", "quantize_act", "norm_quantize_act", "rstd_near_midpoint",
     "weights_level1", "weights_level2", "pack_q4",
-    "dequant_i8", "gemm_acc", "epilogue", "quantize_weights", "linear",
+    "dequant_i8", "gemm_acc", "gemm_w4a16", "epilogue", "quantize_weights", "linear",
     "linear_timed_buffers", "linear_into",
 ]

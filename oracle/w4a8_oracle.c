@@ -394,6 +394,38 @@ void orc_epilogue(const int32_t *acc, const float *s_a, const uint16_t *s0,
 }
 
 /* ------------------------------------------------------------------------ */
+/* W4A16 on the same weights: fp16 activations times the dequantized        */
+/* weights, no activation quantization.  QFactory notes 2.1 give the        */
+/* dequantization w = (w_quant - zero) * scale with a half-precision scale; */
+/* Lecture 15 notes 15.5 describe this int4 -> fp16 path inside the main    */
+/* loop.  With this build's two-level weights the dequantized weight is     */
+/* r[n,k] * s0[n], r = q4*s1 - z*s1 from orc_dequant_i8, so                 */
+/*   ref[m,n]    = sum_k x[m,k] * r[n,k] * s0[n]     (double)               */
+/*   absref[m,n] = sum_k |x[m,k] * r[n,k] * s0[n]|                          */
+/* Each product is exact in double (11 + 7 + 11 significant bits); the sums */
+/* are rounded, k in order.  absref scales the rounding error of an fp32    */
+/* evaluation, for the tolerance of the comparison.                         */
+/* ------------------------------------------------------------------------ */
+void orc_gemm_w4a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *r,
+                    const uint16_t *s0, int64_t N, double *ref, double *absref)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        const double sc = (double)orc_f16_to_f32(s0[n]);
+        for (int64_t m = 0; m < M; m++) {
+            double sum = 0.0, asum = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                const double p = (double)orc_f16_to_f32(x[m * K + k]) * (double)r[n * K + k] * sc;
+                sum = sum + p;
+                asum = asum + fabs(p);
+            }
+            ref[m * N + n] = sum;
+            absref[m * N + n] = asum;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* The whole serving-time path for one call, from fp16 activations and the  */
 /* level-2 weight form to fp16 outputs.  Used to time the oracle.           */
 /* r (int8 [N,K]) is caller-provided scratch.  Returns the number of        */

@@ -42,8 +42,13 @@ MUTANTS = [
      "mean = (double)(float)(ldexp((double)S, -24) / (double)K);"),
     ("norm rsqrt in single precision", "double r = ve == 0.0 ? INFINITY : 1.0 / sqrt(ve);",
      "double r = ve == 0.0 ? INFINITY : 1.0 / (double)sqrtf((float)ve);"),
+    ("w4a16 weight index transposed", "(double)r[n * K + k] * sc;", "(double)r[(k * N + n) % (N * K)] * sc;"),
+    ("w4a16 channel scale dropped", "const double sc = (double)orc_f16_to_f32(s0[n]);", "const double sc = 1.0;"),
+    ("w4a16 products in single precision",
+     "const double p = (double)orc_f16_to_f32(x[m * K + k]) * (double)r[n * K + k] * sc;",
+     "const double p = (double)(orc_f16_to_f32(x[m * K + k]) * (float)r[n * K + k] * (float)sc);"),
 ]
-PIN_FILES = ["test_oracle_pins.py", "test_oracle_norm_pins.py"]
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_norm_pins.py", "test_oracle_w4a16_pins.py"]
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
