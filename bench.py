@@ -11,10 +11,12 @@ so weight bytes really come from HBM.
 
 Prints one JSON line: whole-step throughput (TOPS), the roofline of the
 dominant kernel (the M=4096 GEMM), per-M kernel figures, and the CPU oracle
-timed on a bounded sample of the same workload.  A separate "norm_quant"
-object measures the fused LayerNorm + INT8 producer (norm_quantize_act_i8) on
-the same activations, against the HBM roofline, with its oracle beside it;
-it is not part of the step or of `value`.
+timed on a bounded sample of the same workload.  Two separate objects, not
+part of the step or of `value`, measure the other entry points on the same
+tensors against the HBM roofline, each with its oracle beside it:
+"norm_quant" (the fused LayerNorm + INT8 producer, norm_quantize_act_i8) and
+"w4a16" (the W4A16 GEMM on the same packed weights, gemm_w4a16, at the
+decode token counts, next to the W4A8 GEMM's times).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5]
 """
@@ -61,7 +63,7 @@ def main():
     import torch
 
     from w4a8_quantized_linear_amd import _lib, accounting as A, workloads
-    from w4a8_quantized_linear_amd import (gemm_w4a8, norm_quantize_act_i8,
+    from w4a8_quantized_linear_amd import (gemm_w4a8, gemm_w4a16, norm_quantize_act_i8,
                                            quantize_act_per_token_i8, quantize_weights_w4g128)
     if not os.path.exists(_lib.LIB_PATH):
         import __graft_entry__
@@ -195,6 +197,29 @@ def main():
         "unfused_bytes_per_launch": A.unfused_norm_quant_bytes(MS[-1], K_DIM),
     }
 
+    # ---- W4A16 on the same weights at the decode token counts (not part of the step)
+    w16 = []
+    for M in [m for m in MS if m <= 32]:
+        gemm_w4a16(xs[M], wcopies[0], s0, N_DIM, y=ys[M], stream=stream)   # (first call loads the kernel)
+        reps = args.reps
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for r in range(reps):
+            gemm_w4a16(xs[M], wcopies[r % nrot], s0, N_DIM, y=ys[M], stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / reps
+        nbytes = A.w4a16_bytes(M, N_DIM, K_DIM)
+        w8 = next(r for r in per_m if r["M"] == M)
+        w16.append({"M": M, "us": round(us, 3), "GBps": round(nbytes / us * 1e-3, 1),
+                    "hbm_frac": round(nbytes / us * 1e-3 / (A.MI355X_HBM_BYTES_PER_S / 1e9), 4),
+                    "w4a8_act_quant_plus_gemm_us": round(w8["act_quant_us"] + w8["gemm_us"], 3)})
+    w4a16 = {"kernel": "gemm_w4a16 K=%d N=%d" % (K_DIM, N_DIM), "per_m": w16,
+             "roofline": {"bound": "hbm", "achieved": w16[0]["GBps"], "peak": A.MI355X_HBM_BYTES_PER_S / 1e9,
+                          "unit": "GB/s", "frac": w16[0]["hbm_frac"], "traffic": None, "M": w16[0]["M"],
+                          "bytes_per_launch": A.w4a16_bytes(w16[0]["M"], N_DIM, K_DIM)}}
+
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
@@ -207,11 +232,13 @@ def main():
         "roofline": roofline,
         "per_m": per_m,
         "norm_quant": norm_quant,
+        "w4a16": w4a16,
     }
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w_np, args.cpu_rows)
         norm_quant["cpu_baseline"] = cpu_baseline_norm_quant()
+        w4a16["cpu_baseline"] = cpu_baseline_w4a16(w_np)
 
     print(json.dumps(out), flush=True)
 
@@ -284,6 +311,21 @@ def cpu_baseline_norm_quant(rows: int = 1024):
     return {"value": round(A.norm_quant_bytes(rows, K_DIM) / s / 1e9, 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle", "seconds": round(s, 3),
             "sample": "oracle LayerNorm + per-token INT8, K=%d, the first %d tokens of M=%d" % (K_DIM, rows, MS[-1])}
+
+
+def cpu_baseline_w4a16(w_np, rows: int = 8):
+    """The W4A16 oracle (double products and sums) on a bounded sample: the M = 8 activations."""
+    import oracle as orc
+    from w4a8_quantized_linear_amd import accounting as A, workloads
+    wq = orc.quantize_weights(w_np)
+    r, _ = orc.dequant_i8(wq["q4"], wq["s1"], wq["z"])
+    x = workloads.activations(FAMILY, rows, K_DIM, N_DIM)
+    t0 = time.perf_counter()
+    orc.gemm_w4a16(x, r, wq["s0"])
+    s = time.perf_counter() - t0
+    return {"value": round(A.w4a16_bytes(rows, N_DIM, K_DIM) / s / 1e9, 3), "unit": "GB/s",
+            "cores": orc.num_threads(), "kind": "oracle", "seconds": round(s, 3),
+            "sample": "oracle W4A16 (double), K=%d N=%d, M=%d" % (K_DIM, N_DIM, rows)}
 
 
 if __name__ == "__main__":

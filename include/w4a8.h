@@ -170,6 +170,25 @@ w4a8_status gemm_w4a8(const int8_t *qx, const float *s_a, const void *wpacked,
                       uint16_t *y_fp16, int32_t *acc_out, void *ws,
                       size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * W4A16 GEMM on the same weights: fp16 activations, no activation
+ * quantization; the weights are dequantized to fp16 inside the main loop
+ * (QFactory reading notes, 2.1: w = (w_quant - zero) * scale; Lecture 15
+ * notes, 15.5: the int4 -> fp16 path).  With the two-level weights the
+ * dequantized weight is r * s0[n], r = q4*s1 - z*s1 (an integer in
+ * [-127, 127]):
+ *   y[m,n] = fp16_rne( float(s0[n]) * sum_k x[m,k] * r[n,k] )
+ * with every product exact and the sum accumulated in fp32 on the matrix
+ * cores (order unspecified, deterministic run to run).
+ * x_fp16: [M, K] fp16, row stride ldx >= K (a multiple of 8).  wpacked and
+ * s0_fp16 as written by quantize_weights_w4g128.  y_fp16: [M, N] fp16,
+ * row-major.  Built for few tokens (the weight stream is read once per 16
+ * tokens).
+ * ------------------------------------------------------------------------ */
+w4a8_status gemm_w4a16(const uint16_t *x_fp16, int64_t M, int64_t K, int64_t ldx,
+                       const void *wpacked, const uint16_t *s0_fp16, int64_t N,
+                       uint16_t *y_fp16, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

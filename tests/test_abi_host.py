@@ -167,6 +167,28 @@ def test_norm_quant_validation(lib):
 
 
 @needs_no_gpu
+def test_w4a16_validation(lib):
+    f = lib.gemm_w4a16
+
+    def call(x=A, M=4, K=128, ldx=128, w=A, s0=A, N=16, y=B):
+        return f(x, M, K, ldx, w, s0, N, y, S)
+
+    assert call(M=0) == 0 and call(M=0, x=NUL, y=NUL) == 0
+    assert call(M=-1) == -2
+    assert call(K=100, ldx=100) == -2
+    assert call(N=24) == -2
+    assert call(ldx=64) == -2
+    assert call(ldx=132) == -2
+    assert call(x=NUL) == -1
+    assert call(w=NUL) == -1
+    assert call(s0=NUL) == -1
+    assert call(y=NUL) == -1
+    assert call(x=MIS) == -3
+    assert call(w=MIS) == -3
+    assert call(y=MIS) == -3
+
+
+@needs_no_gpu
 def test_gemm_validation(lib, monkeypatch):
     f = lib.gemm_w4a8
     ok = dict(qx=A, sa=A, w=A, s0=A, M=1, N=16, K=128, y=B, acc=NUL, ws=NUL, wsb=0)

@@ -24,7 +24,7 @@ W4A8_E_HIP = -5
 EXPORTS = (
     "w4a8_status_string", "w4a8_version", "w4a8_packed_weight_bytes",
     "quantize_weights_w4g128", "w4a8_unpack_weights", "quantize_act_per_token_i8",
-    "norm_quantize_act_i8", "gemm_w4a8_workspace_bytes", "gemm_w4a8",
+    "norm_quantize_act_i8", "gemm_w4a8_workspace_bytes", "gemm_w4a8", "gemm_w4a16",
 )
 
 _lock = threading.Lock()
@@ -66,6 +66,8 @@ def load() -> ctypes.CDLL:
         lib.gemm_w4a8_workspace_bytes.restype = SZ
         lib.gemm_w4a8.argtypes = [P, P, P, P, I64, I64, I64, P, P, P, SZ, P]
         lib.gemm_w4a8.restype = I32
+        lib.gemm_w4a16.argtypes = [P, I64, I64, I64, P, P, I64, P, P]
+        lib.gemm_w4a16.restype = I32
         _lib = lib
         return lib
 
@@ -205,6 +207,18 @@ def gemm_w4a8(qx, s_a, wpacked, s0, N: int, *, y=None, acc_out=None, ws=None, st
     st = load().gemm_w4a8(_ptr(qx), _ptr(s_a), _ptr(wpacked), _ptr(s0), M, N, K, _ptr(y),
                           _ptr(acc_out), _ptr(ws), wsb, _stream(stream))
     _check(st, "gemm_w4a8")
+    return y
+
+
+def gemm_w4a16(x, wpacked, s0, N: int, *, y=None, stream=None):
+    """fp16 activations [M, K] (row stride x.stride(0)) x packed weights -> fp16 y [M, N]."""
+    import torch
+    assert x.dtype == torch.float16 and x.dim() == 2 and x.stride(1) == 1
+    M, K = x.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    st = load().gemm_w4a16(_ptr(x), M, K, x.stride(0), _ptr(wpacked), _ptr(s0), N, _ptr(y), _stream(stream))
+    _check(st, "gemm_w4a16")
     return y
 
 

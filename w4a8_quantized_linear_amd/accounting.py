@@ -75,6 +75,11 @@ def gemm_bytes(M: int, N: int, K: int) -> int:
     return weight_stream_bytes(N, K) + M * K + 4 * M + 2 * M * N
 
 
+def w4a16_bytes(M: int, N: int, K: int) -> int:
+    """gemm_w4a16: weight stream + fp16 activations + fp16 output."""
+    return weight_stream_bytes(N, K) + 2 * M * K + 2 * M * N
+
+
 def act_quant_bytes(M: int, K: int) -> int:
     """quantize_act_per_token_i8: fp16 in (absmax pass + quantize pass read the same row) counted once, int8 + fp32 out."""
     return 2 * M * K + M * K + 4 * M

@@ -109,6 +109,22 @@ w4a8_status norm_quantize_act_i8(const uint16_t *x_fp16, int64_t M, int64_t K, i
                                         stream));
 }
 
+w4a8_status gemm_w4a16(const uint16_t *x_fp16, int64_t M, int64_t K, int64_t ldx,
+                       const void *wpacked, const uint16_t *s0_fp16, int64_t N, uint16_t *y_fp16,
+                       hipStream_t stream)
+{
+    if (M < 0 || M > ((int64_t)1 << 31) - 1 || !weight_shape_ok(N, K) || ldx < K || ldx % 8 != 0)
+        return W4A8_E_SHAPE;
+    if (M == 0)
+        return W4A8_OK;
+    if (!x_fp16 || !wpacked || !s0_fp16 || !y_fp16)
+        return W4A8_E_NULL;
+    if (!aligned16(x_fp16) || !aligned16(wpacked) || !aligned16(s0_fp16) || !aligned16(y_fp16))
+        return W4A8_E_ALIGN;
+    return hip_status(launch_gemm_w4a16(x_fp16, M, K, ldx, static_cast<const uint8_t *>(wpacked),
+                                        s0_fp16, N, y_fp16, stream));
+}
+
 size_t gemm_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M <= 0 || M > kMaxM || !weight_shape_ok(N, K))

@@ -1,0 +1,252 @@
+// gemm_w4a16.hip -- W4A16 GEMM on the W4A8 weight stream, gfx950.
+//
+// The activations stay fp16 (no per-token quantization) and the weights are
+// dequantized to fp16 inside the main loop: the QFactory reading notes (2.1)
+// give the dequantization w = (w_quant - zero) * scale, and Lecture 15 notes
+// (15.5) describe this int4 -> fp16 path as the one whose per-weight
+// instruction count decides decode time.  On the two-level weights of this
+// library the dequantized weight is r s0 with r = q4 s1 - z s1 (an integer in
+// [-127, 127]), so
+//   y[m,n] = fp16( s0[n] * sum_k x[m,k] r[n,k] )
+// with r exact in fp16, every product x r exact in fp32, the sums in fp32 on
+// the matrix cores (v_mfma_f32_16x16x32_f16) and s0 in the epilogue.
+//
+// Rebuild per 4 weights (one dword of codes): mask, v_pk_mad_u16 to the
+// biased bytes r + 128 (exactly as the W4A8 path, without its final xor),
+// then two v_perm_b32 that place each byte under the fp16 exponent of 1024
+// (0x64XX = 1024 + r + 128) and two v_pk_add_f16 of -1152: 1.75 VALU
+// instructions per weight with the shift, against 0.875 for int4 -> int8.
+//
+// Operand order.  A lane's 16-byte weight load holds, for its channel, the
+// codes of k = 16 kb + [0, 16) (low nibbles) and 64 + 16 kb + [0, 16) (high
+// nibbles), kb = lane / 16.  Each group is four MFMAs of 32 k; MFMA q takes
+// from every lane the 8 consecutive k = 8 (q & 1) + 64 (q >> 1) + 16 kb + j,
+// j < 8, for both operands (the activation operand of a lane is one 16-byte
+// load of those 8 halves), so the weights are used in their stored order and
+// the contraction still covers each k once.
+//
+// Work decomposition (decode shapes: the weight stream is read once per 16
+// tokens).  A workgroup of four waves owns NT tiles of 16 channels and 16
+// tokens; the waves split the K groups into four runs and stream their
+// weight tiles, parameter dwords and activation operands DEPTH groups ahead
+// (unconditional loads, so the compiler's vmcnt waits are exact).  The four
+// partial sums meet in LDS and are added in wave order (deterministic).
+#include <algorithm>
+#include <cstdlib>
+
+#include "w4a8_internal.h"
+
+namespace w4a8 {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBufFlags = 0x00020000;   // raw buffer resource, dword 3 (gfx9 family)
+constexpr int kWaves = 4;
+constexpr int kDepth = 4;                // groups of loads in flight per wave
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *p, int64_t bytes)
+{
+    const int64_t lim = bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)lim, kBufFlags);
+}
+
+// four biased bytes u = r + 128 (k order) -> two fp16 pairs r
+__device__ inline void to_half(uint32_t u, uint32_t &lo, uint32_t &hi)
+{
+    const h2 off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    lo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) + off);
+    hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) + off);
+}
+
+struct W16Args {
+    const uint16_t *x;        // [M, ldx] fp16
+    const uint8_t *codes;
+    const uint8_t *params;
+    const uint16_t *s0;       // [N] fp16
+    int64_t M, N, K, ldx;
+    uint16_t *y;              // [M, N] fp16
+};
+
+template <int NT>
+struct Slot {
+    v4i w[NT];                // codes of the NT tiles, one group
+    uint32_t p[NT];           // parameter dword (four groups) of the lane's channel
+    v4i x[4];                 // activation operands of the group's four MFMAs
+};
+
+template <int NT>
+__global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
+{
+    __shared__ f4 red[kWaves][NT][64];
+    const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int l = threadIdx.x & 63, lr = l & 15, kb = l >> 4;
+    const int nt0 = blockIdx.x * NT;                  // first 16-channel tile
+    const int ntiles = (int)(a.N / kTileN);
+    const int64_t m0 = (int64_t)blockIdx.y * 16;
+    const int G = (int)(a.K / kGroup), G4 = (int)groups_padded(a.K);
+    const int g0 = (int)((int64_t)G * wv / kWaves), g1 = (int)((int64_t)G * (wv + 1) / kWaves);
+
+    // tiles past N re-read the last tile (their outputs are not stored);
+    // tokens past M re-read the last token's row
+    const __amdgpu_buffer_rsrc_t rw = rsrc(a.codes, code_bytes(a.N, a.K));
+    const __amdgpu_buffer_rsrc_t rp = rsrc(a.params, param_bytes(a.N, a.K));
+    const __amdgpu_buffer_rsrc_t rx = rsrc(a.x, (a.M - 1) * a.ldx * 2 + a.K * 2);
+    int tile[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+        tile[t] = min(nt0 + t, ntiles - 1);
+    const int64_t row = min<int64_t>(m0 + lr, a.M - 1);
+    const int xoff = (int)(row * a.ldx * 2) + 32 * kb;    // bytes: token row, k-block
+    const int glast = max(g1 - 1, g0);
+
+    auto load = [&](Slot<NT> &s, int g) {
+        g = min(g, glast);
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            s.w[t] = __builtin_amdgcn_raw_buffer_load_b128(rw, 16 * l, ((int64_t)tile[t] * G + g) * kTileBytes, 2);
+            s.p[t] = __builtin_amdgcn_raw_buffer_load_b32(rp, (int)(param_index(tile[t] * 16 + lr, g, G4) & ~3),
+                                                          0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+            s.x[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff, g * 256 + 2 * (8 * (q & 1) + 64 * (q >> 1)), 0);
+    };
+
+    f4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+        acc[t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    Slot<NT> ring[kDepth];
+#pragma unroll
+    for (int d = 0; d < kDepth; d++)
+        load(ring[d], g0 + d);
+
+    auto step = [&](Slot<NT> &s, int g) {
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            const uint32_t pb = (s.p[t] >> (8 * (g & 3))) & 0xFFu;
+            const uint32_t s1 = (pb & 15u) + 1u;
+            const uint32_t c16 = ((128u - (pb >> 4) * s1) * 257u) & 0xFFFFu;
+            const us2 S = {(unsigned short)s1, (unsigned short)s1};
+            const us2 C = {(unsigned short)c16, (unsigned short)c16};
+            uint32_t b[2][4][2];   // [k-half][dword][pair]: fp16 pairs of the rebuilt weights
+#pragma unroll
+            for (int d = 0; d < 4; d++) {
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const uint32_t nib = ((uint32_t)s.w[t][d] >> (4 * h)) & 0x0F0F0F0Fu;
+                    const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_bit_cast(us2, nib) * S + C);
+                    to_half(u, b[h][d][0], b[h][d][1]);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int h = q >> 1, d0 = 2 * (q & 1);
+                const v4i bw = {(int)b[h][d0][0], (int)b[h][d0][1], (int)b[h][d0 + 1][0], (int)b[h][d0 + 1][1]};
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, s.x[q]),
+                                                                __builtin_bit_cast(h8, bw), acc[t], 0, 0, 0);
+            }
+        }
+        load(s, g + kDepth);
+    };
+
+    int g = g0;
+    for (; g + kDepth <= g1; g += kDepth) {
+#pragma unroll
+        for (int d = 0; d < kDepth; d++)
+            step(ring[d], g + d);
+    }
+#pragma unroll
+    for (int d = 0; d < kDepth - 1; d++)
+        if (g + d < g1)
+            step(ring[d], g + d);
+
+    // the waves' partial sums, added in wave order; lane l holds tokens
+    // 4 (l / 16) + r, channel l % 16 of each tile
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+        red[wv][t][l] = acc[t];
+    __syncthreads();
+    if (wv == 0) {
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            f4 v = red[0][t][l];
+#pragma unroll
+            for (int w = 1; w < kWaves; w++)
+                v += red[w][t][l];
+            if (nt0 + t >= ntiles)
+                continue;
+            const int64_t n = (int64_t)(nt0 + t) * 16 + lr;
+            const float sc = (float)__builtin_bit_cast(_Float16, a.s0[n]);
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int64_t m = m0 + 4 * kb + r;
+                if (m < a.M)
+                    a.y[m * a.N + n] = __builtin_bit_cast(uint16_t, (_Float16)(v[r] * sc));
+            }
+        }
+    }
+}
+
+template <int NT>
+hipError_t launch_nt(const W16Args &a, hipStream_t st)
+{
+    const int64_t nblk = (a.N / kTileN + NT - 1) / NT;
+    const int64_t mblk = (a.M + 15) / 16;
+    hipLaunchKernelGGL(gemm_w4a16_kernel<NT>, dim3((unsigned)nblk, (unsigned)mblk), dim3(64 * kWaves), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Tiles per workgroup.  Every workgroup reads the activation operands of its
+// 16 tokens from L2 once, so NT tiles share that read: with more than 8
+// distinct tokens it costs as much as the weight tiles and four tiles per
+// workgroup pay off when at least 128 workgroups remain; otherwise two tiles
+// when that still leaves 256 workgroups per 16 tokens (or there are several
+// token blocks), else one.  W4A8_W16_NT=1|2|4 overrides (sweeps).
+static int pick_nt(int64_t M, int64_t N)
+{
+    const int64_t tiles = N / kTileN;
+    if (M > 8 && tiles >= 512)
+        return 4;
+    if (tiles >= 512 || M > 16)
+        return 2;
+    return 1;
+}
+
+hipError_t launch_gemm_w4a16(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                             const uint8_t *stream_bytes, const uint16_t *s0, int64_t N, uint16_t *y,
+                             hipStream_t st)
+{
+    // the activations are addressed with 32-bit buffer offsets: launches of
+    // at most rows_max tokens
+    const int64_t rows_max = std::max<int64_t>(16, (0x7FFFFFFF - 2 * K) / (2 * ldx) / 16 * 16);
+    for (int64_t r0 = 0; r0 < M; r0 += rows_max) {
+        W16Args a;
+        a.x = x + r0 * ldx;
+        a.codes = stream_bytes;
+        a.params = stream_bytes + code_bytes(N, K);
+        a.s0 = s0;
+        a.M = std::min(rows_max, M - r0);
+        a.N = N;
+        a.K = K;
+        a.ldx = ldx;
+        a.y = y + r0 * N;
+        int nt = pick_nt(a.M, N);
+        if (const char *env = std::getenv("W4A8_W16_NT"))
+            nt = std::atoi(env) == 4 ? 4 : (std::atoi(env) == 2 ? 2 : (std::atoi(env) == 1 ? 1 : nt));
+        const hipError_t e = nt == 4 ? launch_nt<4>(a, st) : (nt == 2 ? launch_nt<2>(a, st) : launch_nt<1>(a, st));
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace w4a8

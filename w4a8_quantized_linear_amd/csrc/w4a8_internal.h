@@ -51,6 +51,10 @@ hipError_t launch_norm_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ld
                              const uint16_t *gamma, const uint16_t *beta, float eps, int rms,
                              int8_t *qx, float *s_a, hipStream_t st);
 
+hipError_t launch_gemm_w4a16(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                             const uint8_t *stream_bytes, const uint16_t *s0, int64_t N, uint16_t *y,
+                             hipStream_t st);
+
 hipError_t launch_weight_quant(const float *w, int64_t N, int64_t K, uint8_t *stream_bytes,
                                uint8_t *s1, uint8_t *z, uint16_t *s0, hipStream_t st);
 
