@@ -75,6 +75,11 @@ def _load():
         lib.orc_gemm_acc.restype = I64
         lib.orc_gemm_w4a16.argtypes = [P, I64, I64, P, P, I64, P, P]
         lib.orc_gemm_w4a16.restype = None
+        lib.orc_quantize_kv4.argtypes = [P, I64, I64, P, P, P]
+        lib.orc_quantize_kv4.restype = None
+        lib.orc_kv4_attention.argtypes = [P, I64, I64, I64, I64, P, P, P, P, P, P, I64, P,
+                                          ctypes.c_double, P, P, P, P]
+        lib.orc_kv4_attention.restype = None
         lib.orc_epilogue.argtypes = [P, P, P, I64, I64, P]
         lib.orc_epilogue.restype = None
         lib.orc_linear.argtypes = [P, I64, I64, P, P, P, P, I64, P, P, P, P, P]
@@ -255,6 +260,48 @@ def gemm_w4a16(x_f16: np.ndarray, r: np.ndarray, s0: np.ndarray):
     return ref, absref
 
 
+def quantize_kv4(x_f16: np.ndarray) -> dict:
+    """4-bit KV cache rows: x fp16 [..., D] -> codes uint8 [..., D] (one per byte),
+    s fp16 bits uint16 [...], z uint8 [...]; x ~ (codes - z) * s."""
+    x = _as(x_f16, np.float16)
+    D = x.shape[-1]
+    lead = x.shape[:-1]
+    rows = int(np.prod(lead)) if lead else 1
+    codes = np.empty(x.shape, np.uint8)
+    s = np.empty(lead, np.uint16)
+    z = np.empty(lead, np.uint8)
+    _load().orc_quantize_kv4(_p(x.view(np.uint16)), rows, D, _p(codes), _p(s), _p(z))
+    return {"codes": codes, "s": s, "z": z}
+
+
+def kv4_dequant(kv: dict) -> np.ndarray:
+    """(codes - z) * s in double."""
+    s = np.array(kv["s"], np.uint16).view(np.float16).astype(np.float64)
+    return (kv["codes"].astype(np.float64) - kv["z"][..., None].astype(np.float64)) * s[..., None]
+
+
+def kv4_attention(q_f16: np.ndarray, k: dict, v: dict, lens: np.ndarray, sm_scale: float) -> dict:
+    """Decode attention over the 4-bit cache.  q: fp16 [B, Hq, D]; k, v: quantize_kv4 outputs
+    of shape [B, Hkv, S, D]; lens int32 [B].  -> dict of double arrays: out, absout [B, Hq, D],
+    score, absscore [B, Hq, S]."""
+    q = _as(q_f16, np.float16)
+    B, Hq, D = q.shape
+    _, Hkv, S, D2 = k["codes"].shape
+    assert D2 == D and Hq % Hkv == 0 and v["codes"].shape == k["codes"].shape
+    lens = _as(lens, np.int32)
+    assert lens.shape == (B,) and np.all((lens >= 0) & (lens <= S))
+    out = np.empty((B, Hq, D), np.float64)
+    absout = np.empty((B, Hq, D), np.float64)
+    score = np.empty((B, Hq, S), np.float64)
+    absscore = np.empty((B, Hq, S), np.float64)
+    kc, ks, kz = (_as(k["codes"], np.uint8), _as(k["s"], np.uint16), _as(k["z"], np.uint8))
+    vc, vs, vz = (_as(v["codes"], np.uint8), _as(v["s"], np.uint16), _as(v["z"], np.uint8))
+    _load().orc_kv4_attention(_p(q.view(np.uint16)), B, Hq, Hkv, D, _p(kc), _p(ks), _p(kz), _p(vc), _p(vs),
+                              _p(vz), S, _p(lens), float(sm_scale), _p(out), _p(absout), _p(score),
+                              _p(absscore))
+    return {"out": out, "absout": absout, "score": score, "absscore": absscore}
+
+
 def quantize_weights(w: np.ndarray) -> dict:
     """Both levels of the progressive weight quantization."""
     q8, s0 = weights_level1(w)
@@ -295,5 +342,6 @@ __all__ = [
     "rne_div", "num_threads", "quantize_act", "norm_quantize_act", "rstd_near_midpoint",
     "weights_level1", "weights_level2", "pack_q4",
     "dequant_i8", "gemm_acc", "gemm_w4a16", "epilogue", "quantize_weights", "linear",
+    "quantize_kv4", "kv4_dequant", "kv4_attention",
     "linear_timed_buffers", "linear_into",
 ]

@@ -426,6 +426,139 @@ void orc_gemm_w4a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *r,
 }
 
 /* ------------------------------------------------------------------------ */
+/* KV cache: 4-bit asymmetric quantization per (token, head).               */
+/* The QServe talk summary ("Smooth Attention for K4V4 KV Cache             */
+/* Compression", "Attention Computation Acceleration") stores keys and      */
+/* values in 4 bits with zero points and scaling factors that the attention */
+/* kernel prefetches, and ("Long Context Challenges") has those factors     */
+/* grow with the sequence: one (scale, zero) per cached token and head.    */
+/* The form is the QFactory notes' (2.1) asymmetric one,                    */
+/*   x ~ (code - zero) * scale.                                             */
+/* Readings, the same as the weights' level 2 where they apply:             */
+/*   - the range includes 0: lo = min(0, min x), hi = max(0, max x), so the  */
+/*     zero point lies in [0, 15] and 0 is represented exactly;            */
+/*   - scale = fp16((hi - lo) / 15) (fp32 subtraction and IEEE division,    */
+/*     then round to nearest even); the codes divide by that stored value;  */
+/*   - zero = rint(-lo / scale) and code = rint(x / scale) + zero, both in  */
+/*     fp32 with ties to even and clamped to [0, 15];                        */
+/*   - a row whose scale rounds to 0 stores scale 0, zero 0 and codes 0.    */
+/* x: fp16 bits [rows, D]; codes one per byte [rows, D]; s fp16 bits, z.    */
+/* ------------------------------------------------------------------------ */
+void orc_quantize_kv4(const uint16_t *x, int64_t rows, int64_t D, uint8_t *codes,
+                      uint16_t *s, uint8_t *z)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; i++) {
+        const uint16_t *xi = x + i * D;
+        float lo = 0.0f, hi = 0.0f;
+        for (int64_t d = 0; d < D; d++) {
+            const float v = orc_f16_to_f32(xi[d]);
+            if (v < lo)
+                lo = v;
+            if (v > hi)
+                hi = v;
+        }
+        const uint16_t sh = orc_f32_to_f16((hi - lo) / 15.0f);
+        const float sf = orc_f16_to_f32(sh);
+        s[i] = sh;
+        if (sf == 0.0f) {
+            s[i] = 0;
+            z[i] = 0;
+            for (int64_t d = 0; d < D; d++)
+                codes[i * D + d] = 0;
+            continue;
+        }
+        const float zf = clampf(rintf(-lo / sf), 0.0f, 15.0f);
+        z[i] = (uint8_t)zf;
+        for (int64_t d = 0; d < D; d++) {
+            const float t = rintf(orc_f16_to_f32(xi[d]) / sf) + zf;
+            codes[i * D + d] = (uint8_t)clampf(t, 0.0f, 15.0f);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention over the 4-bit cache.  One new query token per          */
+/* sequence; the cache is dequantized as (code - zero) * scale (QServe talk */
+/* summary, "Attention Computation Acceleration": the 4-bit elements are    */
+/* converted for the score computation; Lecture 15 notes, 15.6: the kernel  */
+/* works on the int4 cache directly and never writes it back at higher      */
+/* precision).  For sequence b and query head h, with kv head g = h / (Hq / */
+/* Hkv) (consecutive query heads share a kv head) and L = lens[b] tokens:  */
+/*   score_t = sm_scale * sum_d q[d] * kdq[t, d]          (t < L)           */
+/*   p_t     = exp(score_t - max_t score_t)                                 */
+/*   out[d]  = sum_t p_t vdq[t, d] / sum_t p_t                              */
+/* all in double (each q * (code - zero) is exact, and the sums of those    */
+/* exact products over D = 128 are exact too); L = 0 gives out = 0.         */
+/* Also returned, for error bounds: absout[d] = sum_t p_t |vdq[t, d]| /     */
+/* sum_t p_t, score_t and absscore_t = sm_scale * sum_d |q[d] kdq[t, d]|    */
+/* (both 0 for t >= L).  Codes one per byte [B, Hkv, S, D]; scales fp16     */
+/* bits and zeros [B, Hkv, S]; q [B, Hq, D] fp16 bits; out [B, Hq, D].      */
+/* ------------------------------------------------------------------------ */
+void orc_kv4_attention(const uint16_t *q, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                       const uint8_t *kc, const uint16_t *ks, const uint8_t *kz,
+                       const uint8_t *vc, const uint16_t *vs, const uint8_t *vz,
+                       int64_t S, const int32_t *lens, double sm_scale,
+                       double *out, double *absout, double *score, double *absscore)
+{
+    const int64_t G = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; b++) {
+        for (int64_t h = 0; h < Hq; h++) {
+            const int64_t g = h / G;
+            const int64_t L = lens[b];
+            const uint16_t *qh = q + (b * Hq + h) * D;
+            const int64_t row0 = (b * Hkv + g) * S;      /* first cache row of (b, g) */
+            double *sc = score + (b * Hq + h) * S;
+            double *asc = absscore + (b * Hq + h) * S;
+            double *o = out + (b * Hq + h) * D;
+            double *ao = absout + (b * Hq + h) * D;
+            for (int64_t t = 0; t < S; t++) {
+                sc[t] = 0.0;
+                asc[t] = 0.0;
+            }
+            for (int64_t d = 0; d < D; d++) {
+                o[d] = 0.0;
+                ao[d] = 0.0;
+            }
+            if (L == 0)
+                continue;
+            double mx = -INFINITY;
+            for (int64_t t = 0; t < L; t++) {
+                const double kscale = (double)orc_f16_to_f32(ks[row0 + t]);
+                double dot = 0.0, adot = 0.0;
+                for (int64_t d = 0; d < D; d++) {
+                    const double kd = ((double)kc[(row0 + t) * D + d] - (double)kz[row0 + t]) * kscale;
+                    const double prod = (double)orc_f16_to_f32(qh[d]) * kd;
+                    dot = dot + prod;
+                    adot = adot + fabs(prod);
+                }
+                sc[t] = sm_scale * dot;
+                asc[t] = sm_scale * adot;
+                if (sc[t] > mx)
+                    mx = sc[t];
+            }
+            double den = 0.0;
+            for (int64_t t = 0; t < L; t++)
+                den = den + exp(sc[t] - mx);
+            for (int64_t t = 0; t < L; t++) {
+                const double p = exp(sc[t] - mx);
+                const double vscale = (double)orc_f16_to_f32(vs[row0 + t]);
+                for (int64_t d = 0; d < D; d++) {
+                    const double vd = ((double)vc[(row0 + t) * D + d] - (double)vz[row0 + t]) * vscale;
+                    o[d] = o[d] + p * vd;
+                    ao[d] = ao[d] + p * fabs(vd);
+                }
+            }
+            for (int64_t d = 0; d < D; d++) {
+                o[d] = o[d] / den;
+                ao[d] = ao[d] / den;
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* The whole serving-time path for one call, from fp16 activations and the  */
 /* level-2 weight form to fp16 outputs.  Used to time the oracle.           */
 /* r (int8 [N,K]) is caller-provided scratch.  Returns the number of        */

@@ -47,8 +47,25 @@ MUTANTS = [
     ("w4a16 products in single precision",
      "const double p = (double)orc_f16_to_f32(x[m * K + k]) * (double)r[n * K + k] * sc;",
      "const double p = (double)(orc_f16_to_f32(x[m * K + k]) * (float)r[n * K + k] * (float)sc);"),
+    ("kv range without zero", "float lo = 0.0f, hi = 0.0f;\n        for (int64_t d = 0; d < D; d++) {\n            const float v",
+     "float lo = INFINITY, hi = -INFINITY;\n        for (int64_t d = 0; d < D; d++) {\n            const float v"),
+    ("kv sixteen levels", "orc_f32_to_f16((hi - lo) / 15.0f)", "orc_f32_to_f16((hi - lo) / 16.0f)"),
+    ("kv zero point truncated", "clampf(rintf(-lo / sf), 0.0f, 15.0f)", "clampf(truncf(-lo / sf), 0.0f, 15.0f)"),
+    ("kv code ties away from zero", "rintf(orc_f16_to_f32(xi[d]) / sf) + zf", "roundf(orc_f16_to_f32(xi[d]) / sf) + zf"),
+    ("kv key zero not subtracted", "((double)kc[(row0 + t) * D + d] - (double)kz[row0 + t]) * kscale",
+     "((double)kc[(row0 + t) * D + d]) * kscale"),
+    ("kv value zero added", "((double)vc[(row0 + t) * D + d] - (double)vz[row0 + t]) * vscale",
+     "((double)vc[(row0 + t) * D + d] + (double)vz[row0 + t]) * vscale"),
+    ("kv head modulo instead of group", "const int64_t g = h / G;", "const int64_t g = h % Hkv;"),
+    ("attention scale dropped", "sc[t] = sm_scale * dot;", "sc[t] = dot;"),
+    ("softmax normalizer without the max", "den = den + exp(sc[t] - mx);", "den = den + exp(sc[t]);"),
+    ("value scale taken from the keys", "const double vscale = (double)orc_f16_to_f32(vs[row0 + t]);",
+     "const double vscale = (double)orc_f16_to_f32(ks[row0 + t]);"),
+    ("attention length off by one", "for (int64_t t = 0; t < L; t++) {\n                const double kscale",
+     "for (int64_t t = 0; t <= L && t < S; t++) {\n                const double kscale"),
 ]
-PIN_FILES = ["test_oracle_pins.py", "test_oracle_norm_pins.py", "test_oracle_w4a16_pins.py"]
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_norm_pins.py", "test_oracle_w4a16_pins.py",
+             "test_oracle_kv4_pins.py"]
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
