@@ -16,7 +16,9 @@ part of the step or of `value`, measure the other entry points on the same
 tensors against the HBM roofline, each with its oracle beside it:
 "norm_quant" (the fused LayerNorm + INT8 producer, norm_quantize_act_i8) and
 "w4a16" (the W4A16 GEMM on the same packed weights, gemm_w4a16, at the
-decode token counts, next to the W4A8 GEMM's times).
+decode token counts, next to the W4A8 GEMM's times) and "kv4_attention"
+(decode attention over the 4-bit KV cache, attention_kv4_decode, on the
+reference 7B at a 4,096-token context, multi-head and with 8 kv heads).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5]
 """
@@ -220,6 +222,8 @@ def main():
                           "unit": "GB/s", "frac": w16[0]["hbm_frac"], "traffic": None, "M": w16[0]["M"],
                           "bytes_per_launch": A.w4a16_bytes(w16[0]["M"], N_DIM, K_DIM)}}
 
+    kv4 = bench_kv4(args, stream)
+
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
@@ -233,12 +237,14 @@ def main():
         "per_m": per_m,
         "norm_quant": norm_quant,
         "w4a16": w4a16,
+        "kv4_attention": kv4,
     }
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w_np, args.cpu_rows)
         norm_quant["cpu_baseline"] = cpu_baseline_norm_quant()
         w4a16["cpu_baseline"] = cpu_baseline_w4a16(w_np)
+        kv4["cpu_baseline"] = cpu_baseline_kv4()
 
     print(json.dumps(out), flush=True)
 
@@ -311,6 +317,89 @@ def cpu_baseline_norm_quant(rows: int = 1024):
     return {"value": round(A.norm_quant_bytes(rows, K_DIM) / s / 1e9, 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle", "seconds": round(s, 3),
             "sample": "oracle LayerNorm + per-token INT8, K=%d, the first %d tokens of M=%d" % (K_DIM, rows, MS[-1])}
+
+
+def bench_kv4(args, stream):
+    """Decode attention over the 4-bit KV cache on each configuration (every sequence
+    at the full context), and the one-token append that precedes it in a decode step."""
+    import torch
+
+    from w4a8_quantized_linear_amd import (accounting as A, attention_kv4_decode, kv4_attention_workspace_bytes,
+                                           kv4_cache_alloc, quantize_kv4, workloads as W)
+    dev = torch.device("cuda:0")
+    res = {}
+    for name, cfg in sorted(W.KV_CONFIGS.items()):
+        B, Hq, Hkv, S = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["S"]
+        kc, vc = kv4_cache_alloc(B, Hkv, S, device=dev)
+        for part in range(S // 256):
+            k, v = W.kv_rows_torch(41, B, 256, Hkv, part, dev)
+            quantize_kv4(k, v, torch.full((B,), part * 256, dtype=torch.int32, device=dev), kc, vc, S, stream=stream)
+        del k, v
+        q = torch.from_numpy(W.kv_query(41, B, Hq)).to(dev)
+        lens = torch.full((B,), S, dtype=torch.int32, device=dev)
+        out = torch.empty_like(q)
+        ws = torch.empty(max(1, kv4_attention_workspace_bytes(B, Hq, S)), dtype=torch.uint8, device=dev)
+        sm = 1.0 / math.sqrt(128)
+        attention_kv4_decode(q, kc, vc, S, Hkv, lens, sm, out=out, ws=ws, stream=stream)
+        torch.cuda.synchronize()
+        reps = max(10, args.reps // 2)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            attention_kv4_decode(q, kc, vc, S, Hkv, lens, sm, out=out, ws=ws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / reps
+        nbytes = A.kv4_attention_bytes([S] * B, Hq, Hkv)
+        # the decode step's append: one new token per sequence, written at position S - 1
+        k1, v1 = W.kv_rows_torch(42, B, 1, Hkv, 0, dev)
+        pos = torch.full((B,), S - 1, dtype=torch.int32, device=dev)
+        quantize_kv4(k1, v1, pos, kc, vc, S, stream=stream)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            quantize_kv4(k1, v1, pos, kc, vc, S, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        qus = 1e3 * e0.elapsed_time(e1) / reps
+        res[name] = {"B": B, "Hq": Hq, "Hkv": Hkv, "S": S, "head_dim": 128, "attention_us": round(us, 3),
+                     "bytes_per_launch": nbytes, "GBps": round(nbytes / us * 1e-3, 1),
+                     "hbm_frac": round(nbytes / us * 1e-3 / (A.MI355X_HBM_BYTES_PER_S / 1e9), 4),
+                     "tokens_per_s": round(B / us * 1e6, 1), "append_one_token_us": round(qus, 3)}
+        del kc, vc, ws
+        torch.cuda.empty_cache()
+    first = res[sorted(res)[0]]
+    return {"kernel": "attention_kv4_decode (kv4_attn_kernel + kv4_combine_kernel), every sequence at S",
+            "configs": res,
+            "roofline": {"bound": "hbm", "achieved": first["GBps"], "peak": A.MI355X_HBM_BYTES_PER_S / 1e9,
+                         "unit": "GB/s", "frac": first["hbm_frac"], "traffic": None, "config": sorted(res)[0],
+                         "bytes_per_launch": first["bytes_per_launch"]}}
+
+
+def cpu_baseline_kv4(seqs: int = 2):
+    """The oracle's KV4 attention (double) on a bounded sample: `seqs` sequences of the
+    multi-head configuration at the full context, all 32 heads."""
+    import numpy as np
+
+    import oracle as orc
+    from w4a8_quantized_linear_amd import accounting as A, workloads as W
+    cfg = W.KV_CONFIGS["7b_mha"]
+    Hq, Hkv, S = cfg["Hq"], cfg["Hkv"], cfg["S"]
+    k, v = W.kv_rows(43, seqs, S, Hkv)
+    kq = orc.quantize_kv4(np.ascontiguousarray(k.transpose(0, 2, 1, 3)))
+    vq = orc.quantize_kv4(np.ascontiguousarray(v.transpose(0, 2, 1, 3)))
+    q = W.kv_query(43, seqs, Hq)
+    lens = np.full(seqs, S, np.int32)
+    calls, t0 = 0, time.perf_counter()
+    while calls == 0 or time.perf_counter() - t0 < 2.0:
+        orc.kv4_attention(q, kq, vq, lens, 1.0 / math.sqrt(128))
+        calls += 1
+    s = (time.perf_counter() - t0) / calls
+    return {"value": round(A.kv4_attention_bytes([S] * seqs, Hq, Hkv) / s / 1e9, 3), "unit": "GB/s",
+            "cores": orc.num_threads(), "kind": "oracle", "seconds": round(s * calls, 3),
+            "sample": "oracle KV4 decode attention (double), 7b_mha: %d sequences x %d tokens x %d heads, "
+                      "%d calls" % (seqs, S, Hq, calls)}
 
 
 def cpu_baseline_w4a16(w_np, rows: int = 8):

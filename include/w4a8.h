@@ -189,6 +189,67 @@ w4a8_status gemm_w4a16(const uint16_t *x_fp16, int64_t M, int64_t K, int64_t ldx
                        const void *wpacked, const uint16_t *s0_fp16, int64_t N,
                        uint16_t *y_fp16, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * 4-bit KV cache and decode attention over it.
+ *
+ * Format (QServe talk summary, "Smooth Attention for K4V4 KV Cache
+ * Compression", "Attention Computation Acceleration", "Long Context
+ * Challenges": 4-bit keys and values with per-token zero points and scales;
+ * QFactory reading notes, 2.1: x ~ (code - zero) * scale).  Every (token,
+ * kv head) row of head_dim = 128 values is quantized on its own:
+ *   lo = min(0, min x), hi = max(0, max x)
+ *   scale = fp16_rne((hi - lo) / 15)            (fp32 subtraction, IEEE division)
+ *   zero  = clamp(rint(-lo / scale), 0, 15)     (fp32, ties to even)
+ *   code  = clamp(rint(x / scale) + zero, 0, 15)
+ * and a row whose scale rounds to 0 stores scale 0, zero 0 and codes 0.
+ * Inputs must be finite.
+ *
+ * A cache is one device buffer of kv4_cache_bytes(B, Hkv, S) bytes for the
+ * keys and one of the same size for the values, for B sequences, Hkv kv heads
+ * and a capacity of S tokens (S > 0, a multiple of 32).  Its layout is
+ * private (read it back with kv4_unpack); only its size is part of the ABI.
+ * Caches are caller-owned device memory; their content before the first
+ * write is irrelevant.
+ * ------------------------------------------------------------------------ */
+size_t kv4_cache_bytes(int64_t B, int64_t Hkv, int64_t S);
+
+/* Quantize T new tokens per sequence and write them into the caches at
+ * positions pos[b] .. pos[b] + T - 1 (pos: device int32 [B]; tokens at or
+ * past the capacity S, and sequences with pos[b] < 0, are not written).
+ * k_fp16, v_fp16: [B, T, Hkv, 128] fp16, contiguous (the layout of a fused
+ * QKV projection's K and V columns for T tokens of each sequence).  Calls
+ * that write the same cache must be ordered on one stream. */
+w4a8_status quantize_kv4(const uint16_t *k_fp16, const uint16_t *v_fp16, int64_t B, int64_t Hkv,
+                         int64_t T, const int32_t *pos, void *k_cache, void *v_cache, int64_t S,
+                         hipStream_t stream);
+
+/* Test inverse of the cache layout: the logical codes [B, Hkv, S, 128] (one
+ * per byte), scales [B, Hkv, S] (fp16 bits) and zeros [B, Hkv, S] of one
+ * cache (is_v = 0: a key cache, 1: a value cache). */
+w4a8_status kv4_unpack(const void *cache, int is_v, int64_t B, int64_t Hkv, int64_t S,
+                       uint8_t *codes, uint16_t *scales_fp16, uint8_t *zeros, hipStream_t stream);
+
+/* Decode attention: one query token per sequence over the first lens[b]
+ * cached tokens (lens: device int32 [B]; values above S are taken as S,
+ * negative ones as 0).  For query head h, kv head g = h / (Hq / Hkv)
+ * (consecutive query heads share a kv head; Hq / Hkv <= 16):
+ *   score_t = sm_scale * sum_d q[d] * (kcode[t,d] - kzero[t]) * kscale[t]
+ *   out[d]  = sum_t softmax(score)_t * (vcode[t,d] - vzero[t]) * vscale[t]
+ * and out = 0 when lens[b] = 0.  q_fp16: [B, Hq, 128] fp16; out_fp16:
+ * [B, Hq, 128] fp16.  Scores accumulate exact products in fp32; the
+ * softmax runs in fp32 base 2 over chunks of 256 tokens; the value sum takes
+ * fp16(p_t * vscale[t] * 2^E) (2^E a per-chunk power of two) against the
+ * exact (code - zero).  The error bound that follows is stated with the
+ * tests.  ws: kv4_attention_workspace_bytes(B, Hq, S) bytes of device memory
+ * (chunk partial sums; scratch, no initial content) or NULL when that is 0;
+ * a smaller size is W4A8_E_WORKSPACE.  Calls sharing ws must be ordered. */
+size_t kv4_attention_workspace_bytes(int64_t B, int64_t Hq, int64_t S);
+
+w4a8_status attention_kv4_decode(const uint16_t *q_fp16, int64_t B, int64_t Hq, int64_t Hkv,
+                                 const void *k_cache, const void *v_cache, int64_t S,
+                                 const int32_t *lens, float sm_scale, uint16_t *out_fp16,
+                                 void *ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

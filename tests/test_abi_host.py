@@ -189,6 +189,41 @@ def test_w4a16_validation(lib):
 
 
 @needs_no_gpu
+def test_kv4_validation(lib):
+    assert lib.kv4_cache_bytes(2, 4, 64) == 2 * 4 * 64 * 68
+    assert lib.kv4_cache_bytes(2, 4, 48) == 0 and lib.kv4_cache_bytes(0, 4, 64) == 0
+    assert lib.kv4_attention_workspace_bytes(2, 8, 256) == 0            # one chunk: no partial sums
+    assert lib.kv4_attention_workspace_bytes(2, 8, 512) == 2 * 8 * 2 * 130 * 4
+    assert lib.kv4_attention_workspace_bytes(2, 8, 100) == 0
+
+    def quant(k=A, v=A, Bn=2, H=4, T=1, pos=A, kc=B, vc=B, Sc=64):
+        return lib.quantize_kv4(k, v, Bn, H, T, pos, kc, vc, Sc, S)
+
+    assert quant(T=0) == 0 and quant(T=0, k=NUL) == 0
+    assert quant(Sc=40) == -2 and quant(T=-1) == -2 and quant(H=0) == -2
+    assert quant(k=NUL) == -1 and quant(pos=NUL) == -1 and quant(vc=NUL) == -1
+    assert quant(k=MIS) == -3 and quant(kc=MIS) == -3
+
+    def unpack(c=A, isv=0, Bn=2, H=4, Sc=64, codes=B, sc=B, z=B):
+        return lib.kv4_unpack(c, isv, Bn, H, Sc, codes, sc, z, S)
+
+    assert unpack(isv=2) == -2 and unpack(Sc=33) == -2
+    assert unpack(c=NUL) == -1 and unpack(z=NUL) == -1
+    assert unpack(c=MIS) == -3
+
+    def attn(q=A, Bn=2, Hq=8, H=4, kc=A, vc=A, Sc=512, lens=A, sm=0.088, out=B, ws=B, wsb=1 << 20):
+        return lib.attention_kv4_decode(q, Bn, Hq, H, kc, vc, Sc, lens, sm, out, ws, wsb, S)
+
+    assert attn(Hq=6) == -2                    # Hq not a multiple of Hkv
+    assert attn(Hq=4 * 17) == -2               # more than 16 query heads per kv head
+    assert attn(Sc=500) == -2 and attn(sm=0.0) == -2 and attn(sm=float("nan")) == -2
+    assert attn(q=NUL) == -1 and attn(lens=NUL) == -1 and attn(out=NUL) == -1
+    assert attn(q=MIS) == -3 and attn(kc=MIS) == -3
+    assert attn(ws=NUL, wsb=0) == -4           # two chunks need partial sums
+    assert attn(wsb=100) == -4
+
+
+@needs_no_gpu
 def test_gemm_validation(lib, monkeypatch):
     f = lib.gemm_w4a8
     ok = dict(qx=A, sa=A, w=A, s0=A, M=1, N=16, K=128, y=B, acc=NUL, ws=NUL, wsb=0)

@@ -7,12 +7,18 @@ binding.  The library is loaded on first use, so importing the package (or its
 """
 from ._lib import (  # noqa: F401
     W4A8Error,
+    attention_kv4_decode,
     gemm_w4a8,
     gemm_w4a16,
     gemm_w4a8_workspace_bytes,
+    kv4_attention_workspace_bytes,
+    kv4_cache_alloc,
+    kv4_cache_bytes,
+    kv4_unpack,
     linear,
     norm_quantize_act_i8,
     quantize_act_per_token_i8,
+    quantize_kv4,
     quantize_weights_w4g128,
     status_string,
     version,
@@ -21,8 +27,9 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "W4A8Error", "gemm_w4a8", "gemm_w4a16", "gemm_w4a8_workspace_bytes", "linear", "norm_quantize_act_i8",
-    "quantize_act_per_token_i8",
+    "W4A8Error", "attention_kv4_decode", "gemm_w4a8", "gemm_w4a16", "gemm_w4a8_workspace_bytes",
+    "kv4_attention_workspace_bytes", "kv4_cache_alloc", "kv4_cache_bytes", "kv4_unpack", "linear",
+    "norm_quantize_act_i8", "quantize_act_per_token_i8", "quantize_kv4",
     "quantize_weights_w4g128", "status_string", "version", "w4a8_packed_weight_bytes",
     "w4a8_unpack_weights",
 ]

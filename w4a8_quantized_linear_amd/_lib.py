@@ -25,6 +25,8 @@ EXPORTS = (
     "w4a8_status_string", "w4a8_version", "w4a8_packed_weight_bytes",
     "quantize_weights_w4g128", "w4a8_unpack_weights", "quantize_act_per_token_i8",
     "norm_quantize_act_i8", "gemm_w4a8_workspace_bytes", "gemm_w4a8", "gemm_w4a16",
+    "kv4_cache_bytes", "quantize_kv4", "kv4_unpack", "kv4_attention_workspace_bytes",
+    "attention_kv4_decode",
 )
 
 _lock = threading.Lock()
@@ -68,6 +70,16 @@ def load() -> ctypes.CDLL:
         lib.gemm_w4a8.restype = I32
         lib.gemm_w4a16.argtypes = [P, I64, I64, I64, P, P, I64, P, P]
         lib.gemm_w4a16.restype = I32
+        lib.kv4_cache_bytes.argtypes = [I64, I64, I64]
+        lib.kv4_cache_bytes.restype = SZ
+        lib.quantize_kv4.argtypes = [P, P, I64, I64, I64, P, P, P, I64, P]
+        lib.quantize_kv4.restype = I32
+        lib.kv4_unpack.argtypes = [P, I32, I64, I64, I64, P, P, P, P]
+        lib.kv4_unpack.restype = I32
+        lib.kv4_attention_workspace_bytes.argtypes = [I64, I64, I64]
+        lib.kv4_attention_workspace_bytes.restype = SZ
+        lib.attention_kv4_decode.argtypes = [P, I64, I64, I64, P, P, I64, P, ctypes.c_float, P, P, SZ, P]
+        lib.attention_kv4_decode.restype = I32
         _lib = lib
         return lib
 
@@ -220,6 +232,67 @@ def gemm_w4a16(x, wpacked, s0, N: int, *, y=None, stream=None):
     st = load().gemm_w4a16(_ptr(x), M, K, x.stride(0), _ptr(wpacked), _ptr(s0), N, _ptr(y), _stream(stream))
     _check(st, "gemm_w4a16")
     return y
+
+
+def kv4_cache_bytes(B: int, Hkv: int, S: int) -> int:
+    """Bytes of one 4-bit cache (keys or values) for B sequences, Hkv heads, S tokens (0: invalid)."""
+    return int(load().kv4_cache_bytes(B, Hkv, S))
+
+
+def kv4_cache_alloc(B: int, Hkv: int, S: int, device=None):
+    """A (key, value) pair of uint8 device buffers of kv4_cache_bytes each."""
+    import torch
+    n = kv4_cache_bytes(B, Hkv, S)
+    if n == 0:
+        raise W4A8Error(W4A8_E_SHAPE, "kv4_cache_bytes")
+    return (torch.empty(n, dtype=torch.uint8, device=device), torch.empty(n, dtype=torch.uint8, device=device))
+
+
+def quantize_kv4(k, v, pos, k_cache, v_cache, S: int, *, stream=None):
+    """New tokens k, v: fp16 [B, T, Hkv, 128]; pos: int32 [B] (first cache index per sequence)."""
+    import torch
+    assert k.dtype == torch.float16 and v.dtype == torch.float16 and k.shape == v.shape and k.dim() == 4
+    assert k.is_contiguous() and v.is_contiguous() and pos.dtype == torch.int32
+    B, T, Hkv, D = k.shape
+    assert D == 128
+    st = load().quantize_kv4(_ptr(k), _ptr(v), B, Hkv, T, _ptr(pos), _ptr(k_cache), _ptr(v_cache), S,
+                             _stream(stream))
+    _check(st, "quantize_kv4")
+
+
+def kv4_unpack(cache, is_v: bool, B: int, Hkv: int, S: int, *, stream=None):
+    """-> (codes uint8 [B, Hkv, S, 128], scales fp16-bits int16 [B, Hkv, S], zeros uint8 [B, Hkv, S])."""
+    import torch
+    dev = cache.device
+    codes = torch.empty((B, Hkv, S, 128), dtype=torch.uint8, device=dev)
+    sc = torch.empty((B, Hkv, S), dtype=torch.int16, device=dev)
+    z = torch.empty((B, Hkv, S), dtype=torch.uint8, device=dev)
+    st = load().kv4_unpack(_ptr(cache), int(bool(is_v)), B, Hkv, S, _ptr(codes), _ptr(sc), _ptr(z), _stream(stream))
+    _check(st, "kv4_unpack")
+    return codes, sc, z
+
+
+def kv4_attention_workspace_bytes(B: int, Hq: int, S: int) -> int:
+    return int(load().kv4_attention_workspace_bytes(B, Hq, S))
+
+
+def attention_kv4_decode(q, k_cache, v_cache, S: int, Hkv: int, lens, sm_scale: float, *, out=None,
+                         ws=None, stream=None):
+    """q: fp16 [B, Hq, 128]; lens: int32 [B] -> fp16 [B, Hq, 128]."""
+    import torch
+    assert q.dtype == torch.float16 and q.dim() == 3 and q.is_contiguous() and lens.dtype == torch.int32
+    B, Hq, D = q.shape
+    assert D == 128
+    if out is None:
+        out = torch.empty_like(q)
+    need = kv4_attention_workspace_bytes(B, Hq, S)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = load().attention_kv4_decode(_ptr(q), B, Hq, Hkv, _ptr(k_cache), _ptr(v_cache), S, _ptr(lens),
+                                     float(sm_scale), _ptr(out), _ptr(ws), nbytes, _stream(stream))
+    _check(st, "attention_kv4_decode")
+    return out
 
 
 def linear(x, wq: dict, *, acc_out=None, stream=None):

@@ -80,6 +80,23 @@ def w4a16_bytes(M: int, N: int, K: int) -> int:
     return weight_stream_bytes(N, K) + 2 * M * K + 2 * M * N
 
 
+def kv4_row_bytes(head_dim: int = 128) -> int:
+    """One (token, head) row of the 4-bit cache: head_dim / 2 code bytes + one parameter dword."""
+    return head_dim // 2 + 4
+
+
+def kv4_attention_bytes(lens, Hq: int, Hkv: int, head_dim: int = 128) -> int:
+    """attention_kv4_decode: the keys and values of every live token (codes + parameters) once,
+    the fp16 queries in and the fp16 outputs out (chunk partial sums excluded)."""
+    B = len(lens)
+    return 2 * Hkv * int(sum(int(x) for x in lens)) * kv4_row_bytes(head_dim) + 2 * 2 * B * Hq * head_dim
+
+
+def kv4_quant_bytes(B: int, T: int, Hkv: int, head_dim: int = 128) -> int:
+    """quantize_kv4: fp16 keys and values in, their 4-bit rows out."""
+    return 2 * B * T * Hkv * (2 * head_dim + kv4_row_bytes(head_dim))
+
+
 def act_quant_bytes(M: int, K: int) -> int:
     """quantize_act_per_token_i8: fp16 in (absmax pass + quantize pass read the same row) counted once, int8 + fp32 out."""
     return 2 * M * K + M * K + 4 * M

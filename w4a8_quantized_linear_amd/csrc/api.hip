@@ -34,7 +34,7 @@ const char *w4a8_status_string(w4a8_status st)
     case W4A8_E_NULL: return "a required pointer is NULL";
     case W4A8_E_SHAPE: return "invalid shape (need M >= 0, N > 0, K > 0, K % 128 == 0, N % 16 == 0, ldx >= K, ldx % 8 == 0)";
     case W4A8_E_ALIGN: return "a device pointer is not 16-byte aligned";
-    case W4A8_E_WORKSPACE: return "workspace smaller than gemm_w4a8_workspace_bytes()";
+    case W4A8_E_WORKSPACE: return "workspace missing or smaller than the *_workspace_bytes() size";
     case W4A8_E_HIP: return "HIP launch or runtime error";
     }
     return "unknown status";
@@ -123,6 +123,78 @@ w4a8_status gemm_w4a16(const uint16_t *x_fp16, int64_t M, int64_t K, int64_t ldx
         return W4A8_E_ALIGN;
     return hip_status(launch_gemm_w4a16(x_fp16, M, K, ldx, static_cast<const uint8_t *>(wpacked),
                                         s0_fp16, N, y_fp16, stream));
+}
+
+// KV cache shapes: head_dim 128; S a multiple of 32; B * Hkv and B * Hq
+// within the grid's x range; the 8-token blocks of one call within y.
+static bool kv_shape_ok(int64_t B, int64_t Hkv, int64_t S)
+{
+    return B > 0 && Hkv > 0 && S > 0 && S % 32 == 0 && B * Hkv <= ((int64_t)1 << 31) - 1 &&
+           S <= ((int64_t)1 << 24) && kv4_buffer_bytes(B, Hkv, S) <= ((int64_t)1 << 46);
+}
+
+size_t kv4_cache_bytes(int64_t B, int64_t Hkv, int64_t S)
+{
+    return kv_shape_ok(B, Hkv, S) ? (size_t)kv4_buffer_bytes(B, Hkv, S) : 0;
+}
+
+w4a8_status quantize_kv4(const uint16_t *k_fp16, const uint16_t *v_fp16, int64_t B, int64_t Hkv, int64_t T,
+                         const int32_t *pos, void *k_cache, void *v_cache, int64_t S, hipStream_t stream)
+{
+    if (!kv_shape_ok(B, Hkv, S) || T < 0 || T > ((int64_t)1 << 19))
+        return W4A8_E_SHAPE;
+    if (T == 0)
+        return W4A8_OK;
+    if (!k_fp16 || !v_fp16 || !pos || !k_cache || !v_cache)
+        return W4A8_E_NULL;
+    if (!aligned16(k_fp16) || !aligned16(v_fp16) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        (reinterpret_cast<uintptr_t>(pos) & 3u))
+        return W4A8_E_ALIGN;
+    return hip_status(launch_kv4_quant(k_fp16, v_fp16, B, Hkv, T, pos, static_cast<uint8_t *>(k_cache),
+                                       static_cast<uint8_t *>(v_cache), S, stream));
+}
+
+w4a8_status kv4_unpack(const void *cache, int is_v, int64_t B, int64_t Hkv, int64_t S, uint8_t *codes,
+                       uint16_t *scales_fp16, uint8_t *zeros, hipStream_t stream)
+{
+    if (!kv_shape_ok(B, Hkv, S) || (is_v != 0 && is_v != 1) || B * Hkv * S > ((int64_t)1 << 32))
+        return W4A8_E_SHAPE;
+    if (!cache || !codes || !scales_fp16 || !zeros)
+        return W4A8_E_NULL;
+    if (!aligned16(cache) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(scales_fp16) & 1u))
+        return W4A8_E_ALIGN;
+    return hip_status(launch_kv4_unpack(static_cast<const uint8_t *>(cache), is_v, B, Hkv, S, codes,
+                                        scales_fp16, zeros, stream));
+}
+
+size_t kv4_attention_workspace_bytes(int64_t B, int64_t Hq, int64_t S)
+{
+    if (B <= 0 || Hq <= 0 || S <= 0 || S % 32 != 0 || S > ((int64_t)1 << 24))
+        return 0;
+    const int64_t ns = kv4_splits(S);
+    return ns <= 1 ? 0 : (size_t)(B * Hq * ns * (kKvHeadDim + 2) * 4);
+}
+
+w4a8_status attention_kv4_decode(const uint16_t *q_fp16, int64_t B, int64_t Hq, int64_t Hkv, const void *k_cache,
+                                 const void *v_cache, int64_t S, const int32_t *lens, float sm_scale,
+                                 uint16_t *out_fp16, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (!kv_shape_ok(B, Hkv, S) || Hq <= 0 || Hq % Hkv != 0 || Hq / Hkv > 16 ||
+        B * Hq > ((int64_t)1 << 31) - 1 || kv4_splits(S) > 65535)
+        return W4A8_E_SHAPE;
+    if (!(sm_scale > 0.0f) || sm_scale > 1e30f)
+        return W4A8_E_SHAPE;
+    if (!q_fp16 || !k_cache || !v_cache || !lens || !out_fp16)
+        return W4A8_E_NULL;
+    if (!aligned16(q_fp16) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out_fp16) ||
+        (reinterpret_cast<uintptr_t>(lens) & 3u) || (ws && !aligned16(ws)))
+        return W4A8_E_ALIGN;
+    const size_t need = kv4_attention_workspace_bytes(B, Hq, S);
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+        return W4A8_E_WORKSPACE;
+    return hip_status(launch_kv4_attention(q_fp16, B, Hq, Hkv, static_cast<const uint8_t *>(k_cache),
+                                           static_cast<const uint8_t *>(v_cache), S, lens, sm_scale, out_fp16,
+                                           ws, stream));
 }
 
 size_t gemm_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K)

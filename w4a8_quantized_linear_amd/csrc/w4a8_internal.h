@@ -61,6 +61,25 @@ hipError_t launch_weight_quant(const float *w, int64_t N, int64_t K, uint8_t *st
 hipError_t launch_weight_unpack(const uint8_t *stream_bytes, int64_t N, int64_t K,
                                 uint8_t *q4_canon, uint8_t *s1, uint8_t *z, hipStream_t st);
 
+// 4-bit KV cache (kv4_attention.hip).  One buffer for K and one for V, each
+// [ codes: B*Hkv*S rows x 64 bytes ][ params: B*Hkv*S dwords ], row
+// (b, g, t) = (b * Hkv + g) * S + t, S the capacity in tokens (a multiple of
+// 32).  The code layouts are described in kv4_attention.hip.
+constexpr int kKvHeadDim = 128;
+constexpr int kKvRowBytes = 64;
+constexpr int kKvChunk = 256;          // tokens per attention workgroup
+__host__ __device__ inline int64_t kv4_code_bytes(int64_t B, int64_t Hkv, int64_t S) { return B * Hkv * S * kKvRowBytes; }
+__host__ __device__ inline int64_t kv4_buffer_bytes(int64_t B, int64_t Hkv, int64_t S) { return B * Hkv * S * (kKvRowBytes + 4); }
+__host__ __device__ inline int64_t kv4_splits(int64_t S) { return (S + kKvChunk - 1) / kKvChunk; }
+
+hipError_t launch_kv4_quant(const uint16_t *k, const uint16_t *v, int64_t B, int64_t Hkv, int64_t T,
+                            const int32_t *pos, uint8_t *k_cache, uint8_t *v_cache, int64_t S, hipStream_t st);
+hipError_t launch_kv4_unpack(const uint8_t *cache, int is_v, int64_t B, int64_t Hkv, int64_t S, uint8_t *codes,
+                             uint16_t *s, uint8_t *z, hipStream_t st);
+hipError_t launch_kv4_attention(const uint16_t *q, int64_t B, int64_t Hq, int64_t Hkv, const uint8_t *k_cache,
+                                const uint8_t *v_cache, int64_t S, const int32_t *lens, float sm_scale,
+                                uint16_t *out, void *ws, hipStream_t st);
+
 // GEMM workspace (split-K of decode shapes, stream-K of prefill shapes).  One
 // fixed layout for every call, so that calls of different shapes may share a
 // buffer: kWsCounters arrival counters at the front (the only part that must

@@ -16,6 +16,9 @@ Recipe (one per workload family; every draw is seeded):
 The outlier structure follows the pages' description of LLM activations: a
 small fraction of feature channels, fixed across tokens, tens to hundreds of
 times larger than the rest.
+  * KV cache rows (decode attention over the 4-bit cache): keys and values
+    N(0, 1) fp16, keys with 4 channels per head x10, fixed across tokens;
+    queries N(0, 1); ragged context lengths uniform in [1, S];
   * normalization rows (the fused LayerNorm/RMSNorm producer): gamma =
     fp16(1 + 0.1 N(0, 1)), beta = fp16(0.05 N(0, 1)), stand-ins for trained
     affine parameters (no checkpoint is used).
@@ -100,6 +103,74 @@ def norm_affine(K: int) -> Tuple[np.ndarray, np.ndarray]:
     g = (1 + 0.1 * rng.standard_normal(K)).astype(np.float16)
     b = (0.05 * rng.standard_normal(K)).astype(np.float16)
     return g, b
+
+
+# ---------------------------------------------------------------------------
+# KV cache workloads (decode attention over the 4-bit cache).  The shapes are
+# the lectures' reference 7B at a 4,096-token context (32 query heads of 128):
+# multi-head (32 kv heads) and grouped-query with 8 kv heads.  Keys carry a
+# few large channels, fixed per head across tokens (the QServe talk summary:
+# the key cache has outlier channels, the value cache is closer to normal);
+# values are N(0, 1).
+# ---------------------------------------------------------------------------
+KV_HEAD_DIM = 128
+KV_CONFIGS = {
+    "7b_mha": dict(B=64, Hq=32, Hkv=32, S=4096),
+    "7b_gqa8": dict(B=256, Hq=32, Hkv=8, S=4096),
+}
+KV_OUTLIERS_PER_HEAD = 4
+KV_OUTLIER_SCALE = 10.0
+
+
+def _kv_rng(*ids: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED_ROOT, 5, *ids])))
+
+
+def kv_outlier_channels(seed: int, Hkv: int) -> np.ndarray:
+    """[Hkv, KV_OUTLIERS_PER_HEAD] key channels that are large in every token."""
+    rng = _kv_rng(seed, Hkv, 0)
+    return np.stack([np.sort(rng.choice(KV_HEAD_DIM, KV_OUTLIERS_PER_HEAD, replace=False)) for _ in range(Hkv)])
+
+
+def kv_rows(seed: int, B: int, T: int, Hkv: int, part: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """fp16 new keys and values [B, T, Hkv, 128] (part: an index for filling a cache piecewise)."""
+    rng = _kv_rng(seed, B, T, Hkv, part + 1)
+    k = rng.standard_normal((B, T, Hkv, KV_HEAD_DIM), dtype=np.float32)
+    v = rng.standard_normal((B, T, Hkv, KV_HEAD_DIM), dtype=np.float32)
+    cols = kv_outlier_channels(seed, Hkv)
+    for g in range(Hkv):
+        k[:, :, g, cols[g]] *= np.float32(KV_OUTLIER_SCALE)
+    return k.astype(np.float16), v.astype(np.float16)
+
+
+def kv_rows_torch(seed: int, B: int, T: int, Hkv: int, part: int, device):
+    """The same distribution drawn on the GPU with torch's seeded generator (for filling
+    caches too large to draw on the host); same outlier channels as kv_rows."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed((seed * 1000003 + part * 7919 + B * 131 + T * 17 + Hkv) & 0x7FFFFFFF)
+    k = torch.randn((B, T, Hkv, KV_HEAD_DIM), generator=gen, device=device, dtype=torch.float32)
+    v = torch.randn((B, T, Hkv, KV_HEAD_DIM), generator=gen, device=device, dtype=torch.float32)
+    cols = torch.from_numpy(kv_outlier_channels(seed, Hkv)).to(device)
+    scale = torch.ones((Hkv, KV_HEAD_DIM), device=device)
+    scale.scatter_(1, cols, KV_OUTLIER_SCALE)
+    k *= scale
+    return k.half(), v.half()
+
+
+def kv_query(seed: int, B: int, Hq: int) -> np.ndarray:
+    """fp16 queries [B, Hq, 128], N(0, 1)."""
+    return _kv_rng(seed, B, Hq, 0, 1).standard_normal((B, Hq, KV_HEAD_DIM), dtype=np.float32).astype(np.float16)
+
+
+def kv_lens(seed: int, B: int, S: int) -> np.ndarray:
+    """Ragged context lengths in [1, S] (uniform), the longest and shortest included."""
+    rng = _kv_rng(seed, B, S, 0, 2)
+    lens = rng.integers(1, S + 1, B).astype(np.int32)
+    lens[0] = S
+    if B > 1:
+        lens[-1] = 1
+    return lens
 
 
 def all_cases():
