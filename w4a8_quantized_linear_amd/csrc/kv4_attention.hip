@@ -71,13 +71,45 @@ __device__ __host__ inline int nib(int j) { return (j >> 1) + 4 * (j & 1); }
 
 __device__ inline float half_lo(uint32_t p) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xFFFFu)); }
 
-// (code - zero) for the two values of nibble pair m of dword u; zz holds
-// -(1024 + zero) for each half
-__device__ inline uint32_t deq2(uint32_t u, int m, uint32_t zz)
+// Constants of the INT4 -> FP16 conversion, held in registers so that each
+// masked OR is one v_and_or_b32 (a VOP3 instruction takes no literal on this
+// chip and reads at most one scalar register): masks in SGPRs, biases in VGPRs.
+struct Deq {
+    uint32_t m0, m1;          // 0x000F000F, 0x00F000F0
+    uint32_t b0, b1;          // 0x64006400 (1024 + c), 0x54005400 (64 + c)
+};
+
+__device__ inline Deq deq_consts()
 {
-    const uint32_t biased = ((u >> (4 * m)) & 0x000F000Fu) | 0x64006400u;
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, biased) + __builtin_bit_cast(h2, zz));
+    Deq d;
+    d.m0 = 0x000F000Fu;
+    d.m1 = 0x00F000F0u;
+    d.b0 = 0x64006400u;
+    d.b1 = 0x54005400u;
+    asm volatile("" : "+s"(d.m0), "+s"(d.m1));
+    asm volatile("" : "+v"(d.b0), "+v"(d.b1));
+    return d;
 }
+
+// The four fp16 pairs (code - zero) of one code dword u, in operand order:
+// pair d takes nibbles d and d + 4.  Nibbles at bits 0-3 (and 16-19) under
+// the exponent of 1024 read 1024 + c; nibbles at bits 4-7 under the exponent
+// of 64 read 64 + c (the mantissa step there is 1/16); the upper byte of each
+// half is shifted down once.  z10 = -(1024 + zero), z6 = -(64 + zero) per half.
+__device__ inline v4i deq8(uint32_t u, const Deq &k, uint32_t z10a, uint32_t z6a, uint32_t z10b, uint32_t z6b)
+{
+    const uint32_t u8 = u >> 8;
+    const uint32_t p0 = (u & k.m0) | k.b0, p1 = (u & k.m1) | k.b1;
+    const uint32_t p2 = (u8 & k.m0) | k.b0, p3 = (u8 & k.m1) | k.b1;
+    auto add = [](uint32_t x, uint32_t z) {
+        return (int)__builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, x) + __builtin_bit_cast(h2, z));
+    };
+    return v4i{add(p0, z10a), add(p1, z6a), add(p2, z10b), add(p3, z6b)};
+}
+
+// -(1024 + z) and -(64 + z) as fp16 bits
+__device__ inline uint32_t zneg10(uint32_t z) { return 0xE400u | z; }
+__device__ inline uint32_t zneg6(uint32_t z) { return 0xD400u | (z << 4); }
 
 __device__ inline float wave_max(float v)
 {
@@ -226,7 +258,9 @@ struct AttnArgs {
     const uint8_t *kc, *vc;
     const int32_t *lens;       // [B]
     int64_t B, Hq, Hkv, S;
-    int G, nsplit;
+    int G;
+    int nsplit;                // workspace slots per (sequence, query head)
+    int cps;                   // 256-token chunks per workgroup
     float kscale;              // sm_scale * log2(e)
     uint16_t *out;             // [B][Hq][128] fp16
     float *ws_o;               // [B][Hq][nsplit][128]
@@ -239,170 +273,255 @@ __device__ inline int seq_len(const AttnArgs &a, int64_t b)
     return L < 0 ? 0 : (int)std::min<int64_t>(L, a.S);
 }
 
-__global__ __launch_bounds__(256) void kv4_attn_kernel(AttnArgs a)
+constexpr int kBufFlags = 0x00020000;   // raw buffer resource, dword 3 (gfx9 family)
+
+// a buffer resource over [p, p + bytes): the chunk's rows, addressed with
+// 32-bit offsets from a scalar base (no per-load 64-bit address arithmetic)
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *p, int bytes)
 {
-    __shared__ float sc[16][kSC];
-    __shared__ __attribute__((aligned(16))) _Float16 pp[16][kPC];
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, kBufFlags);
+}
+
+#ifndef KV4_ATTN_WAVES
+#define KV4_ATTN_WAVES 4
+#endif
+constexpr int kAttnWaves = KV4_ATTN_WAVES;  // waves per SIMD the register budget is cut for
+
+// GP: the number of query heads per kv head rounded up to a power of two;
+// the softmax gives each of those rows 256 / GP threads.  A workgroup takes
+// a run of cps chunks of one (sequence, kv head) and carries the softmax
+// across them (running maximum and sum per query head, the output
+// accumulators rescaled when the maximum grows); the runs of one sequence
+// meet in kv4_combine_kernel.
+template <int GP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kAttnWaves, 8))) void kv4_attn_kernel(AttnArgs a)
+{
+    constexpr int P = 256 / GP;             // threads per softmax row
+    constexpr int PW = P > 64 ? P / 64 : 1; // waves per row
+    __shared__ float sc[GP][kSC];
+    __shared__ __attribute__((aligned(16))) _Float16 pp[GP][kPC];
     __shared__ uint32_t vpar[kC];
-    __shared__ __attribute__((aligned(16))) uint32_t zc[kC / 2];
-    __shared__ float red[4];
-    __shared__ float mrow[16], lrow[16];
+    __shared__ __attribute__((aligned(16))) uint32_t zc10[kC / 2], zc6[kC / 2];
+    __shared__ float red[4], redm[4], redl[4];
+    __shared__ float mrow[GP], lrow[GP], arow[GP];
+    __shared__ __attribute__((aligned(16))) uint16_t qs[GP][kD];
 
     const int64_t bg = blockIdx.x;
     const int split = blockIdx.y;
     const int64_t b = bg / a.Hkv, g = bg % a.Hkv;
     const int L = seq_len(a, b);
-    const int c0 = split * kC;
-    if (c0 >= L)
+    const int nch = (L + kC - 1) / kC;
+    const int cb = split * a.cps, ce = std::min(cb + a.cps, nch);
+    if (cb >= ce)
         return;
-    const int n = std::min(kC, L - c0);
-    const int n32 = (n + 31) & ~31;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, kb = l >> 4;
+    const int tid = threadIdx.x, l = tid & 63, lr = l & 15, kb = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = a.G;
-
-    const int64_t row0 = bg * a.S + c0;
     const int64_t codes_total = kv4_code_bytes(a.B, a.Hkv, a.S);
-    const uint8_t *kcodes = a.kc + row0 * kKvRowBytes;
-    const uint32_t *kparg = reinterpret_cast<const uint32_t *>(a.kc + codes_total) + row0;
-    const uint8_t *vcodes = a.vc + row0 * kKvRowBytes;
-    const uint32_t *vparg = reinterpret_cast<const uint32_t *>(a.vc + codes_total) + row0;
 
-    // every load of the chunk up front: V parameters, the query operand, this
-    // wave's K tiles, the V codes of this wave's channel slice.  Loads and
-    // tile loops are unconditional (tiles past the end re-read the chunk's
-    // first tile and are masked), so no load is sunk into a branch and every
-    // wait is a counted vmcnt.
-    const uint32_t vp_reg = vparg[tid < n32 ? tid : 0];
-    const int64_t hq = g * G + lr;
-    // rows of the MFMA past the group's G heads re-read head 0 of the group:
-    // their scores are never read and their P' rows are zero
-    const uint16_t *qrow = a.q + (b * a.Hq + (lr < G ? hq : g * G)) * kD;
-    v4i qa[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-        qa[i] = *reinterpret_cast<const v4i *>(qrow + 32 * i + 8 * kb);
-    const int nk = (n + 15) >> 4;
-    v4i kq[kKT];
-    uint32_t kp[kKT];
-#pragma unroll
-    for (int j = 0; j < kKT; j++) {
-        const int tt = (w + 4 * j) < nk ? w + 4 * j : 0;
-        kq[j] = *reinterpret_cast<const v4i *>(kcodes + (int64_t)(16 * tt + lr) * kKvRowBytes + 16 * kb);
-        kp[j] = kparg[16 * tt + lr];
+    // the group's query rows, 16 bytes per thread, staged in LDS once the
+    // first chunk's loads are in flight; rows past G re-read head 0 of the
+    // group: their results are never stored
+    v4i qv = v4i{0, 0, 0, 0};
+    if (tid < GP * kD / 8) {
+        const int hr = tid / (kD / 8);
+        qv = *reinterpret_cast<const v4i *>(a.q + (b * a.Hq + g * G + (hr < G ? hr : 0)) * kD + 8 * (tid % (kD / 8)));
     }
-    v2i vq[kVT];
-#pragma unroll
-    for (int j = 0; j < kVT; j++) {
-        const int js = 32 * j < n ? j : 0;
-        vq[j] = *reinterpret_cast<const v2i *>(vcodes + (int64_t)(4 * js + kb) * 512 + 4 * (32 * w + 2 * lr));
-    }
-    // scores (log2 units) of this wave's tiles
-#pragma unroll
-    for (int j = 0; j < kKT; j++) {
-        const int t0 = 16 * (w + 4 * j);
-        const uint32_t par = kp[j];
-        const uint32_t zz = (0xE400u | ((par >> 16) & 15u)) * 0x10001u;
-        f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const uint32_t u = (uint32_t)kq[j][i];
-            const v4i bw = {(int)deq2(u, 0, zz), (int)deq2(u, 1, zz), (int)deq2(u, 2, zz), (int)deq2(u, 3, zz)};
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, qa[i]), __builtin_bit_cast(h8, bw),
-                                                         acc, 0, 0, 0);
-        }
-        const float f = half_lo(par) * a.kscale;
-        const bool live = t0 + lr < n;
-#pragma unroll
-        for (int r = 0; r < 4; r++)
-            sc[4 * kb + r][t0 + lr] = live ? acc[r] * f : -INFINITY;
-    }
-    vpar[tid] = vp_reg;
-    __syncthreads();
-
-    // softmax statistics: 16 threads per query-head row
-    const int row = tid >> 4, part = tid & 15;
-    float m = -INFINITY, lsum = 0.0f;
-    if (row < G) {
-        for (int t = part; t < n; t += 16)
-            m = fmaxf(m, sc[row][t]);
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1)
-            m = fmaxf(m, __shfl_xor(m, o));
-        for (int t = part; t < n; t += 16) {
-            const float p = __builtin_amdgcn_exp2f(sc[row][t] - m);
-            sc[row][t] = p;
-            lsum += p;
-        }
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1)
-            lsum += __shfl_xor(lsum, o);
-    }
-    {
-        const float sv = tid < n ? half_lo(vp_reg) : 0.0f;
-        const float mx = wave_max(sv);
-        if (l == 0)
-            red[w] = mx;
-    }
-    if (tid < kC / 2) {
-        uint32_t z0 = 0, z1 = 0;                        // tokens past the end: any finite operand
-        if (tid < n32 / 2) {
-            z0 = (vpar[2 * tid] >> 16) & 15u;
-            z1 = (vpar[2 * tid + 1] >> 16) & 15u;
-        }
-        zc[tid] = (0xE400u | z0) | ((0xE400u | z1) << 16);
-    }
-    __syncthreads();
-
-    // P' = fp16(p s_v 2^E); zero for padding rows and tokens past the end
-    // (the whole chunk: the PV loop runs every tile)
-    const float smax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    int e = 0;
-    (void)frexpf(smax, &e);
-    const float sfac = smax > 0.0f ? ldexpf(1.0f, 14 - e) : 1.0f;
-    for (int t = part; t < kC; t += 16) {
-        float pv = 0.0f;
-        if (row < G && t < n)
-            pv = sc[row][t] * (half_lo(vpar[t]) * sfac);
-        pp[row][t] = (_Float16)pv;
-    }
-    if (part == 0) {
-        mrow[row] = m;
-        lrow[row] = lsum;
-    }
-    __syncthreads();
-
-    // PV: this wave's two 16-channel tiles over the whole chunk
+    const Deq dq = deq_consts();
+    const int qr = lr < GP ? lr : 0;
+    const int row = tid / P, part = tid % P;          // softmax role
+    float m_run = -INFINITY, l_run = 0.0f;            // per row (l: this thread's share)
     f4 o2[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+
+    for (int c = cb; c < ce; c++) {
+        const int c0 = c * kC;
+        const int n = std::min(kC, L - c0);
+        const int n32 = (n + 31) & ~31;
+        const int64_t row0 = bg * a.S + c0;
+        const __amdgpu_buffer_rsrc_t rk = rsrc(a.kc + row0 * kKvRowBytes, n32 * kKvRowBytes);
+        const __amdgpu_buffer_rsrc_t rkp = rsrc(a.kc + codes_total + row0 * 4, n32 * 4);
+        const __amdgpu_buffer_rsrc_t rv = rsrc(a.vc + row0 * kKvRowBytes, n32 * kKvRowBytes);
+        const __amdgpu_buffer_rsrc_t rvp = rsrc(a.vc + codes_total + row0 * 4, n32 * 4);
+
+        // every load of the chunk up front: V parameters, this wave's K tiles,
+        // the V codes of this wave's channel slice.  Loads and tile loops are
+        // unconditional (tiles past the end re-read the chunk's first tile and
+        // are masked), so no load is sunk into a branch and every wait is a
+        // counted vmcnt.
+        const uint32_t vp_reg = __builtin_amdgcn_raw_buffer_load_b32(rvp, 4 * (tid < n32 ? tid : 0), 0, 0);
+        const int nk = (n + 15) >> 4;
+        v4i kq[kKT];
+        uint32_t kp[kKT];
 #pragma unroll
-    for (int j = 0; j < kVT; j++) {
-        const h8 pa = *reinterpret_cast<const h8 *>(&pp[lr][32 * j + 8 * kb]);
-        const v4i zq = *reinterpret_cast<const v4i *>(&zc[16 * j + 4 * kb]);
+        for (int j = 0; j < kKT; j++) {
+            const int tt = (w + 4 * j) < nk ? w + 4 * j : 0;            // wave-uniform
+            kq[j] = __builtin_amdgcn_raw_buffer_load_b128(rk, lr * kKvRowBytes + 16 * kb, 16 * tt * kKvRowBytes, 0);
+            kp[j] = __builtin_amdgcn_raw_buffer_load_b32(rkp, 4 * lr, 64 * tt, 0);
+        }
+        v2i vq[kVT];
 #pragma unroll
-        for (int c2 = 0; c2 < 2; c2++) {
-            const uint32_t u = (uint32_t)vq[j][c2];
-            const v4i bw = {(int)deq2(u, 0, (uint32_t)zq[0]), (int)deq2(u, 1, (uint32_t)zq[1]),
-                            (int)deq2(u, 2, (uint32_t)zq[2]), (int)deq2(u, 3, (uint32_t)zq[3])};
-            o2[c2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(h8, bw), o2[c2], 0, 0, 0);
+        for (int j = 0; j < kVT; j++) {
+            const int js = 32 * j < n ? j : 0;
+            vq[j] = __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(rv, kb * 512 + 4 * (32 * w + 2 * lr),
+                                                                                 js * 2048, 0));
+        }
+        if (c == cb) {
+            if (tid < GP * kD / 8)
+                *reinterpret_cast<v4i *>(&qs[tid / (kD / 8)][8 * (tid % (kD / 8))]) = qv;
+            __syncthreads();
+        }
+
+        // scores (log2 units) of this wave's tiles; rows past GP are not stored
+#pragma unroll
+        for (int j = 0; j < kKT; j++) {
+            const int t0 = 16 * (w + 4 * j);
+            const uint32_t par = kp[j];
+            const uint32_t zk = (par >> 16) & 15u;
+            const uint32_t z10 = zneg10(zk) * 0x10001u, z6 = zneg6(zk) * 0x10001u;
+            f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const v4i bw = deq8((uint32_t)kq[j][i], dq, z10, z6, z10, z6);
+                const v4i qa = *reinterpret_cast<const v4i *>(&qs[qr][32 * i + 8 * kb]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, qa), __builtin_bit_cast(h8, bw),
+                                                             acc, 0, 0, 0);
+            }
+            const float f = half_lo(par) * a.kscale;
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                if (4 * kb + r < GP)
+                    sc[4 * kb + r][t0 + lr] = acc[r] * f;
+        }
+        vpar[tid] = vp_reg;
+        {
+            const float mx = wave_max(tid < n ? half_lo(vp_reg) : 0.0f);
+            if (l == 0)
+                red[w] = mx;
+        }
+        __syncthreads();
+
+        // softmax step: P threads per row, GP tokens per thread (t = part + P i)
+        const float smax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        int e = 0;
+        (void)frexpf(smax, &e);
+        const float sfac = smax > 0.0f ? ldexpf(1.0f, 14 - e) : 1.0f;    // 2^E: max scale * 2^E < 2^14
+        float sv[GP];                                  // this thread's scores, read once
+#pragma unroll
+        for (int i = 0; i < GP; i++)
+            sv[i] = sc[row][part + P * i];
+        float m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < GP; i++)
+            if (part + P * i < n)
+                m = fmaxf(m, sv[i]);
+#pragma unroll
+        for (int o = (P < 64 ? P : 64) / 2; o > 0; o >>= 1)
+            m = fmaxf(m, __shfl_xor(m, o));
+        if constexpr (PW > 1) {
+            if (l == 0)
+                redm[w] = m;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < PW; i++)
+                m = fmaxf(m, redm[row * PW + i]);
+        }
+        const float m_new = fmaxf(m_run, m);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first chunk
+        m_run = m_new;
+        float lsum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < GP; i++) {
+            const int t = part + P * i;
+            float pv = 0.0f;
+            if (t < n) {
+                const float p = __builtin_amdgcn_exp2f(sv[i] - m_new);
+                lsum += p;
+                pv = p * (half_lo(vpar[t]) * sfac);
+            }
+            pp[row][t] = (_Float16)pv;                 // every token of the chunk: the PV loop reads them all
+        }
+        l_run = l_run * alpha + lsum;
+        if (part == 0)
+            arow[row] = alpha;
+        if (tid < kC / 2) {
+            uint32_t z0 = 0, z1 = 0;                    // tokens past the end: any finite operand
+            if (tid < n32 / 2) {
+                z0 = (vpar[2 * tid] >> 16) & 15u;
+                z1 = (vpar[2 * tid + 1] >> 16) & 15u;
+            }
+            zc10[tid] = zneg10(z0) | (zneg10(z1) << 16);
+            zc6[tid] = zneg6(z0) | (zneg6(z1) << 16);
+        }
+        __syncthreads();
+
+        // PV: this wave's two 16-channel tiles over the chunk.  Operand rows of
+        // heads past G (and past GP, which re-read row 0) only feed output rows
+        // that are not stored: row i of the product depends on row i of P'.
+        const int prow = lr < GP ? lr : 0;
+        f4 t2[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int j = 0; j < kVT; j++) {
+            const v4i pa = *reinterpret_cast<const v4i *>(&pp[prow][32 * j + 8 * kb]);
+            const v4i z10 = *reinterpret_cast<const v4i *>(&zc10[16 * j + 4 * kb]);
+            const v4i z6 = *reinterpret_cast<const v4i *>(&zc6[16 * j + 4 * kb]);
+#pragma unroll
+            for (int c2 = 0; c2 < 2; c2++) {
+                // operand pair d holds tokens 2d, 2d + 1 of the lane's 8-token block
+                const v4i bw = deq8((uint32_t)vq[j][c2], dq, (uint32_t)z10[0], (uint32_t)z6[1], (uint32_t)z10[2],
+                                    (uint32_t)z6[3]);
+                t2[c2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, pa),
+                                                                __builtin_bit_cast(h8, bw), t2[c2], 0, 0, 0);
+            }
+        }
+        const float unscale = 1.0f / sfac;             // exact: a power of two
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const float al = arow[4 * kb + r < GP ? 4 * kb + r : 0];
+#pragma unroll
+            for (int c2 = 0; c2 < 2; c2++)
+                o2[c2][r] = o2[c2][r] * al + t2[c2][r] * unscale;
         }
     }
 
-    // lane l holds heads 4 kb + r, channel 16 (2w + c2) + lr
-    const float unscale = 1.0f / sfac;                 // exact: a power of two
-    const bool single = L <= kC;
+    // the rows' sums, then the outputs: final when this run covers the whole
+    // sequence, else a partial (max, sum, unnormalized output) for the combine
+#pragma unroll
+    for (int o = (P < 64 ? P : 64) / 2; o > 0; o >>= 1)
+        l_run += __shfl_xor(l_run, o);
+    if constexpr (PW > 1) {
+        if (l == 0)
+            redl[w] = l_run;
+        __syncthreads();
+        if (part == 0) {
+            float t = 0.0f;
+#pragma unroll
+            for (int i = 0; i < PW; i++)
+                t += redl[row * PW + i];
+            lrow[row] = t;
+            mrow[row] = m_run;
+        }
+    } else {
+        if (part == 0) {
+            lrow[row] = l_run;
+            mrow[row] = m_run;
+        }
+    }
+    __syncthreads();
+    const bool single = cb == 0 && ce == nch;
 #pragma unroll
     for (int r = 0; r < 4; r++) {
         const int hh = 4 * kb + r;
-        if (hh >= G)
+        if (hh >= G || hh >= GP)
             continue;
         const int64_t bh = b * a.Hq + g * G + hh;
+        const float inv_l = single ? __builtin_amdgcn_rcpf(lrow[hh]) : 1.0f;
 #pragma unroll
         for (int c2 = 0; c2 < 2; c2++) {
             const int ch = 16 * (2 * w + c2) + lr;
-            const float v = o2[c2][r] * unscale;
             if (single)
-                a.out[bh * kD + ch] = __builtin_bit_cast(uint16_t, (_Float16)(v / lrow[hh]));
+                a.out[bh * kD + ch] = __builtin_bit_cast(uint16_t, (_Float16)(o2[c2][r] * inv_l));
             else
-                a.ws_o[(bh * a.nsplit + split) * kD + ch] = v;
+                a.ws_o[(bh * a.nsplit + split) * kD + ch] = o2[c2][r];
         }
     }
     if (!single && tid < G) {
@@ -412,10 +531,13 @@ __global__ __launch_bounds__(256) void kv4_attn_kernel(AttnArgs a)
     }
 }
 
-// Sequences longer than one chunk: merge the chunks' (max, sum, partial
-// output); empty sequences get zeros.
+// Sequences split over several workgroups: merge their (max, sum, partial
+// output); empty sequences get zeros.  One wave per (sequence, query head):
+// lane i reads split i's max and sum, the weights 2^(m_i - M) are shared
+// across the wave, and each lane then adds two channels over the splits.
 __global__ __launch_bounds__(64) void kv4_combine_kernel(AttnArgs a)
 {
+    __shared__ float wgt[64];
     const int64_t bh = blockIdx.x;
     const int64_t b = bh / a.Hq;
     const int L = seq_len(a, b);
@@ -425,23 +547,52 @@ __global__ __launch_bounds__(64) void kv4_combine_kernel(AttnArgs a)
         o[l] = 0;
         return;
     }
-    const int ns = (L + kC - 1) / kC;
+    const int nch = (L + kC - 1) / kC;
+    const int ns = (nch + a.cps - 1) / a.cps;
     if (ns == 1)
         return;
     const float *ml = a.ws_ml + bh * a.nsplit * 2;
+    const float *po = a.ws_o + bh * a.nsplit * kD + 2 * l;
     float M = -INFINITY;
-    for (int i = 0; i < ns; i++)
+    for (int i = l; i < ns; i += 64)
         M = fmaxf(M, ml[2 * i]);
+    M = wave_max(M);
     float den = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    for (int i = 0; i < ns; i++) {
-        const float wgt = __builtin_amdgcn_exp2f(ml[2 * i] - M);
-        den += ml[2 * i + 1] * wgt;
-        const float *po = a.ws_o + (bh * a.nsplit + i) * kD;
-        o0 += po[2 * l] * wgt;
-        o1 += po[2 * l + 1] * wgt;
+    for (int i0 = 0; i0 < ns; i0 += 64) {
+        const int i = i0 + l;
+        float wi = 0.0f;
+        if (i < ns) {
+            wi = __builtin_amdgcn_exp2f(ml[2 * i] - M);
+            den += ml[2 * i + 1] * wi;
+        }
+        wgt[l] = wi;
+        __syncthreads();
+        const int cnt = std::min(64, ns - i0);
+        int k = 0;
+        for (; k + 4 <= cnt; k += 4) {
+            float2 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                v[u] = *reinterpret_cast<const float2 *>(po + (int64_t)(i0 + k + u) * kD);
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                o0 += v[u].x * wgt[k + u];
+                o1 += v[u].y * wgt[k + u];
+            }
+        }
+        for (; k < cnt; k++) {
+            const float2 v = *reinterpret_cast<const float2 *>(po + (int64_t)(i0 + k) * kD);
+            o0 += v.x * wgt[k];
+            o1 += v.y * wgt[k];
+        }
+        __syncthreads();
     }
-    const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)(o0 / den));
-    const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)(o1 / den));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        den += __shfl_xor(den, off);
+    const float inv = 1.0f / den;
+    const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)(o0 * inv));
+    const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)(o1 * inv));
     o[l] = lo | (hi << 16);
 }
 
@@ -480,11 +631,19 @@ hipError_t launch_kv4_attention(const uint16_t *q, int64_t B, int64_t Hq, int64_
     a.S = S;
     a.G = (int)(Hq / Hkv);
     a.nsplit = (int)kv4_splits(S);
+    a.cps = kv4_chunks_per_run(B * Hkv, S);
     a.kscale = sm_scale * 1.4426950408889634f;
     a.out = out;
     a.ws_o = static_cast<float *>(ws);
     a.ws_ml = a.ws_o ? a.ws_o + B * Hq * a.nsplit * kD : nullptr;
-    hipLaunchKernelGGL(kv4_attn_kernel, dim3((unsigned)(B * Hkv), (unsigned)a.nsplit), dim3(256), 0, st, a);
+    const dim3 grid((unsigned)(B * Hkv), (unsigned)((a.nsplit + a.cps - 1) / a.cps));
+    switch (a.G <= 1 ? 1 : a.G <= 2 ? 2 : a.G <= 4 ? 4 : a.G <= 8 ? 8 : 16) {
+    case 1: hipLaunchKernelGGL(kv4_attn_kernel<1>, grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL(kv4_attn_kernel<2>, grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(kv4_attn_kernel<4>, grid, dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL(kv4_attn_kernel<8>, grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL(kv4_attn_kernel<16>, grid, dim3(256), 0, st, a); break;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;

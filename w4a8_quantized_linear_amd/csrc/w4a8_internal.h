@@ -27,6 +27,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 namespace w4a8 {
@@ -67,10 +69,26 @@ hipError_t launch_weight_unpack(const uint8_t *stream_bytes, int64_t N, int64_t 
 // 32).  The code layouts are described in kv4_attention.hip.
 constexpr int kKvHeadDim = 128;
 constexpr int kKvRowBytes = 64;
-constexpr int kKvChunk = 256;          // tokens per attention workgroup
+#ifndef KV4_CHUNK
+#define KV4_CHUNK 256
+#endif
+constexpr int kKvChunk = KV4_CHUNK;    // tokens per attention workgroup
 __host__ __device__ inline int64_t kv4_code_bytes(int64_t B, int64_t Hkv, int64_t S) { return B * Hkv * S * kKvRowBytes; }
 __host__ __device__ inline int64_t kv4_buffer_bytes(int64_t B, int64_t Hkv, int64_t S) { return B * Hkv * S * (kKvRowBytes + 4); }
 __host__ __device__ inline int64_t kv4_splits(int64_t S) { return (S + kKvChunk - 1) / kKvChunk; }
+// Chunks per attention workgroup: enough workgroups for the chip (about
+// kKvTargetWgs) with as few split runs per sequence as that allows, at most
+// 16 chunks per run.
+#ifndef KV4_TARGET_WGS
+#define KV4_TARGET_WGS 4096
+#endif
+constexpr int64_t kKvTargetWgs = KV4_TARGET_WGS;
+inline int kv4_chunks_per_run(int64_t pairs, int64_t S)
+{
+    const int64_t nch = kv4_splits(S);
+    int64_t cps = nch * pairs / kKvTargetWgs;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(cps, 16));
+}
 
 hipError_t launch_kv4_quant(const uint16_t *k, const uint16_t *v, int64_t B, int64_t Hkv, int64_t T,
                             const int32_t *pos, uint8_t *k_cache, uint8_t *v_cache, int64_t S, hipStream_t st);
