@@ -171,6 +171,37 @@ w4a8_status gemm_w4a8(const int8_t *qx, const float *s_a, const void *wpacked,
                       size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Plan introspection and the learned plan selector (host only; no GPU work).
+ *
+ * gemm_w4a8_plan: the plan gemm_w4a8 would launch for (M, N, K) on the
+ * current device: desc[0..7] = kind (0 streamed-weight decode kernel, 1
+ * matrix-core kernel), m-tiles (TM for kind 1), n-tiles, split-K (stream-K
+ * ranges for kind 1), waves, pipeline depth, staged activations (0/1),
+ * workspace bytes.
+ *
+ * gemm_w4a8_decode_candidates: the decode-kernel plans that can run (M <=
+ * 64): *count is their number; the first max_plans are written to plans as
+ * rows of six int32 (m-tiles, n-tiles, split-K, waves, depth, staged).
+ * Each row, set in W4A8_DECODE_PLAN as "mt,nt,splitk,waves,depth,staged",
+ * makes gemm_w4a8 run that plan (for tuning sweeps).
+ *
+ * gemm_w4a8_selector_score: the compiled-in model's predicted fraction of the
+ * HBM peak for one such plan row on a device with `cus` compute units, or a
+ * negative value when no model is compiled in or the arguments are invalid.
+ * The model follows the QFactory reading notes (6.2, "ML-based kernel
+ * selector"): a small multilayer perceptron over the matrix shape and the
+ * tiling parameters, trained on measured bandwidth utilization; gemm_w4a8
+ * takes the candidate it scores highest (W4A8_SELECTOR=0 restores the fixed
+ * rules).
+ * ------------------------------------------------------------------------ */
+w4a8_status gemm_w4a8_plan(int64_t M, int64_t N, int64_t K, int64_t *desc);
+
+w4a8_status gemm_w4a8_decode_candidates(int64_t M, int64_t N, int64_t K, int32_t *plans,
+                                        int32_t max_plans, int32_t *count);
+
+float gemm_w4a8_selector_score(int64_t M, int64_t N, int64_t K, const int32_t *plan, int64_t cus);
+
+/* ------------------------------------------------------------------------
  * W4A16 GEMM on the same weights: fp16 activations, no activation
  * quantization; the weights are dequantized to fp16 inside the main loop
  * (QFactory reading notes, 2.1: w = (w_quant - zero) * scale; Lecture 15

@@ -456,3 +456,32 @@ def test_workspace_shared_across_shapes_and_kernels():
                 os.environ.pop(k, None)
             else:
                 os.environ[k] = v
+
+
+@pytest.mark.parametrize("M,K,N", [(5, 1152, 272), (40, 2048, 528)])
+def test_every_decode_candidate_is_exact(M, K, N):
+    """Every plan the learned selector may pick (gemm_w4a8_decode_candidates)
+    runs, and gives the oracle's INT32 accumulators bit for bit."""
+    import torch
+    from w4a8_quantized_linear_amd import (gemm_w4a8, gemm_w4a8_decode_candidates, gemm_w4a8_plan,
+                                           quantize_act_per_token_i8)
+    rng = np.random.default_rng(M * 7 + K)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    wq = gpu_weights(w)
+    qx, sa = quantize_act_per_token_i8(to_dev(x))
+    want = orc.linear(x, orc.quantize_weights(w))["acc"]
+    cands = gemm_w4a8_decode_candidates(M, N, K)
+    assert len(cands) >= 40
+    for c in cands:
+        plan = ",".join(str(v) for v in c)
+        say("decode candidate M=%d K=%d N=%d plan=%s" % (M, K, N, plan))
+
+        def run():
+            got = gemm_w4a8_plan(M, N, K)
+            assert got["kind"] == 0 and tuple(got[f] for f in ("mt", "nt", "splitk", "waves", "depth", "xstage")) == c
+            acc = torch.empty((M, N), dtype=torch.int32, device=dev())
+            gemm_w4a8(qx, sa, wq["wpacked"], wq["s0"], N, acc_out=acc)
+            torch.cuda.synchronize()
+            return to_host(acc)
+        assert np.array_equal(_with_plan(plan, run), want), plan

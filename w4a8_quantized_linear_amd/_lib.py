@@ -26,7 +26,7 @@ EXPORTS = (
     "quantize_weights_w4g128", "w4a8_unpack_weights", "quantize_act_per_token_i8",
     "norm_quantize_act_i8", "gemm_w4a8_workspace_bytes", "gemm_w4a8", "gemm_w4a16",
     "kv4_cache_bytes", "quantize_kv4", "kv4_unpack", "kv4_attention_workspace_bytes",
-    "attention_kv4_decode",
+    "attention_kv4_decode", "gemm_w4a8_plan", "gemm_w4a8_decode_candidates", "gemm_w4a8_selector_score",
 )
 
 _lock = threading.Lock()
@@ -70,6 +70,12 @@ def load() -> ctypes.CDLL:
         lib.gemm_w4a8.restype = I32
         lib.gemm_w4a16.argtypes = [P, I64, I64, I64, P, P, I64, P, P]
         lib.gemm_w4a16.restype = I32
+        lib.gemm_w4a8_plan.argtypes = [I64, I64, I64, P]
+        lib.gemm_w4a8_plan.restype = I32
+        lib.gemm_w4a8_decode_candidates.argtypes = [I64, I64, I64, P, I32, P]
+        lib.gemm_w4a8_decode_candidates.restype = I32
+        lib.gemm_w4a8_selector_score.argtypes = [I64, I64, I64, P, I64]
+        lib.gemm_w4a8_selector_score.restype = ctypes.c_float
         lib.kv4_cache_bytes.argtypes = [I64, I64, I64]
         lib.kv4_cache_bytes.restype = SZ
         lib.quantize_kv4.argtypes = [P, P, I64, I64, I64, P, P, P, I64, P]
@@ -232,6 +238,32 @@ def gemm_w4a16(x, wpacked, s0, N: int, *, y=None, stream=None):
     st = load().gemm_w4a16(_ptr(x), M, K, x.stride(0), _ptr(wpacked), _ptr(s0), N, _ptr(y), _stream(stream))
     _check(st, "gemm_w4a16")
     return y
+
+
+PLAN_FIELDS = ("kind", "mt", "nt", "splitk", "waves", "depth", "xstage", "ws_bytes")
+CANDIDATE_FIELDS = ("mt", "nt", "splitk", "waves", "depth", "xstage")
+
+
+def gemm_w4a8_plan(M: int, N: int, K: int) -> dict:
+    """The plan gemm_w4a8 launches for (M, N, K) (host-side query)."""
+    desc = (ctypes.c_int64 * 8)()
+    _check(load().gemm_w4a8_plan(M, N, K, desc), "gemm_w4a8_plan")
+    return dict(zip(PLAN_FIELDS, list(desc)))
+
+
+def gemm_w4a8_decode_candidates(M: int, N: int, K: int) -> list:
+    """Every decode-kernel plan that can run (M <= 64), as tuples (mt, nt, splitk, waves, depth, xstage)."""
+    n = ctypes.c_int32(0)
+    _check(load().gemm_w4a8_decode_candidates(M, N, K, None, 0, ctypes.byref(n)), "gemm_w4a8_decode_candidates")
+    buf = (ctypes.c_int32 * (6 * max(1, n.value)))()
+    _check(load().gemm_w4a8_decode_candidates(M, N, K, buf, n.value, ctypes.byref(n)), "gemm_w4a8_decode_candidates")
+    return [tuple(buf[6 * i:6 * i + 6]) for i in range(n.value)]
+
+
+def gemm_w4a8_selector_score(M: int, N: int, K: int, plan, cus: int = 256) -> float:
+    """The compiled-in selector's predicted HBM fraction for one plan tuple (< 0: no model)."""
+    arr = (ctypes.c_int32 * 6)(*[int(v) for v in plan])
+    return float(load().gemm_w4a8_selector_score(M, N, K, arr, cus))
 
 
 def kv4_cache_bytes(B: int, Hkv: int, S: int) -> int:

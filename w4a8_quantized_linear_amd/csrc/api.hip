@@ -197,6 +197,58 @@ w4a8_status attention_kv4_decode(const uint16_t *q_fp16, int64_t B, int64_t Hq, 
                                            ws, stream));
 }
 
+w4a8_status gemm_w4a8_plan(int64_t M, int64_t N, int64_t K, int64_t *desc)
+{
+    if (!desc)
+        return W4A8_E_NULL;
+    if (M <= 0 || M > kMaxM || !weight_shape_ok(N, K))
+        return W4A8_E_SHAPE;
+    const GemmPlan p = plan_gemm(M, N, K);
+    const int64_t d[8] = {p.kind, p.mt, p.nt, p.splitk, p.waves, p.depth, p.xstage ? 1 : 0, (int64_t)p.ws_bytes};
+    for (int i = 0; i < 8; i++)
+        desc[i] = d[i];
+    return W4A8_OK;
+}
+
+w4a8_status gemm_w4a8_decode_candidates(int64_t M, int64_t N, int64_t K, int32_t *plans, int32_t max_plans,
+                                        int32_t *count)
+{
+    if (!count || (max_plans > 0 && !plans))
+        return W4A8_E_NULL;
+    if (M <= 0 || M > 64 || max_plans < 0 || !weight_shape_ok(N, K))
+        return W4A8_E_SHAPE;
+    GemmPlan cand[256];
+    const int n = decode_candidates(M, N, K, cand, 256);
+    *count = n;
+    for (int i = 0; i < n && i < max_plans && i < 256; i++) {
+        const int32_t row[6] = {cand[i].mt, cand[i].nt, cand[i].splitk, cand[i].waves, cand[i].depth,
+                                cand[i].xstage ? 1 : 0};
+        for (int j = 0; j < 6; j++)
+            plans[6 * i + j] = row[j];
+    }
+    return W4A8_OK;
+}
+
+float gemm_w4a8_selector_score(int64_t M, int64_t N, int64_t K, const int32_t *plan, int64_t cus)
+{
+    if (!plan || M <= 0 || M > 64 || !weight_shape_ok(N, K) || cus <= 0)
+        return -1.0f;
+    GemmPlan p{};
+    p.mt = plan[0];
+    p.nt = plan[1];
+    p.splitk = plan[2];
+    p.waves = plan[3];
+    p.depth = plan[4];
+    p.xstage = plan[5] != 0;
+    if (p.mt <= 0 || p.nt <= 0 || p.splitk <= 0 || p.waves <= 0 || p.depth <= 0)
+        return -1.0f;
+    p.m_blocks = (M + 16 * p.mt - 1) / (16 * p.mt);
+    p.n_blocks = (N / kTileN + p.nt - 1) / p.nt;
+    float x[kSelFeatures];
+    selector_features(p, M, N, K, cus, x);
+    return selector_predict(x);
+}
+
 size_t gemm_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M <= 0 || M > kMaxM || !weight_shape_ok(N, K))

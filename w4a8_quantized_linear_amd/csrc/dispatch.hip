@@ -6,8 +6,11 @@
 // the plan gemm_w4a8 launches always agree.  W4A8_DECODE_PLAN=
 // "mt,nt,splitk[,waves[,depth[,xstage]]]" overrides the decode choice (for
 // tuning sweeps); an override that names no instantiated variant is ignored.
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
+#include <unordered_map>
 
 #include "w4a8_internal.h"
 
@@ -58,6 +61,64 @@ bool launchable(const GemmPlan &p, int64_t M, int64_t K)
     const size_t lds = decode_lds_bytes(p, M, K);
     return decode_variant_exists(p.mt, p.nt, p.waves, p.depth, p.xstage) && lds > 0 &&
            lds <= 160 * 1024;
+}
+
+// The selector's choice for (M, N, K) on a device with `cus` compute units:
+// the candidate with the highest predicted utilization when that prediction
+// beats the fixed rule's plan by more than kSelMargin (the margin that gave
+// the lowest time over the best measured plan on held-out shapes, both
+// random ones and the 7B / 70B decode shapes), else the rule's plan.
+// Ranking all candidates costs tens of microseconds of host time, so the
+// choice is kept per shape (at most 4096 shapes; the table restarts when
+// full).  Guarded by a mutex: calls may come from several host threads.
+GemmPlan selected_plan(int64_t M, int64_t N, int64_t K, const GemmPlan &fallback)
+{
+    struct Key {
+        int64_t M, N, K, cus;
+        bool operator==(const Key &o) const { return M == o.M && N == o.N && K == o.K && cus == o.cus; }
+    };
+    struct Hash {
+        size_t operator()(const Key &k) const
+        {
+            uint64_t h = 1469598103934665603ull;
+            for (int64_t v : {k.M, k.N, k.K, k.cus})
+                h = (h ^ (uint64_t)v) * 1099511628211ull;
+            return (size_t)h;
+        }
+    };
+    static std::mutex mu;
+    static std::unordered_map<Key, GemmPlan, Hash> table;
+    const int64_t cus = num_cus();
+    const Key key{M, N, K, cus};
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        const auto it = table.find(key);
+        if (it != table.end())
+            return it->second;
+    }
+    GemmPlan cand[256];
+    const int nc = std::min(decode_candidates(M, N, K, cand, 256), 256);
+    GemmPlan top = fallback;
+    float best = -1.0f;
+    for (int i = 0; i < nc; i++) {
+        float x[kSelFeatures];
+        selector_features(cand[i], M, N, K, cus, x);
+        const float u = selector_predict(x);
+        if (u > best) {
+            best = u;
+            top = cand[i];
+        }
+    }
+    // the rule's plan stays unless the model expects more than kSelMargin
+    // better utilization from its top candidate
+    float xf[kSelFeatures];
+    selector_features(fallback, M, N, K, cus, xf);
+    const GemmPlan p = best > selector_predict(xf) * (1.0f + kSelMargin) ? top : fallback;
+    std::lock_guard<std::mutex> lock(mu);
+    if (table.size() >= 4096)
+        table.clear();
+    table[key] = p;
+    return p;
 }
 
 }  // namespace
@@ -115,6 +176,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
         if (launchable(q, M, K) && decode_lds_bytes(q, M, K) <= 64 * 1024)
             p = q;
     }
+    // the learned selector, when a model is compiled in: the candidate with
+    // the highest predicted bandwidth utilization (remembered per shape)
+    if (M <= 64 && selector_enabled())
+        p = selected_plan(M, N, K, p);
 
     // many tokens: the matrix-core kernel with (16 TM) x 256 workgroup tiles.
     // Rules fitted to rocprofv3 sweeps (TM x stream-K on/off, M = 128..4096,

@@ -439,6 +439,42 @@ bool decode_variant_exists(int mt, int nt, int waves, int depth, bool xs)
     return false;
 }
 
+size_t decode_lds_bytes(const GemmPlan &p, int64_t M, int64_t K);
+
+int decode_candidates(int64_t M, int64_t N, int64_t K, GemmPlan *out, int max)
+{
+    const int64_t ntiles = N / kTileN, G = num_groups(K), P = (G + 1) / 2;
+    int n = 0;
+    auto add = [&](int mt, int nt, int wv, int dp, bool xs) {
+        for (int s : {1, 2, 4, 8}) {
+            if (s > P || (xs && (mt != 1 || s != 1)))
+                continue;
+            GemmPlan p{};
+            p.kind = 0;
+            p.mt = mt;
+            p.nt = nt;
+            p.splitk = s;
+            p.waves = wv;
+            p.depth = dp;
+            p.xstage = xs;
+            p.m_blocks = (M + 16 * mt - 1) / (16 * mt);
+            p.n_blocks = (ntiles + nt - 1) / nt;
+            if (s > 1 && p.m_blocks * p.n_blocks > kWsCounters)
+                continue;
+            const size_t lds = decode_lds_bytes(p, M, K);
+            if (lds == 0 || lds > 160 * 1024 || (xs && lds > 64 * 1024))
+                continue;
+            if (n < max)
+                out[n] = p;
+            n++;
+        }
+    };
+#define W4A8_DECODE_ADD(MT_, NT_, WV_, D_, XS_) add(MT_, NT_, WV_, D_, XS_);
+    W4A8_DECODE_VARIANTS(W4A8_DECODE_ADD)
+#undef W4A8_DECODE_ADD
+    return n;
+}
+
 // Dynamic LDS of one decode workgroup (0 if the plan does not fit).
 size_t decode_lds_bytes(const GemmPlan &p, int64_t M, int64_t K)
 {

@@ -125,6 +125,21 @@ struct GemmPlan {
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
 
+// Decode plans that can run (M, N, K): every instantiated decode variant with
+// every split-K count in {1, 2, 4, 8} the K groups allow, whose LDS fits (and,
+// for staged activations, fits in 64 KB without splitting K).  Writes at most
+// max plans, returns how many there are.
+int decode_candidates(int64_t M, int64_t N, int64_t K, GemmPlan *out, int max);
+
+// Learned plan selector (selector.hip): the QFactory reading notes (6.2) rank
+// kernel configurations by a small MLP's predicted memory-bandwidth
+// utilization, from the matrix shape and the tiling parameters.
+constexpr int kSelFeatures = 12;
+constexpr float kSelMargin = 0.05f;
+void selector_features(const GemmPlan &p, int64_t M, int64_t N, int64_t K, int64_t cus, float *x);
+float selector_predict(const float *x);      // predicted fraction of HBM peak; < 0: no model
+bool selector_enabled();
+
 // compute units of the current device (256 when it cannot be queried)
 int64_t num_cus();
 

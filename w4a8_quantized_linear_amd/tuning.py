@@ -1,0 +1,153 @@
+"""Offline profiling of the decode GEMM plans, the training data of the learned
+plan selector (QFactory reading notes, 6.2: the kernel-efficiency model is
+trained on measured runs of randomly drawn configurations).
+
+For each shape (M <= 64 tokens, K, N) every plan that can run
+(gemm_w4a8_decode_candidates) is timed with HIP events, its weight bytes
+coming from HBM (the calls rotate over copies in a 1 GiB buffer), and the
+achieved fraction of the 8 TB/s HBM peak is recorded:
+
+    python -m w4a8_quantized_linear_amd.tuning OUT.csv [--shapes 120] [--seed 0] [--eval]
+
+--eval measures the 7B / 70B decode shapes instead of random ones (the
+held-out set).  --compare re-times, on those shapes and the 7B MLP shape
+(K = 4096, N = 11008), the rule table's plan against the selector's
+(W4A8_SELECTOR=0 versus the compiled-in model), interleaved, 50 calls per
+timing, three rounds, medians.  Needs a GPU; the weights are random bytes (every byte is a
+valid code pair and group parameter), timing does not depend on the values.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import math
+import os
+import sys
+
+import numpy as np
+
+FIELDS = ("set", "M", "N", "K", "mt", "nt", "splitk", "waves", "depth", "xstage", "rules", "us", "util")
+EVAL_SHAPES = [(M, N, K) for M in (1, 8, 16, 32, 64)
+               for (K, N) in ((4096, 12288), (4096, 4096), (4096, 22016), (11008, 4096),
+                              (8192, 10240), (8192, 57344), (28672, 8192))]
+
+
+def random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(round(2 ** rng.uniform(0, 6)))
+        K = 128 * int(round(2 ** rng.uniform(2, math.log2(224))))
+        N = 16 * int(round(2 ** rng.uniform(5, math.log2(3584))))
+        if N * K // 2 <= 512 << 20:
+            out.append((M, N, K))
+    return out
+
+
+def measure(shapes, tag, writer, reps=10):
+    import torch
+
+    from w4a8_quantized_linear_amd import (accounting as A, gemm_w4a8, gemm_w4a8_decode_candidates,
+                                           gemm_w4a8_plan, w4a8_packed_weight_bytes)
+    dev = torch.device("cuda:0")
+    pool = torch.randint(0, 256, (1 << 30,), dtype=torch.uint8, device=dev)
+    for (M, N, K) in shapes:
+        wb = w4a8_packed_weight_bytes(N, K)
+        stride = (wb + 4095) // 4096 * 4096
+        copies = max(1, (1 << 30) // stride)
+        views = [pool[i * stride:i * stride + wb] for i in range(min(copies, 64))]
+        qx = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev)
+        sa = torch.rand(M, device=dev) * 0.01
+        s0 = (torch.rand(N, device=dev) * 1e-3).half()
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        os.environ["W4A8_SELECTOR"] = "0"
+        rules = gemm_w4a8_plan(M, N, K)
+        rules_t = tuple(rules[f] for f in ("mt", "nt", "splitk", "waves", "depth", "xstage"))
+        nbytes = A.gemm_bytes(M, N, K)
+        for c in gemm_w4a8_decode_candidates(M, N, K):
+            os.environ["W4A8_DECODE_PLAN"] = ",".join(str(v) for v in c)
+            got = gemm_w4a8_plan(M, N, K)
+            if tuple(got[f] for f in ("mt", "nt", "splitk", "waves", "depth", "xstage")) != c:
+                continue
+            gemm_w4a8(qx, sa, views[0], s0, N, y=y)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for r in range(reps):
+                gemm_w4a8(qx, sa, views[(r + 1) % len(views)], s0, N, y=y)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            writer.writerow([tag, M, N, K, *c, int(c == rules_t), round(us, 3),
+                             round(nbytes / us * 1e-6 / 8.0, 5)])
+        del os.environ["W4A8_DECODE_PLAN"]
+        print("measured %s M=%d N=%d K=%d" % (tag, M, N, K), flush=True)
+    os.environ.pop("W4A8_SELECTOR", None)
+
+
+COMPARE_FIELDS = ("M", "N", "K", "rules_plan", "selector_plan", "rules_us", "selector_us", "ratio")
+
+
+def compare(shapes, writer, reps=50, rounds=3):
+    import torch
+
+    from w4a8_quantized_linear_amd import gemm_w4a8, gemm_w4a8_plan, w4a8_packed_weight_bytes
+    dev = torch.device("cuda:0")
+    pool = torch.randint(0, 256, (1 << 30,), dtype=torch.uint8, device=dev)
+    fields = ("mt", "nt", "splitk", "waves", "depth", "xstage")
+    for (M, N, K) in shapes:
+        wb = w4a8_packed_weight_bytes(N, K)
+        stride = (wb + 4095) // 4096 * 4096
+        views = [pool[i * stride:i * stride + wb] for i in range(min(max(1, (1 << 30) // stride), 64))]
+        qx = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev)
+        sa = torch.rand(M, device=dev) * 0.01
+        s0 = (torch.rand(N, device=dev) * 1e-3).half()
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        plans, times = {}, {"0": [], "1": []}
+        for _ in range(rounds):
+            for sel in ("0", "1"):
+                os.environ["W4A8_SELECTOR"] = sel
+                plans[sel] = gemm_w4a8_plan(M, N, K)
+                gemm_w4a8(qx, sa, views[0], s0, N, y=y)
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for r in range(reps):
+                    gemm_w4a8(qx, sa, views[(r + 1) % len(views)], s0, N, y=y)
+                e1.record()
+                torch.cuda.synchronize()
+                times[sel].append(e0.elapsed_time(e1) * 1e3 / reps)
+        os.environ.pop("W4A8_SELECTOR", None)
+        desc = lambda p: "%d:%s" % (p["kind"], ",".join(str(p[f]) for f in fields))
+        tr, ts = float(np.median(times["0"])), float(np.median(times["1"]))
+        writer.writerow([M, N, K, desc(plans["0"]), desc(plans["1"]), round(tr, 3), round(ts, 3), round(ts / tr, 4)])
+        print("compared M=%d N=%d K=%d rules %.2f us selector %.2f us" % (M, N, K, tr, ts), flush=True)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("out")
+    ap.add_argument("--shapes", type=int, default=120)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--eval", action="store_true")
+    ap.add_argument("--compare", action="store_true")
+    args = ap.parse_args(argv)
+    if args.compare:
+        shapes = EVAL_SHAPES + [(M, 11008, 4096) for M in (1, 8, 16, 32, 64)]
+        with open(args.out, "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(COMPARE_FIELDS)
+            compare(shapes, w)
+        return 0
+    shapes = EVAL_SHAPES if args.eval else random_shapes(args.shapes, args.seed)
+    with open(args.out, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(FIELDS)
+        measure(shapes, "eval" if args.eval else "train", w)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
