@@ -60,7 +60,7 @@ bool launchable(const GemmPlan &p, int64_t M, int64_t K)
 {
     const size_t lds = decode_lds_bytes(p, M, K);
     return decode_variant_exists(p.mt, p.nt, p.waves, p.depth, p.xstage) && lds > 0 &&
-           lds <= 160 * 1024;
+           lds <= kDecodeLdsMax;
 }
 
 // The selector's choice for (M, N, K) on a device with `cus` compute units:

@@ -238,7 +238,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
         for (int mt = 0; mt < MT; mt++)
             acc[t][mt] = v4i{0, 0, 0, 0};
 
-    const int8_t *xrow = xlds + (XS ? min(c, mrows - 1) : 0) * xstride + 16 * kb;
+    // staged activations: the B-operand row of token 16 mt + c
+    const int8_t *xrow[XS ? MT : 1];
+#pragma unroll
+    for (int mt = 0; mt < (XS ? MT : 1); mt++)
+        xrow[mt] = xlds + (XS ? min(16 * mt + c, mrows - 1) : 0) * xstride + 16 * kb;
 
     auto compute = [&](const Chunk<MT, NT, XS> &ch, int pr) {
 #pragma unroll
@@ -249,8 +253,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
             const int gr = g - gbase;
             v4i xf[MT][2];
             if constexpr (XS) {
-                xf[0][0] = *reinterpret_cast<const v4i *>(xrow + gr * kGroup);
-                xf[0][1] = *reinterpret_cast<const v4i *>(xrow + gr * kGroup + 64);
+#pragma unroll
+                for (int mt = 0; mt < MT; mt++) {
+                    xf[mt][0] = *reinterpret_cast<const v4i *>(xrow[mt] + gr * kGroup);
+                    xf[mt][1] = *reinterpret_cast<const v4i *>(xrow[mt] + gr * kGroup + 64);
+                }
             } else {
 #pragma unroll
                 for (int mt = 0; mt < MT; mt++) {
@@ -412,6 +419,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
 template <int MT, int NT, int WAVES, int DEPTH, bool XS>
 hipError_t launch_decode_t(const GemmPlan &p, const DecodeArgs &a, size_t lds, hipStream_t st)
 {
+    // plans with staged activation rows may use more than the default 64 KB of
+    // dynamic LDS: raise this kernel's limit to what the plan needs (the
+    // largest size asked so far is remembered per kernel)
+    static size_t lds_limit = 64 * 1024;
+    if (lds > lds_limit) {
+        const hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&gemm_decode_kernel<MT, NT, WAVES, DEPTH, XS>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess)
+            return e;
+        lds_limit = lds;
+    }
     dim3 grid((unsigned)p.n_blocks, (unsigned)p.splitk, (unsigned)p.m_blocks);
     hipLaunchKernelGGL((gemm_decode_kernel<MT, NT, WAVES, DEPTH, XS>), grid, dim3(64 * WAVES), lds,
                        st, a);
@@ -428,7 +447,9 @@ hipError_t launch_decode_t(const GemmPlan &p, const DecodeArgs &a, size_t lds, h
     X(2, 1, 4, 2, false) X(2, 2, 4, 2, false) X(2, 4, 4, 2, false) X(2, 1, 8, 2, false)          \
     X(4, 1, 4, 2, false) X(4, 2, 4, 2, false) X(4, 4, 4, 2, false) X(4, 1, 8, 2, false)          \
     X(1, 1, 4, 8, true) X(1, 1, 4, 8, false) X(1, 2, 4, 4, false) X(1, 2, 4, 8, false)           \
-    X(1, 4, 4, 4, false) X(2, 2, 4, 4, false) X(2, 4, 4, 4, false) X(4, 4, 4, 4, false)
+    X(1, 4, 4, 4, false) X(2, 2, 4, 4, false) X(2, 4, 4, 4, false) X(4, 4, 4, 4, false)            \
+    X(2, 1, 4, 2, true) X(2, 2, 4, 2, true) X(2, 4, 4, 2, true) X(2, 2, 8, 2, true)                \
+    X(4, 2, 4, 2, true) X(4, 4, 4, 2, true) X(1, 4, 4, 2, true)
 
 bool decode_variant_exists(int mt, int nt, int waves, int depth, bool xs)
 {
@@ -447,7 +468,7 @@ int decode_candidates(int64_t M, int64_t N, int64_t K, GemmPlan *out, int max)
     int n = 0;
     auto add = [&](int mt, int nt, int wv, int dp, bool xs) {
         for (int s : {1, 2, 4, 8}) {
-            if (s > P || (xs && (mt != 1 || s != 1)))
+            if (s > P)
                 continue;
             GemmPlan p{};
             p.kind = 0;
@@ -462,7 +483,7 @@ int decode_candidates(int64_t M, int64_t N, int64_t K, GemmPlan *out, int max)
             if (s > 1 && p.m_blocks * p.n_blocks > kWsCounters)
                 continue;
             const size_t lds = decode_lds_bytes(p, M, K);
-            if (lds == 0 || lds > 160 * 1024 || (xs && lds > 64 * 1024))
+            if (lds == 0 || lds > kDecodeLdsMax)
                 continue;
             if (n < max)
                 out[n] = p;

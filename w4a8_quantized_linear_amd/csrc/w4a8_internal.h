@@ -126,10 +126,13 @@ struct GemmPlan {
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
 
 // Decode plans that can run (M, N, K): every instantiated decode variant with
-// every split-K count in {1, 2, 4, 8} the K groups allow, whose LDS fits (and,
-// for staged activations, fits in 64 KB without splitting K).  Writes at most
-// max plans, returns how many there are.
+// every split-K count in {1, 2, 4, 8} the K groups allow, whose LDS fits in
+// kDecodeLdsMax.  Writes at most max plans, returns how many there are.
 int decode_candidates(int64_t M, int64_t N, int64_t K, GemmPlan *out, int max);
+// Largest dynamic LDS a decode plan may take.  A workgroup can hold 160 KB,
+// but a launch asking for all of it is refused, and plans that large leave
+// one workgroup per compute unit anyway.
+constexpr size_t kDecodeLdsMax = 128 * 1024;
 
 // Learned plan selector (selector.hip): the QFactory reading notes (6.2) rank
 // kernel configurations by a small MLP's predicted memory-bandwidth

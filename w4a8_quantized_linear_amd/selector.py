@@ -63,7 +63,7 @@ def forward(p, Z):
     return 1.0 / (1.0 + np.exp(-a)), (h1, h2)
 
 
-def train(X, y, seed=0, steps=6000, lr=3e-3, l2=1e-5):
+def train(X, y, seed=0, steps=4000, lr=3e-3, l2=1e-5):
     rng = np.random.default_rng(seed)
     mu, sd = X.mean(axis=0), X.std(axis=0)
     sd[sd < 1e-6] = 1.0
