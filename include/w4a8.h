@@ -177,13 +177,14 @@ w4a8_status gemm_w4a8(const int8_t *qx, const float *s_a, const void *wpacked,
  * current device: desc[0..7] = kind (0 streamed-weight decode kernel, 1
  * matrix-core kernel), m-tiles (TM for kind 1), n-tiles, split-K (stream-K
  * ranges for kind 1), waves, pipeline depth, staged activations (0/1),
- * workspace bytes.
+ * workspace bytes, waves splitting N instead of K (0/1).
  *
  * gemm_w4a8_decode_candidates: the decode-kernel plans that can run (M <=
  * 64): *count is their number; the first max_plans are written to plans as
- * rows of six int32 (m-tiles, n-tiles, split-K, waves, depth, staged).
- * Each row, set in W4A8_DECODE_PLAN as "mt,nt,splitk,waves,depth,staged",
- * makes gemm_w4a8 run that plan (for tuning sweeps).
+ * rows of seven int32 (m-tiles, n-tiles, split-K, waves, depth, staged,
+ * waves splitting N).  Each row, set in W4A8_DECODE_PLAN as
+ * "mt,nt,splitk,waves,depth,staged,wave_n", makes gemm_w4a8 run that plan
+ * (for tuning sweeps).
  *
  * gemm_w4a8_selector_score: the compiled-in model's predicted fraction of the
  * HBM peak for one such plan row on a device with `cus` compute units, or a
@@ -194,7 +195,7 @@ w4a8_status gemm_w4a8(const int8_t *qx, const float *s_a, const void *wpacked,
  * takes the candidate it scores highest (W4A8_SELECTOR=0 restores the fixed
  * rules).
  * ------------------------------------------------------------------------ */
-w4a8_status gemm_w4a8_plan(int64_t M, int64_t N, int64_t K, int64_t *desc);
+w4a8_status gemm_w4a8_plan(int64_t M, int64_t N, int64_t K, int64_t *desc);   /* desc: 9 int64 */
 
 w4a8_status gemm_w4a8_decode_candidates(int64_t M, int64_t N, int64_t K, int32_t *plans,
                                         int32_t max_plans, int32_t *count);

@@ -16,18 +16,19 @@ Python floats (double precision):
 The input vector is the library's documented feature list: log2 M, log2 N,
 log2 K, log2 m-tiles, log2 n-tiles, log2 split-K, log2 waves, log2 depth,
 staged activations (0/1), log2(workgroups / compute units), log2(groups per
-split), filled fraction of the last m-block's rows.
+split), filled fraction of the last m-block's rows, waves splitting N (0/1).
 """
 import math
 
 
-def plan_inputs(M, N, K, mt, nt, splitk, waves, depth, xstage, cus=256):
+def plan_inputs(M, N, K, mt, nt, splitk, waves, depth, xstage, wave_n=0, cus=256):
     groups = K / 128
     m_blocks = -(-M // (16 * mt))
     n_blocks = -(-(N // 16) // nt)
     return [math.log2(M), math.log2(N), math.log2(K), math.log2(mt), math.log2(nt), math.log2(splitk),
             math.log2(waves), math.log2(depth), 1.0 if xstage else 0.0,
-            math.log2(m_blocks * n_blocks * splitk / cus), math.log2(groups / splitk), M / (16 * mt * m_blocks)]
+            math.log2(m_blocks * n_blocks * splitk / cus), math.log2(groups / splitk), M / (16 * mt * m_blocks),
+            1.0 if wave_n else 0.0]
 
 
 def mlp_utilization(model, x):

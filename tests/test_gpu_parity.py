@@ -479,7 +479,8 @@ def test_every_decode_candidate_is_exact(M, K, N):
 
         def run():
             got = gemm_w4a8_plan(M, N, K)
-            assert got["kind"] == 0 and tuple(got[f] for f in ("mt", "nt", "splitk", "waves", "depth", "xstage")) == c
+            assert got["kind"] == 0 and tuple(got[f] for f in ("mt", "nt", "splitk", "waves", "depth", "xstage",
+                                                               "wave_n")) == c
             acc = torch.empty((M, N), dtype=torch.int32, device=dev())
             gemm_w4a8(qx, sa, wq["wpacked"], wq["s0"], N, acc_out=acc)
             torch.cuda.synchronize()

@@ -240,29 +240,29 @@ def gemm_w4a16(x, wpacked, s0, N: int, *, y=None, stream=None):
     return y
 
 
-PLAN_FIELDS = ("kind", "mt", "nt", "splitk", "waves", "depth", "xstage", "ws_bytes")
-CANDIDATE_FIELDS = ("mt", "nt", "splitk", "waves", "depth", "xstage")
+PLAN_FIELDS = ("kind", "mt", "nt", "splitk", "waves", "depth", "xstage", "ws_bytes", "wave_n")
+CANDIDATE_FIELDS = ("mt", "nt", "splitk", "waves", "depth", "xstage", "wave_n")
 
 
 def gemm_w4a8_plan(M: int, N: int, K: int) -> dict:
     """The plan gemm_w4a8 launches for (M, N, K) (host-side query)."""
-    desc = (ctypes.c_int64 * 8)()
+    desc = (ctypes.c_int64 * 9)()
     _check(load().gemm_w4a8_plan(M, N, K, desc), "gemm_w4a8_plan")
     return dict(zip(PLAN_FIELDS, list(desc)))
 
 
 def gemm_w4a8_decode_candidates(M: int, N: int, K: int) -> list:
-    """Every decode-kernel plan that can run (M <= 64), as tuples (mt, nt, splitk, waves, depth, xstage)."""
+    """Every decode-kernel plan that can run (M <= 64), as tuples (mt, nt, splitk, waves, depth, xstage, wave_n)."""
     n = ctypes.c_int32(0)
     _check(load().gemm_w4a8_decode_candidates(M, N, K, None, 0, ctypes.byref(n)), "gemm_w4a8_decode_candidates")
-    buf = (ctypes.c_int32 * (6 * max(1, n.value)))()
+    buf = (ctypes.c_int32 * (7 * max(1, n.value)))()
     _check(load().gemm_w4a8_decode_candidates(M, N, K, buf, n.value, ctypes.byref(n)), "gemm_w4a8_decode_candidates")
-    return [tuple(buf[6 * i:6 * i + 6]) for i in range(n.value)]
+    return [tuple(buf[7 * i:7 * i + 7]) for i in range(n.value)]
 
 
 def gemm_w4a8_selector_score(M: int, N: int, K: int, plan, cus: int = 256) -> float:
     """The compiled-in selector's predicted HBM fraction for one plan tuple (< 0: no model)."""
-    arr = (ctypes.c_int32 * 6)(*[int(v) for v in plan])
+    arr = (ctypes.c_int32 * 7)(*[int(v) for v in (tuple(plan) + (0,))[:7]])
     return float(load().gemm_w4a8_selector_score(M, N, K, arr, cus))
 
 

@@ -204,8 +204,9 @@ w4a8_status gemm_w4a8_plan(int64_t M, int64_t N, int64_t K, int64_t *desc)
     if (M <= 0 || M > kMaxM || !weight_shape_ok(N, K))
         return W4A8_E_SHAPE;
     const GemmPlan p = plan_gemm(M, N, K);
-    const int64_t d[8] = {p.kind, p.mt, p.nt, p.splitk, p.waves, p.depth, p.xstage ? 1 : 0, (int64_t)p.ws_bytes};
-    for (int i = 0; i < 8; i++)
+    const int64_t d[9] = {p.kind, p.mt, p.nt, p.splitk, p.waves, p.depth, p.xstage ? 1 : 0, (int64_t)p.ws_bytes,
+                          p.wave_n ? 1 : 0};
+    for (int i = 0; i < 9; i++)
         desc[i] = d[i];
     return W4A8_OK;
 }
@@ -221,10 +222,10 @@ w4a8_status gemm_w4a8_decode_candidates(int64_t M, int64_t N, int64_t K, int32_t
     const int n = decode_candidates(M, N, K, cand, 256);
     *count = n;
     for (int i = 0; i < n && i < max_plans && i < 256; i++) {
-        const int32_t row[6] = {cand[i].mt, cand[i].nt, cand[i].splitk, cand[i].waves, cand[i].depth,
-                                cand[i].xstage ? 1 : 0};
-        for (int j = 0; j < 6; j++)
-            plans[6 * i + j] = row[j];
+        const int32_t row[7] = {cand[i].mt, cand[i].nt, cand[i].splitk, cand[i].waves, cand[i].depth,
+                                cand[i].xstage ? 1 : 0, cand[i].wave_n ? 1 : 0};
+        for (int j = 0; j < 7; j++)
+            plans[7 * i + j] = row[j];
     }
     return W4A8_OK;
 }
@@ -240,6 +241,7 @@ float gemm_w4a8_selector_score(int64_t M, int64_t N, int64_t K, const int32_t *p
     p.waves = plan[3];
     p.depth = plan[4];
     p.xstage = plan[5] != 0;
+    p.wave_n = plan[6] != 0;
     if (p.mt <= 0 || p.nt <= 0 || p.splitk <= 0 || p.waves <= 0 || p.depth <= 0)
         return -1.0f;
     p.m_blocks = (M + 16 * p.mt - 1) / (16 * p.mt);

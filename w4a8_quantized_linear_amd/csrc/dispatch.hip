@@ -58,6 +58,11 @@ size_t ws_size(const GemmPlan &p)
 
 bool launchable(const GemmPlan &p, int64_t M, int64_t K)
 {
+    if (p.wave_n) {
+        const size_t lds = decode_ns_lds_bytes(p, K);
+        return p.waves == 4 && p.nt % 4 == 0 && decode_ns_variant_exists(p.mt, p.nt / 4, p.depth) && lds > 0 &&
+               lds <= kDecodeLdsMax;
+    }
     const size_t lds = decode_lds_bytes(p, M, K);
     return decode_variant_exists(p.mt, p.nt, p.waves, p.depth, p.xstage) && lds > 0 &&
            lds <= kDecodeLdsMax;
@@ -100,7 +105,10 @@ GemmPlan selected_plan(int64_t M, int64_t N, int64_t K, const GemmPlan &fallback
     const int nc = std::min(decode_candidates(M, N, K, cand, 256), 256);
     GemmPlan top = fallback;
     float best = -1.0f;
+    const bool rank_wave_n = selector_knows_wave_n();
     for (int i = 0; i < nc; i++) {
+        if (cand[i].wave_n && !rank_wave_n)
+            continue;
         float x[kSelFeatures];
         selector_features(cand[i], M, N, K, cus, x);
         const float u = selector_predict(x);
@@ -238,15 +246,16 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     }
 
     if (const char *env = std::getenv("W4A8_DECODE_PLAN")) {
-        int mt = 0, nt = 0, s = 0, wv = 4, dp = 2, xs = 0;
-        int got = std::sscanf(env, "%d,%d,%d,%d,%d,%d", &mt, &nt, &s, &wv, &dp, &xs);
+        int mt = 0, nt = 0, s = 0, wv = 4, dp = 2, xs = 0, wn = 0;
+        int got = std::sscanf(env, "%d,%d,%d,%d,%d,%d,%d", &mt, &nt, &s, &wv, &dp, &xs, &wn);
         GemmPlan q = p;
         q.mt = mt;
         q.nt = nt;
         q.splitk = s;
         q.waves = wv;
         q.depth = dp;
-        q.xstage = xs != 0;
+        q.xstage = xs != 0 || wn != 0;
+        q.wave_n = wn != 0;
         if (got >= 3 && nt > 0 && s >= 1 && s <= P && (mt == 1 || mt == 2 || mt == 4)) {
             q.m_blocks = (M + 16 * mt - 1) / (16 * mt);
             q.n_blocks = (ntiles + nt - 1) / nt;
@@ -274,12 +283,14 @@ hipError_t launch_gemm(const GemmPlan &p, const int8_t *qx, const float *s_a,
     if (std::getenv("W4A8_LOG"))
         std::fprintf(stderr,
                      "w4a8: gemm M=%lld N=%lld K=%lld kind=%d mt=%d nt=%d splitk=%d waves=%d "
-                     "depth=%d xstage=%d grid=%lldx%dx%lld\n",
+                     "depth=%d xstage=%d wave_n=%d grid=%lldx%dx%lld\n",
                      (long long)M, (long long)N, (long long)K, p.kind, p.mt, p.nt, p.splitk,
-                     p.waves, p.depth, (int)p.xstage, (long long)p.n_blocks, p.splitk,
+                     p.waves, p.depth, (int)p.xstage, (int)p.wave_n, (long long)p.n_blocks, p.splitk,
                      (long long)p.m_blocks);
     if (p.kind == 1)
         return launch_gemm_prefill(p, qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, ws, st);
+    if (p.wave_n)
+        return launch_gemm_decode_ns(p, qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, ws, st);
     return launch_gemm_decode(p, qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, ws, st);
 }
 

@@ -493,6 +493,33 @@ int decode_candidates(int64_t M, int64_t N, int64_t K, GemmPlan *out, int max)
 #define W4A8_DECODE_ADD(MT_, NT_, WV_, D_, XS_) add(MT_, NT_, WV_, D_, XS_);
     W4A8_DECODE_VARIANTS(W4A8_DECODE_ADD)
 #undef W4A8_DECODE_ADD
+    // the N-split kernel: four waves, NTW n-tiles each, activations staged
+    for (int mt : {1, 2, 4})
+        for (int ntw : {1, 2, 4})
+            for (int dp : {2})
+                for (int s : {1, 2, 4, 8}) {
+                    if (!decode_ns_variant_exists(mt, ntw, dp) || s > P)
+                        continue;
+                    GemmPlan p{};
+                    p.kind = 0;
+                    p.mt = mt;
+                    p.nt = 4 * ntw;
+                    p.splitk = s;
+                    p.waves = 4;
+                    p.depth = dp;
+                    p.xstage = true;
+                    p.wave_n = true;
+                    p.m_blocks = (M + 16 * mt - 1) / (16 * mt);
+                    p.n_blocks = (ntiles + p.nt - 1) / p.nt;
+                    if (s > 1 && p.m_blocks * p.n_blocks > kWsCounters)
+                        continue;
+                    const size_t lds = decode_ns_lds_bytes(p, K);
+                    if (lds == 0 || lds > kDecodeLdsMax)
+                        continue;
+                    if (n < max)
+                        out[n] = p;
+                    n++;
+                }
     return n;
 }
 

@@ -1,0 +1,432 @@
+// gemm_decode_ns.hip -- decode GEMM whose waves split N, gfx950.
+//
+// Same arithmetic as gemm_decode.hip (QServe talk summary, "Quantized Matrix
+// Multiplication (GEMM) Kernel on GPUs"; the rebuild q4 s1 - z s1 in packed
+// 16-bit lanes, INT8 matrix cores, both scales in the epilogue), with another
+// work split for several token tiles.  There every wave of a workgroup takes a
+// share of the K groups and loads its own activation operands next to its
+// weights, so with 2-4 token tiles half of each wave's registers and of its
+// memory traffic are activations.  Here the four waves of a workgroup split
+// the workgroup's n-tiles (NTW each) and all walk the whole K slice in step:
+//  * the activation rows of the workgroup's tokens are copied into LDS, one
+//    window of two group pairs (512 bytes per row) at a time, by direct-to-
+//    LDS loads shared by the four waves (one 1 KB copy fills two rows),
+//    double-buffered: window j + 1 is in flight while window j is used;
+//  * each wave streams only weight tiles through its register ring (DEPTH
+//    pairs ahead) and keeps only its own accumulators, so no cross-wave
+//    reduction is needed;
+//  * a window row is stored with its 16-byte chunks XOR-swizzled by the row
+//    (chunk k of row r at chunk k ^ (r & 15)), so the 16 token rows a wave
+//    reads at one k land in 16 different bank groups.
+// The decoded group parameters of the slice stay in LDS ([NT][span][16]), so
+// long K slices need split-K to fit; plans are filtered by their LDS size.
+// Split-K across workgroups uses the workspace protocol of gemm_decode.hip:
+// per-split partial tiles stored with agent-coherent stores, an arrival
+// counter per tile, the last arriver sums the slots in split order.
+#include <algorithm>
+
+#include "w4a8_internal.h"
+
+namespace w4a8 {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBufFlags = 0x00020000;   // raw buffer resource, dword 3 (gfx9 family)
+constexpr int kLoadNT = 2;              // non-temporal (streaming) load policy
+constexpr int kWaves = 4;
+constexpr int kWin = 2;                 // group pairs per activation window: 512 bytes per row
+constexpr int kRowBytes = 2 * kWin * kGroup;
+constexpr int kRowChunks = kRowBytes / 16;
+
+__device__ inline uint32_t rebuild4(uint32_t nib, us2 S, us2 C)
+{
+    us2 v = __builtin_bit_cast(us2, nib);
+    v = v * S + C;
+    return __builtin_bit_cast(uint32_t, v) ^ 0x80808080u;
+}
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *p, int64_t bytes)
+{
+    const int64_t lim = bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)lim, kBufFlags);
+}
+
+// A workgroup barrier that waits only for this wave's LDS operations:
+// __syncthreads() would also wait for every outstanding global load, i.e.
+// drain the weight ring at each window.  Callers first wait (counted vmcnt)
+// for their own direct-to-LDS copies that the barrier must publish.
+__device__ inline void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// direct-to-LDS copies of 16 and 4 bytes per lane, buffer form (see the kernel)
+__device__ inline void lds_copy16(const __amdgpu_buffer_rsrc_t &r, void *dst, int voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, 0, 0, 0);
+}
+
+__device__ inline void lds_copy4(const __amdgpu_buffer_rsrc_t &r, void *dst, int voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 4, voff, 0, 0, 0);
+}
+
+__device__ inline uint32_t decode_param(uint32_t p)
+{
+    const uint32_t s1 = (p & 15u) + 1u;
+    const uint32_t c16 = ((128u - (p >> 4) * s1) * 257u) & 0xFFFFu;
+    return s1 | (c16 << 16);
+}
+
+struct NsArgs {
+    const int8_t *qx;
+    const float *s_a;
+    const uint8_t *codes;
+    const uint8_t *params;
+    const uint16_t *s0;
+    int64_t M, N, K;
+    int splitk;
+    uint16_t *y;
+    int32_t *acc_out;
+    int32_t *ws_part;
+    uint32_t *ws_cnt;
+};
+
+// LDS bytes: two windows, the decoded parameters [NT][span][16] and the raw
+// parameter dwords [NT][nq][16] (rounded to whole 256-byte copies)
+__host__ __device__ inline int ns_lds_bytes(int MT, int NT, int span, int nq)
+{
+    return 2 * 16 * MT * kRowBytes + NT * span * 64 + (NT * nq * 64 + 255) / 256 * 256;
+}
+
+template <int MT, int NTW, int DEPTH>
+__global__ __launch_bounds__(64 * kWaves) void gemm_decode_ns_kernel(NsArgs a)
+{
+    constexpr int NT = kWaves * NTW;          // n-tiles of the workgroup
+    constexpr int kRows = 16 * MT;
+    constexpr int kWinBytes = kRows * kRowBytes;
+    static_assert(kWin % DEPTH == 0, "the ring must cycle within a window");
+    extern __shared__ __align__(16) uint8_t smem[];
+
+    const int tid = threadIdx.x;
+    const int l = tid & 63;
+    const int c = l & 15;
+    const int kb = l >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    const int K = (int)a.K;
+    const int G = K / kGroup;
+    const int G4 = (G + 3) / 4 * 4;
+    const int P = (G + 1) / 2;
+    const int ntiles = (int)(a.N / kTileN);
+    const int nt0 = (int)blockIdx.x * NT;
+    const int64_t m0 = (int64_t)blockIdx.z * kRows;
+    const int mrows = (int)min<int64_t>(kRows, a.M - m0);
+
+    const int ps0 = (int)((uint32_t)P * blockIdx.y / (uint32_t)a.splitk);
+    const int ps1 = (int)((uint32_t)P * (blockIdx.y + 1) / (uint32_t)a.splitk);
+    const int npairs = ps1 - ps0;
+    const int gbase = 2 * ps0;
+    const int span = min(2 * npairs, G - gbase);
+    const int q0 = gbase / 4;
+    const int nq = max((gbase + span + 3) / 4 - q0, 1);
+
+    int8_t *win = reinterpret_cast<int8_t *>(smem);
+    uint32_t *ptab = reinterpret_cast<uint32_t *>(smem + 2 * kWinBytes);
+    uint8_t *praw = smem + 2 * kWinBytes + NT * span * 64;
+    const int praw_bytes = (NT * nq * 64 + 255) / 256 * 256;
+
+    const __amdgpu_buffer_rsrc_t rw = rsrc(a.codes, code_bytes(a.N, a.K));
+    const __amdgpu_buffer_rsrc_t rp = rsrc(a.params, param_bytes(a.N, a.K));
+    const __amdgpu_buffer_rsrc_t rx = rsrc(a.qx + m0 * a.K, (int64_t)mrows * a.K);
+    // direct-to-LDS copies use the buffer form: the compiler adds no wait for
+    // them before LDS reads (it cannot tell the two window buffers apart), so
+    // the waits are the counted ones below
+
+    // one window: row r (a token of the block, clamped to the last real one)
+    // takes groups [2 (ps0 + j kWin), +2 kWin) of the slice (clamped to the
+    // last group).  Copy i fills rows 2i and 2i + 1 (lanes 0-31, 32-63); the
+    // lane that writes chunk k of row r loads source chunk k ^ (r & 15).
+    auto window_copy = [&](int j, int buf) {
+#pragma unroll
+        for (int i0 = 0; i0 < kRows / 2; i0 += kWaves) {
+            const int i = i0 + wv;
+            const int r = 2 * i + (l >> 5);
+            const int srow = min(r, mrows - 1);
+            const int chunk = (l & (kRowChunks - 1)) ^ (r & 15);
+            const int g = min(2 * (ps0 + j * kWin) + chunk / 8, G - 1);
+            lds_copy16(rx, win + buf * kWinBytes + 2 * i * kRowBytes, srow * K + g * kGroup + 16 * (chunk & 7));
+        }
+    };
+
+    // ---- 1. staging: parameter bytes, the first window, the weight prologue
+    for (int ch = wv; ch < praw_bytes / 256; ch += kWaves) {
+        const int o = ch * 256 + 4 * l;
+        const int t = o / (nq * 64);
+        const int r = o - t * (nq * 64);
+        const int tt = min(nt0 + min(t, NT - 1), ntiles - 1);
+        lds_copy4(rp, praw + ch * 256, (tt * (G4 / 4) + q0) * 64 + (t < NT ? r : 0));
+    }
+    window_copy(0, 0);
+    __builtin_amdgcn_sched_barrier(0);    // the copies stay ahead of the weight prologue
+
+    int vw[NTW];
+#pragma unroll
+    for (int t = 0; t < NTW; t++)
+        vw[t] = min(nt0 + wv * NTW + t, ntiles - 1) * G * kTileBytes + 16 * l;
+    v4i ring[DEPTH][NTW][2];
+    auto load = [&](v4i (&slot)[NTW][2], int pr) {
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int g = __builtin_amdgcn_readfirstlane(min(2 * pr + j, G - 1));
+#pragma unroll
+            for (int t = 0; t < NTW; t++)
+                slot[t][j] = __builtin_amdgcn_raw_buffer_load_b128(rw, vw[t], g * kTileBytes, kLoadNT);
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < DEPTH; u++)
+        load(ring[u], min(ps0 + u, ps1 - 1));
+
+    // this thread's parameter and window copies were issued before its weight
+    // prologue: they have landed once only the prologue is outstanding
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DEPTH * NTW * 2) : "memory");
+    lds_barrier();
+    for (int e = tid; e < NT * span * 16; e += 64 * kWaves) {
+        const int t = e / (span * 16);
+        const int rem = e - t * span * 16;
+        const int g = rem / 16 + gbase;
+        const int cch = rem - (rem / 16) * 16;
+        const uint32_t dw = reinterpret_cast<const uint32_t *>(praw)[(t * nq + (g / 4 - q0)) * 16 + cch];
+        ptab[e] = decode_param((dw >> (8 * (g & 3))) & 0xFFu);
+    }
+    lds_barrier();
+
+    // ---- 2. main loop: windows of kWin pairs ---------------------------------
+    v4i acc[NTW][MT];
+#pragma unroll
+    for (int t = 0; t < NTW; t++)
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++)
+            acc[t][mt] = v4i{0, 0, 0, 0};
+
+    auto compute = [&](const v4i (&slot)[NTW][2], int pr, const int8_t *wbuf) {
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int g = 2 * pr + j;
+            if (g >= G)
+                break;
+            const int gw = g - 2 * ps0;                           // group within the slice
+            const int gl = gw % (2 * kWin);                       // group within the window
+            v4i xf[MT][2];
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++) {
+                const int8_t *row = wbuf + (16 * mt + c) * kRowBytes;
+                xf[mt][0] = *reinterpret_cast<const v4i *>(row + 16 * ((gl * 8 + kb) ^ c));
+                xf[mt][1] = *reinterpret_cast<const v4i *>(row + 16 * ((gl * 8 + 4 + kb) ^ c));
+            }
+#pragma unroll
+            for (int t = 0; t < NTW; t++) {
+                const uint32_t sc = ptab[((wv * NTW + t) * span + gw) * 16 + c];
+                const us2 S = {(unsigned short)(sc & 0xFFFFu), (unsigned short)(sc & 0xFFFFu)};
+                const us2 C = {(unsigned short)(sc >> 16), (unsigned short)(sc >> 16)};
+                const v4i w = slot[t][j];
+                v4i f0, f1;
+#pragma unroll
+                for (int d = 0; d < 4; d++) {
+                    const uint32_t x = (uint32_t)w[d];
+                    f0[d] = (int)rebuild4(x & 0x0F0F0F0Fu, S, C);
+                    f1[d] = (int)rebuild4((x >> 4) & 0x0F0F0F0Fu, S, C);
+                }
+#pragma unroll
+                for (int mt = 0; mt < MT; mt++) {
+                    acc[t][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f0, xf[mt][0], acc[t][mt], 0, 0, 0);
+                    acc[t][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f1, xf[mt][1], acc[t][mt], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    const int nwin = (npairs + kWin - 1) / kWin;
+    for (int j = 0; j < nwin; j++) {
+        const int buf = j & 1;
+        // the next window goes into the buffer the previous window used; every
+        // wave has left that window (barrier at the end of the last iteration)
+        if (j + 1 < nwin)
+            window_copy(j + 1, buf ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int8_t *wbuf = win + buf * kWinBytes;
+#pragma unroll
+        for (int u = 0; u < kWin; u++) {
+            const int pr = ps0 + j * kWin + u;
+            if (pr < ps1)
+                compute(ring[u % DEPTH], pr, wbuf);
+            load(ring[u % DEPTH], min(pr + DEPTH, ps1 - 1));
+        }
+        // window j + 1 (issued before this window's refills) has landed once
+        // only the last DEPTH pairs of weights are outstanding
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DEPTH * NTW * 2) : "memory");
+        lds_barrier();
+    }
+
+    // ---- 3. outputs: each wave's own tiles ---------------------------------------
+    const int64_t tile_id = (int64_t)blockIdx.z * gridDim.x + blockIdx.x;
+#pragma unroll
+    for (int t = 0; t < NTW; t++) {
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) {
+            const int tt = wv * NTW + t;
+            const int64_t m = m0 + 16 * mt + c;
+            const int64_t n = (int64_t)(nt0 + tt) * kTileN + 4 * kb;
+            if (nt0 + tt >= ntiles || m >= a.M)
+                continue;
+            const v4i sum = acc[t][mt];
+            if (a.splitk > 1) {
+                int32_t *slot = a.ws_part + (tile_id * a.splitk + blockIdx.y) * (256 * MT * NT);
+                const __amdgpu_buffer_rsrc_t rs =
+                    __builtin_amdgcn_make_buffer_rsrc(slot, (short)0, 256 * MT * NT * 4, kBufFlags);
+                __builtin_amdgcn_raw_buffer_store_b128(sum, rs, ((16 * mt + c) * 16 * NT + 16 * tt + 4 * kb) * 4, 0,
+                                                       16);
+            } else {
+                const float sa = a.s_a[m];
+                const uint2 s0p = *reinterpret_cast<const uint2 *>(a.s0 + n);
+                const uint32_t s0w[2] = {s0p.x, s0p.y};
+                uint32_t out[2];
+#pragma unroll
+                for (int r = 0; r < 4; r += 2) {
+                    const float v0 = ((float)sum[r] * sa) *
+                                     (float)__builtin_bit_cast(_Float16, (uint16_t)(s0w[r / 2] & 0xFFFF));
+                    const float v1 = ((float)sum[r + 1] * sa) *
+                                     (float)__builtin_bit_cast(_Float16, (uint16_t)(s0w[r / 2] >> 16));
+                    out[r / 2] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v0) |
+                                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v1) << 16);
+                }
+                *reinterpret_cast<uint2 *>(a.y + m * a.N + n) = make_uint2(out[0], out[1]);
+                if (a.acc_out)
+                    *reinterpret_cast<v4i *>(a.acc_out + m * a.N + n) = sum;
+            }
+        }
+    }
+    if (a.splitk <= 1)
+        return;
+
+    // ---- 4. split-K: the last workgroup of the tile applies the epilogue -------
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    __shared__ uint32_t arrival;
+    if (tid == 0)
+        arrival = __hip_atomic_fetch_add(a.ws_cnt + tile_id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (arrival != (uint32_t)(a.splitk - 1))
+        return;
+    const int ncols = (int)min<int64_t>(NT * kTileN, a.N - (int64_t)nt0 * kTileN);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        a.ws_part + tile_id * a.splitk * (256 * MT * NT), (short)0, a.splitk * 256 * MT * NT * 4, kBufFlags);
+    for (int i = tid; i < mrows * ncols / 4; i += 64 * kWaves) {
+        const int r = i / (ncols / 4);
+        const int q = i - r * (ncols / 4);
+        const int64_t m = m0 + r;
+        const int64_t n = (int64_t)nt0 * kTileN + 4 * q;
+        v4i sum = {0, 0, 0, 0};
+        for (int sp = 0; sp < a.splitk; sp++)
+            sum += __builtin_amdgcn_raw_buffer_load_b128(rs, (r * 16 * NT + 4 * q) * 4, sp * (256 * MT * NT * 4), 16);
+        const float sa = a.s_a[m];
+        const uint2 s0p = *reinterpret_cast<const uint2 *>(a.s0 + n);
+        const uint32_t s0w[2] = {s0p.x, s0p.y};
+        uint32_t out[2];
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+            const float v0 = ((float)sum[e] * sa) * (float)__builtin_bit_cast(_Float16, (uint16_t)(s0w[e / 2] & 0xFFFF));
+            const float v1 = ((float)sum[e + 1] * sa) * (float)__builtin_bit_cast(_Float16, (uint16_t)(s0w[e / 2] >> 16));
+            out[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v0) |
+                         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v1) << 16);
+        }
+        *reinterpret_cast<uint2 *>(a.y + m * a.N + n) = make_uint2(out[0], out[1]);
+        if (a.acc_out)
+            *reinterpret_cast<v4i *>(a.acc_out + m * a.N + n) = sum;
+    }
+    if (tid == 0)
+        __hip_atomic_store(a.ws_cnt + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int MT, int NTW, int DEPTH>
+hipError_t launch_ns_t(const GemmPlan &p, const NsArgs &a, size_t lds, hipStream_t st)
+{
+    static size_t lds_limit = 64 * 1024;
+    if (lds > lds_limit) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_decode_ns_kernel<MT, NTW, DEPTH>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess)
+            return e;
+        lds_limit = lds;
+    }
+    dim3 grid((unsigned)p.n_blocks, (unsigned)p.splitk, (unsigned)p.m_blocks);
+    hipLaunchKernelGGL((gemm_decode_ns_kernel<MT, NTW, DEPTH>), grid, dim3(64 * kWaves), lds, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Instantiated (mt, n-tiles per wave, depth) variants of the N-split kernel.
+#define W4A8_DECODE_NS_VARIANTS(X) X(1, 1, 2) X(1, 2, 2) X(2, 1, 2) X(2, 2, 2) X(2, 4, 2) X(4, 1, 2) X(4, 2, 2)
+
+bool decode_ns_variant_exists(int mt, int ntw, int depth)
+{
+#define W4A8_NS_HAS(MT_, NTW_, D_) \
+    if (mt == MT_ && ntw == NTW_ && depth == D_) return true;
+    W4A8_DECODE_NS_VARIANTS(W4A8_NS_HAS)
+#undef W4A8_NS_HAS
+    return false;
+}
+
+size_t decode_ns_lds_bytes(const GemmPlan &p, int64_t K)
+{
+    const int64_t G = num_groups(K);
+    const int64_t P = (G + 1) / 2;
+    int64_t span = 0, nq = 0;
+    for (int s = 0; s < p.splitk; s++) {
+        const int64_t ps0 = P * s / p.splitk, ps1 = P * (s + 1) / p.splitk;
+        const int64_t sp = std::min<int64_t>(2 * (ps1 - ps0), G - 2 * ps0);
+        span = std::max(span, sp);
+        nq = std::max<int64_t>(nq, std::max<int64_t>((2 * ps0 + sp + 3) / 4 - (2 * ps0) / 4, 1));
+    }
+    return (size_t)ns_lds_bytes(p.mt, p.nt, (int)span, (int)nq);
+}
+
+hipError_t launch_gemm_decode_ns(const GemmPlan &p, const int8_t *qx, const float *s_a, const uint8_t *stream_bytes,
+                                 const uint16_t *s0, int64_t M, int64_t N, int64_t K, uint16_t *y, int32_t *acc_out,
+                                 void *ws, hipStream_t st)
+{
+    NsArgs a;
+    a.qx = qx;
+    a.s_a = s_a;
+    a.codes = stream_bytes;
+    a.params = stream_bytes + code_bytes(N, K);
+    a.s0 = s0;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.splitk = p.splitk;
+    a.y = y;
+    a.acc_out = acc_out;
+    a.ws_part = nullptr;
+    a.ws_cnt = nullptr;
+    if (p.splitk > 1) {
+        a.ws_cnt = reinterpret_cast<uint32_t *>(ws);
+        a.ws_part = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(ws) + kWsPartOffset);
+    }
+    const size_t lds = decode_ns_lds_bytes(p, K);
+    if (p.nt % kWaves != 0 || lds == 0 || lds > kDecodeLdsMax)
+        return hipErrorInvalidValue;
+    const int ntw = p.nt / kWaves;
+#define W4A8_NS_CASE(MT_, NTW_, D_)                                 \
+    if (p.mt == MT_ && ntw == NTW_ && p.depth == D_ && p.waves == kWaves) \
+        return launch_ns_t<MT_, NTW_, D_>(p, a, lds, st);
+    W4A8_DECODE_NS_VARIANTS(W4A8_NS_CASE)
+#undef W4A8_NS_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace w4a8

@@ -17,8 +17,9 @@
 //   log2 M, log2 N, log2 K, log2 m-tiles, log2 n-tiles, log2 split-K,
 //   log2 waves, log2 depth, staged activations (0/1),
 //   log2(workgroups / compute units), log2(groups per split),
-//   filled fraction of the last m-block's rows (M / (16 m-tiles m-blocks)).
-// Network: 12 -> 32 (tanh) -> 32 (tanh) -> 1 (logistic), fp32.
+//   filled fraction of the last m-block's rows (M / (16 m-tiles m-blocks)),
+//   waves splitting N instead of K (0/1).
+// Network: 13 -> 32 (tanh) -> 32 (tanh) -> 1 (logistic), fp32.
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -35,7 +36,7 @@ struct Model {
     float w1[kH][kSelFeatures], b1[kH];
     float w2[kH][kH], b2[kH];
     float w3[kH], b3;
-    int trained;
+    int trained;    // 0: no model; 1: trained without N-split plans; 2: with them
 };
 
 #if __has_include("selector_weights.inc")
@@ -62,6 +63,7 @@ void selector_features(const GemmPlan &p, int64_t M, int64_t N, int64_t K, int64
     x[9] = (float)std::log2(wgs / (double)cus);
     x[10] = (float)std::log2(G / (double)p.splitk);
     x[11] = (float)((double)M / (16.0 * (double)p.mt * (double)p.m_blocks));
+    x[12] = p.wave_n ? 1.0f : 0.0f;
 }
 
 float selector_predict(const float *x)
@@ -89,6 +91,9 @@ float selector_predict(const float *x)
         a += m.w3[i] * h2[i];
     return 1.0f / (1.0f + std::exp(-a));
 }
+
+// Whether the model has seen N-split plans (else they are not ranked).
+bool selector_knows_wave_n() { return kModel.trained >= 2; }
 
 // On when a model is compiled in, unless W4A8_SELECTOR=0.
 bool selector_enabled()

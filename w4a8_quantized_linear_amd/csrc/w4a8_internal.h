@@ -118,6 +118,7 @@ struct GemmPlan {
     int waves;       // waves per workgroup, splitting the slice (decode)
     int depth;       // pairs of groups in flight per wave (decode)
     bool xstage;     // activation rows staged in LDS (decode, few tokens)
+    bool wave_n;     // decode: the waves split the n-tiles (gemm_decode_ns.hip), not K
     int64_t m_blocks;
     int64_t n_blocks;
     size_t ws_bytes; // workspace needed (0 if none)
@@ -129,6 +130,11 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K);
 // every split-K count in {1, 2, 4, 8} the K groups allow, whose LDS fits in
 // kDecodeLdsMax.  Writes at most max plans, returns how many there are.
 int decode_candidates(int64_t M, int64_t N, int64_t K, GemmPlan *out, int max);
+bool decode_ns_variant_exists(int mt, int ntw, int depth);
+size_t decode_ns_lds_bytes(const GemmPlan &p, int64_t K);
+hipError_t launch_gemm_decode_ns(const GemmPlan &p, const int8_t *qx, const float *s_a, const uint8_t *stream_bytes,
+                                 const uint16_t *s0, int64_t M, int64_t N, int64_t K, uint16_t *y, int32_t *acc_out,
+                                 void *ws, hipStream_t st);
 // Largest dynamic LDS a decode plan may take.  A workgroup can hold 160 KB,
 // but a launch asking for all of it is refused, and plans that large leave
 // one workgroup per compute unit anyway.
@@ -137,11 +143,12 @@ constexpr size_t kDecodeLdsMax = 128 * 1024;
 // Learned plan selector (selector.hip): the QFactory reading notes (6.2) rank
 // kernel configurations by a small MLP's predicted memory-bandwidth
 // utilization, from the matrix shape and the tiling parameters.
-constexpr int kSelFeatures = 12;
+constexpr int kSelFeatures = 13;
 constexpr float kSelMargin = 0.05f;
 void selector_features(const GemmPlan &p, int64_t M, int64_t N, int64_t K, int64_t cus, float *x);
 float selector_predict(const float *x);      // predicted fraction of HBM peak; < 0: no model
 bool selector_enabled();
+bool selector_knows_wave_n();
 
 // compute units of the current device (256 when it cannot be queried)
 int64_t num_cus();

@@ -13,7 +13,7 @@ configurations.  This module fits that model to the CSV written by
         --eval data/decode_plans_mi355x_eval.csv.gz
 
 The features are the ones selector.hip computes (same order, same formulas);
-the network is 12 -> 32 (tanh) -> 32 (tanh) -> 1 (logistic), trained by
+the network is 13 -> 32 (tanh) -> 32 (tanh) -> 1 (logistic), trained by
 full-batch Adam on the squared error of the utilization, seeded.
 """
 from __future__ import annotations
@@ -30,28 +30,29 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 INC = os.path.join(HERE, "csrc", "selector_weights.inc")
 JSON = os.path.join(HERE, "data", "selector_model.json")
-PLAN = ("mt", "nt", "splitk", "waves", "depth", "xstage")
+PLAN = ("mt", "nt", "splitk", "waves", "depth", "xstage", "wave_n")
 H = 32
 CUS = 256
 
 
-def features(M, N, K, mt, nt, splitk, waves, depth, xstage, cus=CUS):
-    """The selector's 12 inputs for one (shape, plan); arrays broadcast."""
+def features(M, N, K, mt, nt, splitk, waves, depth, xstage, wave_n=0, cus=CUS):
+    """The selector's 13 inputs for one (shape, plan); arrays broadcast."""
     M, N, K = (np.asarray(v, np.float64) for v in (M, N, K))
     mt, nt, splitk, waves, depth, xstage = (np.asarray(v, np.float64) for v in (mt, nt, splitk, waves, depth, xstage))
+    wave_n = np.broadcast_to(np.asarray(wave_n, np.float64), M.shape)
     G = K / 128.0
     mb = np.ceil(M / (16.0 * mt))
     nb = np.ceil((N / 16.0) / nt)
     return np.stack([np.log2(M), np.log2(N), np.log2(K), np.log2(mt), np.log2(nt), np.log2(splitk),
                      np.log2(waves), np.log2(depth), xstage, np.log2(mb * nb * splitk / cus),
-                     np.log2(G / splitk), M / (16.0 * mt * mb)], axis=-1)
+                     np.log2(G / splitk), M / (16.0 * mt * mb), wave_n], axis=-1)
 
 
 def load(path):
     import gzip
     with (gzip.open(path, "rt") if path.endswith(".gz") else open(path)) as f:
         rows = list(csv.DictReader(f))
-    cols = {k: np.array([float(r[k]) for r in rows]) for k in ("M", "N", "K", *PLAN, "us", "util", "rules")}
+    cols = {k: np.array([float(r.get(k) or 0) for r in rows]) for k in ("M", "N", "K", *PLAN, "us", "util", "rules")}
     X = features(cols["M"], cols["N"], cols["K"], *(cols[k] for k in PLAN))
     return rows, cols, X
 
@@ -117,9 +118,9 @@ def pick_report(model, rows, cols, X):
             "model_worst": float(max(rm)), "rules_worst": float(max(rr)) if rr else float("nan")}, picks
 
 
-def export(model, path_inc=INC, path_json=JSON):
+def export(model, path_inc=INC, path_json=JSON, version=2):
     def arr(a):
-        return "{" + ", ".join("%.9gf" % float(x) for x in np.ravel(a)) + "}"
+        return "{" + ", ".join("%.9ef" % float(x) for x in np.ravel(a)) + "}"
 
     def mat(a):
         return "{" + ", ".join(arr(r) for r in a) + "}"
@@ -129,17 +130,18 @@ def export(model, path_inc=INC, path_json=JSON):
            "    %s," % arr(model["mu"]), "    %s," % arr(model["sd"]),
            "    %s," % mat(model["w1"]), "    %s," % arr(model["b1"]),
            "    %s," % mat(model["w2"]), "    %s," % arr(model["b2"]),
-           "    %s," % arr(model["w3"]), "    %.9gf," % float(model["b3"]),
-           "    1,", "};", ""]
+           "    %s," % arr(model["w3"]), "    %.9ef," % float(model["b3"]),
+           "    %d," % version, "};", ""]
     with open(path_inc, "w") as f:
         f.write("\n".join(txt))
     os.makedirs(os.path.dirname(path_json), exist_ok=True)
     with open(path_json, "w") as f:
-        json.dump({k: np.asarray(v, np.float32).tolist() for k, v in model.items()}, f)
+        json.dump({**{k: np.asarray(v, np.float32).tolist() for k, v in model.items()}, "version": version}, f)
 
 
 def load_model(path_json=JSON):
     d = json.load(open(path_json))
+    d.pop("version", None)
     return {k: np.asarray(v, np.float64) for k, v in d.items()}
 
 

@@ -26,7 +26,7 @@ import sys
 
 import numpy as np
 
-FIELDS = ("set", "M", "N", "K", "mt", "nt", "splitk", "waves", "depth", "xstage", "rules", "us", "util")
+FIELDS = ("set", "M", "N", "K", "mt", "nt", "splitk", "waves", "depth", "xstage", "wave_n", "rules", "us", "util")
 EVAL_SHAPES = [(M, N, K) for M in (1, 8, 16, 32, 64)
                for (K, N) in ((4096, 12288), (4096, 4096), (4096, 22016), (11008, 4096),
                               (8192, 10240), (8192, 57344), (28672, 8192))]
@@ -62,12 +62,12 @@ def measure(shapes, tag, writer, reps=10):
         y = torch.empty((M, N), dtype=torch.float16, device=dev)
         os.environ["W4A8_SELECTOR"] = "0"
         rules = gemm_w4a8_plan(M, N, K)
-        rules_t = tuple(rules[f] for f in ("mt", "nt", "splitk", "waves", "depth", "xstage"))
+        rules_t = tuple(rules[f] for f in ("mt", "nt", "splitk", "waves", "depth", "xstage", "wave_n"))
         nbytes = A.gemm_bytes(M, N, K)
         for c in gemm_w4a8_decode_candidates(M, N, K):
             os.environ["W4A8_DECODE_PLAN"] = ",".join(str(v) for v in c)
             got = gemm_w4a8_plan(M, N, K)
-            if tuple(got[f] for f in ("mt", "nt", "splitk", "waves", "depth", "xstage")) != c:
+            if tuple(got[f] for f in ("mt", "nt", "splitk", "waves", "depth", "xstage", "wave_n")) != c:
                 continue
             gemm_w4a8(qx, sa, views[0], s0, N, y=y)
             torch.cuda.synchronize()
@@ -95,7 +95,7 @@ def compare(shapes, writer, reps=50, rounds=3):
     from w4a8_quantized_linear_amd import gemm_w4a8, gemm_w4a8_plan, w4a8_packed_weight_bytes
     dev = torch.device("cuda:0")
     pool = torch.randint(0, 256, (1 << 30,), dtype=torch.uint8, device=dev)
-    fields = ("mt", "nt", "splitk", "waves", "depth", "xstage")
+    fields = ("mt", "nt", "splitk", "waves", "depth", "xstage", "wave_n")
     for (M, N, K) in shapes:
         wb = w4a8_packed_weight_bytes(N, K)
         stride = (wb + 4095) // 4096 * 4096
