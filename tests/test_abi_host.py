@@ -69,9 +69,18 @@ def test_size_queries(lib):
         assert _lib.w4a8_packed_weight_bytes(N, K) == 0
     assert _lib.gemm_w4a8_workspace_bytes(0, 512, 512) == 0
     assert _lib.gemm_w4a8_workspace_bytes(1, 15, 512) == 0
-    # decode plans (M <= 64) run unsplit by default
-    for (M, N, K) in ((1, 4096, 4096), (32, 22016, 4096)):
-        assert _lib.gemm_w4a8_workspace_bytes(M, N, K) == 0
+    # the fixed rules run these decode shapes unsplit; with the learned selector
+    # the size query still agrees with the plan it picks
+    import os
+    from w4a8_quantized_linear_amd import gemm_w4a8_plan
+    os.environ["W4A8_SELECTOR"] = "0"
+    try:
+        for (M, N, K) in ((1, 4096, 4096), (32, 22016, 4096)):
+            assert _lib.gemm_w4a8_workspace_bytes(M, N, K) == 0
+    finally:
+        del os.environ["W4A8_SELECTOR"]
+    for (M, N, K) in ((1, 4096, 4096), (32, 22016, 4096), (64, 22016, 4096)):
+        assert _lib.gemm_w4a8_workspace_bytes(M, N, K) == gemm_w4a8_plan(M, N, K)["ws_bytes"]
     if not _gpu_visible():   # the planner assumes 256 CUs when no device is present
         # M=512, K=11008, N=4096: long K and 8 x 16 tiles of 64 x 256 fill half
         # the CUs -> 256 stream-K ranges: the fixed 64 KB of counters, then two

@@ -12,7 +12,7 @@ from oracle import selector_oracle as so
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 MODEL = os.path.join(ROOT, "w4a8_quantized_linear_amd", "data", "selector_model.json")
 FIELDS = ("mt", "nt", "splitk", "waves", "depth", "xstage", "wave_n")
-MARGIN = 0.05
+MARGIN = 0.0
 
 
 def tiny(nf=13, h=32, **kw):

@@ -70,9 +70,9 @@ bool launchable(const GemmPlan &p, int64_t M, int64_t K)
 
 // The selector's choice for (M, N, K) on a device with `cus` compute units:
 // the candidate with the highest predicted utilization when that prediction
-// beats the fixed rule's plan by more than kSelMargin (the margin that gave
-// the lowest time over the best measured plan on held-out shapes, both
-// random ones and the 7B / 70B decode shapes), else the rule's plan.
+// beats the fixed rule's plan by more than kSelMargin, else the rule's plan.
+// The margin is chosen on held-out measurements (random shapes and the 7B /
+// 70B decode shapes); for the current model no margin does best.
 // Ranking all candidates costs tens of microseconds of host time, so the
 // choice is kept per shape (at most 4096 shapes; the table restarts when
 // full).  Guarded by a mutex: calls may come from several host threads.

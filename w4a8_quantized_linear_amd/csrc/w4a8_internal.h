@@ -144,7 +144,7 @@ constexpr size_t kDecodeLdsMax = 128 * 1024;
 // kernel configurations by a small MLP's predicted memory-bandwidth
 // utilization, from the matrix shape and the tiling parameters.
 constexpr int kSelFeatures = 13;
-constexpr float kSelMargin = 0.05f;
+constexpr float kSelMargin = 0.0f;
 void selector_features(const GemmPlan &p, int64_t M, int64_t N, int64_t K, int64_t cus, float *x);
 float selector_predict(const float *x);      // predicted fraction of HBM peak; < 0: no model
 bool selector_enabled();

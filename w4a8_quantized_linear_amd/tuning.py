@@ -3,9 +3,11 @@ plan selector (QFactory reading notes, 6.2: the kernel-efficiency model is
 trained on measured runs of randomly drawn configurations).
 
 For each shape (M <= 64 tokens, K, N) every plan that can run
-(gemm_w4a8_decode_candidates) is timed with HIP events, its weight bytes
-coming from HBM (the calls rotate over copies in a 1 GiB buffer), and the
-achieved fraction of the 8 TB/s HBM peak is recorded:
+(gemm_w4a8_decode_candidates) is timed, its weight bytes coming from HBM (the
+calls rotate over copies in a 1 GiB buffer), and the achieved fraction of the
+8 TB/s HBM peak is recorded.  The calls are captured in a HIP graph and the
+graph is replayed under HIP events, so small kernels are timed without the
+host's per-call launch cost:
 
     python -m w4a8_quantized_linear_amd.tuning OUT.csv [--shapes 120] [--seed 0] [--eval]
 
@@ -13,7 +15,7 @@ achieved fraction of the 8 TB/s HBM peak is recorded:
 held-out set).  --compare re-times, on those shapes and the 7B MLP shape
 (K = 4096, N = 11008), the rule table's plan against the selector's
 (W4A8_SELECTOR=0 versus the compiled-in model), interleaved, 50 calls per
-timing, three rounds, medians.  Needs a GPU; the weights are random bytes (every byte is a
+graph, three rounds, medians.  Needs a GPU; the weights are random bytes (every byte is a
 valid code pair and group parameter), timing does not depend on the values.
 """
 from __future__ import annotations
@@ -44,6 +46,32 @@ def random_shapes(n, seed):
     return out
 
 
+def graph_time(call, reps, replays=3):
+    """Microseconds per call: `reps` calls (call(r)) captured once in a HIP graph,
+    replayed `replays` times under events after one warm replay."""
+    import torch
+    call(0)                                   # eager: plan, workspace, kernel attributes
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for r in range(reps):
+                call(r + 1)
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (replays * reps)
+
+
 def measure(shapes, tag, writer, reps=10):
     import torch
 
@@ -69,16 +97,7 @@ def measure(shapes, tag, writer, reps=10):
             got = gemm_w4a8_plan(M, N, K)
             if tuple(got[f] for f in ("mt", "nt", "splitk", "waves", "depth", "xstage", "wave_n")) != c:
                 continue
-            gemm_w4a8(qx, sa, views[0], s0, N, y=y)
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for r in range(reps):
-                gemm_w4a8(qx, sa, views[(r + 1) % len(views)], s0, N, y=y)
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / reps
+            us = graph_time(lambda r: gemm_w4a8(qx, sa, views[r % len(views)], s0, N, y=y), reps)
             writer.writerow([tag, M, N, K, *c, int(c == rules_t), round(us, 3),
                              round(nbytes / us * 1e-6 / 8.0, 5)])
         del os.environ["W4A8_DECODE_PLAN"]
@@ -109,16 +128,7 @@ def compare(shapes, writer, reps=50, rounds=3):
             for sel in ("0", "1"):
                 os.environ["W4A8_SELECTOR"] = sel
                 plans[sel] = gemm_w4a8_plan(M, N, K)
-                gemm_w4a8(qx, sa, views[0], s0, N, y=y)
-                torch.cuda.synchronize()
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for r in range(reps):
-                    gemm_w4a8(qx, sa, views[(r + 1) % len(views)], s0, N, y=y)
-                e1.record()
-                torch.cuda.synchronize()
-                times[sel].append(e0.elapsed_time(e1) * 1e3 / reps)
+                times[sel].append(graph_time(lambda r: gemm_w4a8(qx, sa, views[r % len(views)], s0, N, y=y), reps))
         os.environ.pop("W4A8_SELECTOR", None)
         desc = lambda p: "%d:%s" % (p["kind"], ",".join(str(p[f]) for f in fields))
         tr, ts = float(np.median(times["0"])), float(np.median(times["1"]))
