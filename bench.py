@@ -65,6 +65,7 @@ def main():
     import torch
 
     from w4a8_quantized_linear_amd import _lib, accounting as A, workloads
+    from w4a8_quantized_linear_amd.tuning import graph_time
     from w4a8_quantized_linear_amd import (gemm_w4a8, gemm_w4a16, norm_quantize_act_i8,
                                            quantize_act_per_token_i8, quantize_weights_w4g128)
     if not os.path.exists(_lib.LIB_PATH):
@@ -131,29 +132,21 @@ def main():
     ops_step = sum(A.gemm_ops(M, N_DIM, K_DIM) for M in MS)
     value = ops_step / (ms_per_step * 1e-3) / 1e12
 
-    # ---- per-M kernel figures: back-to-back calls, events on the stream ----
+    # ---- per-M kernel figures: `reps` calls captured in one HIP graph and
+    # replayed under events, so that small-M figures are the kernels' own time
+    # and not the host's launch rate ----------------------------------------
     per_m = []
     for M in MS:
         rec = {"M": M}
         for kind in ("act_quant", "gemm"):
-            reps = args.reps
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for r in range(reps):
-                if kind == "act_quant":
-                    quantize_act_per_token_i8(xs[M], qx=qxs[M], s_a=sas[M], stream=stream)
-                else:
-                    gemm_w4a8(qxs[M], sas[M], wcopies[r % nrot], s0, N_DIM, y=ys[M], ws=ws,
-                              stream=stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            us = 1e3 * e0.elapsed_time(e1) / reps
             if kind == "act_quant":
+                us = graph_time(lambda r: quantize_act_per_token_i8(xs[M], qx=qxs[M], s_a=sas[M]), args.reps)
                 nbytes = A.act_quant_bytes(M, K_DIM)
                 rec["act_quant_us"] = round(us, 3)
                 rec["act_quant_GBps"] = round(nbytes / us * 1e-3, 1)
             else:
+                us = graph_time(lambda r: gemm_w4a8(qxs[M], sas[M], wcopies[r % nrot], s0, N_DIM, y=ys[M],
+                                                    ws=ws), args.reps)
                 nbytes = A.gemm_bytes(M, N_DIM, K_DIM)
                 ops = A.gemm_ops(M, N_DIM, K_DIM)
                 rec["gemm_us"] = round(us, 3)
@@ -177,15 +170,8 @@ def main():
     bet = torch.from_numpy(workloads.norm_affine(K_DIM)[1]).to(dev)
     nq = []
     for M in MS:
-        reps = args.reps
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for r in range(reps):
-            norm_quantize_act_i8(xs[M], gam, bet, eps=1e-5, qx=qxs[M], s_a=sas[M], stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = 1e3 * e0.elapsed_time(e1) / reps
+        us = graph_time(lambda r: norm_quantize_act_i8(xs[M], gam, bet, eps=1e-5, qx=qxs[M], s_a=sas[M]),
+                        args.reps)
         nbytes = A.norm_quant_bytes(M, K_DIM)
         nq.append({"M": M, "us": round(us, 3), "GBps": round(nbytes / us * 1e-3, 1),
                    "hbm_frac": round(nbytes / us * 1e-3 / (A.MI355X_HBM_BYTES_PER_S / 1e9), 4)})
@@ -202,16 +188,7 @@ def main():
     # ---- W4A16 on the same weights at the decode token counts (not part of the step)
     w16 = []
     for M in [m for m in MS if m <= 32]:
-        gemm_w4a16(xs[M], wcopies[0], s0, N_DIM, y=ys[M], stream=stream)   # (first call loads the kernel)
-        reps = args.reps
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for r in range(reps):
-            gemm_w4a16(xs[M], wcopies[r % nrot], s0, N_DIM, y=ys[M], stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = 1e3 * e0.elapsed_time(e1) / reps
+        us = graph_time(lambda r: gemm_w4a16(xs[M], wcopies[r % nrot], s0, N_DIM, y=ys[M]), args.reps)
         nbytes = A.w4a16_bytes(M, N_DIM, K_DIM)
         w8 = next(r for r in per_m if r["M"] == M)
         w16.append({"M": M, "us": round(us, 3), "GBps": round(nbytes / us * 1e-3, 1),
