@@ -194,7 +194,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     // the 7B and 70B shapes) on MI355X:
     //  * long K (>= 64 groups) with few tiles: stream-K over all CUs, with the
     //    largest-count tile (TM 4, else 8) that still leaves the CUs under
-    //    60% filled by whole tiles;
+    //    60% filled by whole tiles; up to 96 groups TM 4 is kept while its
+    //    tiles fill at most 15/16 of the CUs (its partial sums are half the
+    //    size, which outweighs its slower MFMA rate when each range holds few
+    //    groups; measured 12-19% faster on K = 8192 and 11008 at M = 96..768);
     //  * otherwise one workgroup per tile, TM minimising workgroup rounds x
     //    TM x the relative time per MFMA at that TM (1.0, 1.23, 1.75 for
     //    TM 16, 8, 4: smaller tiles rebuild each weight for fewer tokens).
@@ -213,6 +216,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
             tm = 4;   // 33..64 tokens on the widest N: activations shared through LDS
         else if (M > 64) {
             if (G >= 64 && tiles_of(4) * 10 < cus * 6) {
+                tm = 4;
+                ranges = cus;
+            } else if (G >= 64 && G <= 96 && tiles_of(4) * 16 <= cus * 15) {
                 tm = 4;
                 ranges = cus;
             } else if (G >= 64 && tiles_of(8) * 10 < cus * 6) {
