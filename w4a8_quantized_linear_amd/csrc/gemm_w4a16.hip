@@ -208,13 +208,15 @@ hipError_t launch_nt(const W16Args &a, hipStream_t st)
 // Tiles per workgroup.  Every workgroup reads the activation operands of its
 // 16 tokens from L2 once, so NT tiles share that read: with more than 8
 // distinct tokens it costs as much as the weight tiles and four tiles per
-// workgroup pay off when at least 128 workgroups remain; otherwise two tiles
+// workgroup pay off when the launch still has at least 160 workgroups
+// (measured: with 128, N = 8192 at 9..16 tokens, two tiles are 22-35% faster
+// at every K; with 160 and more, four are 7-26% faster); otherwise two tiles
 // when that still leaves 256 workgroups per 16 tokens (or there are several
 // token blocks), else one.  W4A8_W16_NT=1|2|4 overrides (sweeps).
 static int pick_nt(int64_t M, int64_t N)
 {
     const int64_t tiles = N / kTileN;
-    if (M > 8 && tiles >= 512)
+    if (M > 8 && tiles >= 512 && (tiles / 4) * ((M + 15) / 16) >= 160)
         return 4;
     if (tiles >= 512 || M > 16)
         return 2;
