@@ -35,7 +35,8 @@
  *    (hipGetLastError after the launch).  No C++ exception crosses the ABI.
  *  - Shapes: K > 0 and K % 128 == 0; N > 0 and N % 16 == 0; M >= 0.  M == 0
  *    is a successful no-op.  Inputs must be finite; the results for NaN or
- *    Inf inputs are unspecified.
+ *    Inf inputs are unspecified.  The GEMM entry points also need
+ *    K <= 2^22 (W4A8_E_SHAPE otherwise).
  *  - Results are deterministic: bit-identical from run to run.
  */
 #ifndef W4A8_H
@@ -158,8 +159,10 @@ w4a8_status norm_quantize_act_i8(const uint16_t *x_fp16, int64_t M, int64_t K,
  * by the caller once after allocation; every call leaves its counters zeroed
  * again.  It holds the split-K partial sums of decode shapes and the
  * stream-K counters and partial tiles of prefill shapes.  ws may be NULL:
- * the call then runs without splitting K (same results, slower for shapes
- * whose tiles do not fill the GPU).  A non-NULL ws smaller than required is
+ * the call then runs a plan that does not split K (the default plan unsplit
+ * when its LDS still fits, else the best-scored unsplit plan; same results,
+ * slower for shapes whose tiles do not fill the GPU; gemm_w4a8_plan_detail
+ * with with_workspace = 0 names it).  A non-NULL ws smaller than required is
  * W4A8_E_WORKSPACE.  Calls that share one workspace must be ordered (same
  * stream, or synchronised): concurrent calls on one workspace race.
  * ------------------------------------------------------------------------ */
@@ -179,6 +182,10 @@ w4a8_status gemm_w4a8(const int8_t *qx, const float *s_a, const void *wpacked,
  * ranges for kind 1), waves, pipeline depth, staged activations (0/1),
  * workspace bytes, waves splitting N instead of K (0/1).
  *
+ * gemm_w4a8_plan_detail: the same for a call with a workspace
+ * (with_workspace = 1) or with ws == NULL (with_workspace = 0), plus
+ * desc[9] = the dynamic LDS bytes per workgroup its launch requests.
+ *
  * gemm_w4a8_decode_candidates: the decode-kernel plans that can run (M <=
  * 64): *count is their number; the first max_plans are written to plans as
  * rows of seven int32 (m-tiles, n-tiles, split-K, waves, depth, staged,
@@ -196,6 +203,9 @@ w4a8_status gemm_w4a8(const int8_t *qx, const float *s_a, const void *wpacked,
  * rules).
  * ------------------------------------------------------------------------ */
 w4a8_status gemm_w4a8_plan(int64_t M, int64_t N, int64_t K, int64_t *desc);   /* desc: 9 int64 */
+
+w4a8_status gemm_w4a8_plan_detail(int64_t M, int64_t N, int64_t K, int with_workspace,
+                                  int64_t *desc);   /* desc: 10 int64 */
 
 w4a8_status gemm_w4a8_decode_candidates(int64_t M, int64_t N, int64_t K, int32_t *plans,
                                         int32_t max_plans, int32_t *count);

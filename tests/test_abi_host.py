@@ -247,6 +247,7 @@ def test_gemm_validation(lib, monkeypatch):
     assert call(N=0) == -2
     assert call(N=24) == -2
     assert call(K=192) == -2
+    assert call(K=1 << 23) == -2
     assert call(qx=NUL) == -1
     assert call(sa=NUL) == -1
     assert call(w=NUL) == -1
@@ -268,6 +269,41 @@ def test_gemm_validation(lib, monkeypatch):
     need = _lib.gemm_w4a8_workspace_bytes(4096, 4096, 4096)
     assert need > 64 * 2 * 256 * 256 * 4
     assert call(M=4096, N=4096, K=4096, ws=A, wsb=need - 1) == -4
+
+
+CONFIG_KN = [(512, 512), (4096, 12288), (4096, 4096), (4096, 22016), (11008, 4096), (4096, 11008),
+             (8192, 10240), (8192, 57344), (28672, 8192)]
+
+
+@pytest.mark.parametrize("K,N", CONFIG_KN)
+def test_every_plan_fits_its_lds_with_and_without_workspace(lib, K, N):
+    """For every config shape at 1..64 tokens (and a few prefill token
+    counts), the plan gemm_w4a8 launches with a workspace and the one it
+    launches with ws == NULL both request LDS within the kernel's limit, and
+    the NULL-workspace plan needs no workspace.  (An unsplit N-split plan at
+    K = 28672 once asked for 137 KB, over the 128 KB decode limit.)"""
+    from w4a8_quantized_linear_amd import _lib
+    for M in list(range(1, 65)) + [96, 256, 512, 768, 4096]:
+        for with_ws in (True, False):
+            d = _lib.gemm_w4a8_plan_detail(M, N, K, with_ws)
+            limit = 160 * 1024 if d["kind"] == 1 else 128 * 1024
+            assert 0 < d["lds_bytes"] <= limit, (M, with_ws, d)
+            if not with_ws:
+                assert d["ws_bytes"] == 0 and d["splitk"] in (0, 1), (M, d)
+            else:
+                assert d == dict(_lib.gemm_w4a8_plan(M, N, K), lds_bytes=d["lds_bytes"])
+
+
+def test_gemm_k_limit(lib):
+    from w4a8_quantized_linear_amd import _lib
+    assert _lib.gemm_w4a8_workspace_bytes(1, 16, 1 << 23) == 0
+    desc = (ctypes.c_int64 * 10)()
+    assert lib.gemm_w4a8_plan_detail(1, 16, 1 << 23, 1, desc) == -2
+    assert lib.gemm_w4a8_plan_detail(1, 16, 1 << 22, 2, desc) == -2
+    # the longest K still plans a launchable kernel, with or without workspace
+    for with_ws in (True, False):
+        d = _lib.gemm_w4a8_plan_detail(1, 16, 1 << 22, with_ws)
+        assert 0 < d["lds_bytes"] <= 160 * 1024
 
 
 def test_binding_raises_without_library(monkeypatch, tmp_path):

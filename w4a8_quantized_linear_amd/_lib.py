@@ -26,7 +26,8 @@ EXPORTS = (
     "quantize_weights_w4g128", "w4a8_unpack_weights", "quantize_act_per_token_i8",
     "norm_quantize_act_i8", "gemm_w4a8_workspace_bytes", "gemm_w4a8", "gemm_w4a16",
     "kv4_cache_bytes", "quantize_kv4", "kv4_unpack", "kv4_attention_workspace_bytes",
-    "attention_kv4_decode", "gemm_w4a8_plan", "gemm_w4a8_decode_candidates", "gemm_w4a8_selector_score",
+    "attention_kv4_decode", "gemm_w4a8_plan", "gemm_w4a8_plan_detail", "gemm_w4a8_decode_candidates",
+    "gemm_w4a8_selector_score",
 )
 
 _lock = threading.Lock()
@@ -72,6 +73,8 @@ def load() -> ctypes.CDLL:
         lib.gemm_w4a16.restype = I32
         lib.gemm_w4a8_plan.argtypes = [I64, I64, I64, P]
         lib.gemm_w4a8_plan.restype = I32
+        lib.gemm_w4a8_plan_detail.argtypes = [I64, I64, I64, I32, P]
+        lib.gemm_w4a8_plan_detail.restype = I32
         lib.gemm_w4a8_decode_candidates.argtypes = [I64, I64, I64, P, I32, P]
         lib.gemm_w4a8_decode_candidates.restype = I32
         lib.gemm_w4a8_selector_score.argtypes = [I64, I64, I64, P, I64]
@@ -212,14 +215,19 @@ def workspace(device, nbytes: int):
         return buf
 
 
-def gemm_w4a8(qx, s_a, wpacked, s0, N: int, *, y=None, acc_out=None, ws=None, stream=None):
-    """INT8 activations [M, K] x packed weights -> fp16 y [M, N] (and INT32 acc_out if given)."""
+def gemm_w4a8(qx, s_a, wpacked, s0, N: int, *, y=None, acc_out=None, ws=None, use_workspace: bool = True,
+              stream=None):
+    """INT8 activations [M, K] x packed weights -> fp16 y [M, N] (and INT32 acc_out if given).
+
+    ws: the split-K workspace (default: one cached per device); use_workspace=False passes NULL."""
     import torch
     M, K = qx.shape
     if y is None:
         y = torch.empty((M, N), dtype=torch.float16, device=qx.device)
     need = gemm_w4a8_workspace_bytes(M, N, K)
-    if ws is None:
+    if not use_workspace:
+        ws = None
+    elif ws is None:
         ws = workspace(qx.device, need)
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     st = load().gemm_w4a8(_ptr(qx), _ptr(s_a), _ptr(wpacked), _ptr(s0), M, N, K, _ptr(y),
@@ -249,6 +257,13 @@ def gemm_w4a8_plan(M: int, N: int, K: int) -> dict:
     desc = (ctypes.c_int64 * 9)()
     _check(load().gemm_w4a8_plan(M, N, K, desc), "gemm_w4a8_plan")
     return dict(zip(PLAN_FIELDS, list(desc)))
+
+
+def gemm_w4a8_plan_detail(M: int, N: int, K: int, with_workspace: bool = True) -> dict:
+    """The plan gemm_w4a8 launches with a workspace (or with ws = NULL), and its LDS bytes per workgroup."""
+    desc = (ctypes.c_int64 * 10)()
+    _check(load().gemm_w4a8_plan_detail(M, N, K, int(bool(with_workspace)), desc), "gemm_w4a8_plan_detail")
+    return dict(zip(PLAN_FIELDS + ("lds_bytes",), list(desc)))
 
 
 def gemm_w4a8_decode_candidates(M: int, N: int, K: int) -> list:

@@ -21,6 +21,9 @@ bool weight_shape_ok(int64_t N, int64_t K)
            K <= ((int64_t)1 << 24) && code_bytes(N, K) + param_bytes(N, K) <= 0x7FFFFFFF;
 }
 
+// The GEMM also bounds K (kGemmMaxK) for its 32-bit activation offsets.
+bool gemm_shape_ok(int64_t N, int64_t K) { return weight_shape_ok(N, K) && K <= kGemmMaxK; }
+
 w4a8_status hip_status(hipError_t e) { return e == hipSuccess ? W4A8_OK : W4A8_E_HIP; }
 
 }  // namespace
@@ -197,15 +200,30 @@ w4a8_status attention_kv4_decode(const uint16_t *q_fp16, int64_t B, int64_t Hq, 
                                            ws, stream));
 }
 
+w4a8_status gemm_w4a8_plan_detail(int64_t M, int64_t N, int64_t K, int with_workspace, int64_t *desc)
+{
+    if (!desc)
+        return W4A8_E_NULL;
+    if (M <= 0 || M > kMaxM || !gemm_shape_ok(N, K) || (with_workspace != 0 && with_workspace != 1))
+        return W4A8_E_SHAPE;
+    GemmPlan p = plan_gemm(M, N, K);
+    if (!with_workspace && p.ws_bytes > 0)
+        p = plan_without_workspace(p, M, N, K);
+    const int64_t d[10] = {p.kind, p.mt, p.nt, p.splitk, p.waves, p.depth, p.xstage ? 1 : 0, (int64_t)p.ws_bytes,
+                           p.wave_n ? 1 : 0, (int64_t)plan_lds_bytes(p, M, K)};
+    for (int i = 0; i < 10; i++)
+        desc[i] = d[i];
+    return W4A8_OK;
+}
+
 w4a8_status gemm_w4a8_plan(int64_t M, int64_t N, int64_t K, int64_t *desc)
 {
     if (!desc)
         return W4A8_E_NULL;
-    if (M <= 0 || M > kMaxM || !weight_shape_ok(N, K))
-        return W4A8_E_SHAPE;
-    const GemmPlan p = plan_gemm(M, N, K);
-    const int64_t d[9] = {p.kind, p.mt, p.nt, p.splitk, p.waves, p.depth, p.xstage ? 1 : 0, (int64_t)p.ws_bytes,
-                          p.wave_n ? 1 : 0};
+    int64_t d[10];
+    const w4a8_status st = gemm_w4a8_plan_detail(M, N, K, 1, d);
+    if (st != W4A8_OK)
+        return st;
     for (int i = 0; i < 9; i++)
         desc[i] = d[i];
     return W4A8_OK;
@@ -216,7 +234,7 @@ w4a8_status gemm_w4a8_decode_candidates(int64_t M, int64_t N, int64_t K, int32_t
 {
     if (!count || (max_plans > 0 && !plans))
         return W4A8_E_NULL;
-    if (M <= 0 || M > 64 || max_plans < 0 || !weight_shape_ok(N, K))
+    if (M <= 0 || M > 64 || max_plans < 0 || !gemm_shape_ok(N, K))
         return W4A8_E_SHAPE;
     GemmPlan cand[256];
     const int n = decode_candidates(M, N, K, cand, 256);
@@ -232,7 +250,7 @@ w4a8_status gemm_w4a8_decode_candidates(int64_t M, int64_t N, int64_t K, int32_t
 
 float gemm_w4a8_selector_score(int64_t M, int64_t N, int64_t K, const int32_t *plan, int64_t cus)
 {
-    if (!plan || M <= 0 || M > 64 || !weight_shape_ok(N, K) || cus <= 0)
+    if (!plan || M <= 0 || M > 64 || !gemm_shape_ok(N, K) || cus <= 0)
         return -1.0f;
     GemmPlan p{};
     p.mt = plan[0];
@@ -253,7 +271,7 @@ float gemm_w4a8_selector_score(int64_t M, int64_t N, int64_t K, const int32_t *p
 
 size_t gemm_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
-    if (M <= 0 || M > kMaxM || !weight_shape_ok(N, K))
+    if (M <= 0 || M > kMaxM || !gemm_shape_ok(N, K))
         return 0;
     return plan_gemm(M, N, K).ws_bytes;
 }
@@ -262,7 +280,7 @@ w4a8_status gemm_w4a8(const int8_t *qx, const float *s_a, const void *wpacked,
                       const uint16_t *s0_fp16, int64_t M, int64_t N, int64_t K, uint16_t *y_fp16,
                       int32_t *acc_out, void *ws, size_t ws_bytes, hipStream_t stream)
 {
-    if (M < 0 || M > kMaxM || !weight_shape_ok(N, K))
+    if (M < 0 || M > kMaxM || !gemm_shape_ok(N, K))
         return W4A8_E_SHAPE;
     if (M == 0)
         return W4A8_OK;
@@ -273,7 +291,7 @@ w4a8_status gemm_w4a8(const int8_t *qx, const float *s_a, const void *wpacked,
         return W4A8_E_ALIGN;
     GemmPlan p = plan_gemm(M, N, K);
     if (p.ws_bytes > 0 && ws == nullptr)
-        p = plan_without_workspace(p);
+        p = plan_without_workspace(p, M, N, K);
     if (p.ws_bytes > 0 && ws_bytes < p.ws_bytes)
         return W4A8_E_WORKSPACE;
     return hip_status(launch_gemm(p, qx, s_a, static_cast<const uint8_t *>(wpacked), s0_fp16, M,

@@ -7,10 +7,13 @@
 // "mt,nt,splitk[,waves[,depth[,xstage]]]" overrides the decode choice (for
 // tuning sweeps); an override that names no instantiated variant is ignored.
 #include <algorithm>
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <mutex>
+#include <set>
 #include <unordered_map>
+#include <utility>
 
 #include "w4a8_internal.h"
 
@@ -20,6 +23,8 @@ bool decode_variant_exists(int mt, int nt, int waves, int depth, bool xs);
 size_t decode_lds_bytes(const GemmPlan &p, int64_t M, int64_t K);
 bool prefill_tm_supported(int tm);
 size_t prefill_ws_bytes(int tm, int P, int64_t M, int64_t N, int64_t K);
+size_t prefill_lds_bytes(int tm);
+GemmPlan launchable_fallback(int64_t M, int64_t N, int64_t K, bool split);
 hipError_t launch_gemm_prefill(const GemmPlan &p, const int8_t *qx, const float *s_a,
                                const uint8_t *stream_bytes, const uint16_t *s0, int64_t M,
                                int64_t N, int64_t K, uint16_t *y, int32_t *acc_out, void *ws,
@@ -29,20 +34,44 @@ hipError_t launch_gemm_decode(const GemmPlan &p, const int8_t *qx, const float *
                               int64_t N, int64_t K, uint16_t *y, int32_t *acc_out, void *ws,
                               hipStream_t st);
 
-// compute units of the current device (cached per device)
+// compute units of the current device (cached per device; several host
+// threads may race to fill an entry, all with the same value)
 int64_t num_cus()
 {
-    static int cached[64] = {};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
+}
+
+// The dynamic-LDS limit of a kernel is a per-device function attribute.  It
+// is raised once per (kernel, device) to the kernel's own maximum and never
+// lowered, so no launch can run under a smaller limit that another host
+// thread set between its check and its launch.  The mutex orders the first
+// calls; later calls find the pair in the set.
+hipError_t raise_lds_limit(const void *kernel, int bytes)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    static std::mutex mu;
+    static std::set<std::pair<const void *, int>> done;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_pair(kernel, dev);
+    if (done.count(key))
+        return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess)
+        done.insert(key);
+    return e;
 }
 
 namespace {
@@ -270,16 +299,82 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
         }
     }
     if (p.splitk > 1 && p.m_blocks * p.n_blocks > kWsCounters)
-        p.splitk = 1;   // more tiles than counters: run unsplit
+        return plan_without_workspace(p, M, N, K);   // more tiles than counters: run unsplit
+    if (!launchable(p, M, K))
+        return launchable_fallback(M, N, K, true);   // very long K: the plan's LDS does not fit
     p.ws_bytes = ws_size(p);
     return p;
 }
 
-GemmPlan plan_without_workspace(GemmPlan p)
+namespace {
+
+// The many-token kernel with the smallest tile, one workgroup per tile: its
+// LDS does not depend on K, so it runs every shape the C ABI accepts.
+GemmPlan prefill_unsplit(int64_t M, int64_t N)
 {
-    p.splitk = p.kind == 1 ? 0 : 1;
-    p.ws_bytes = 0;
+    GemmPlan q{};
+    q.kind = 1;
+    q.mt = 4;
+    q.nt = 16;
+    q.m_blocks = (M + 63) / 64;
+    q.n_blocks = (N + 255) / 256;
+    return q;
+}
+
+}  // namespace
+
+// The best-scored decode candidate that can launch (unsplit ones only unless
+// `split` is set), or the many-token kernel when no decode plan fits.
+GemmPlan launchable_fallback(int64_t M, int64_t N, int64_t K, bool split)
+{
+    GemmPlan cand[256];
+    const int nc = std::min(decode_candidates(M, N, K, cand, 256), 256);
+    const int64_t cus = num_cus();
+    const bool rank = selector_enabled();
+    const bool rank_wave_n = rank && selector_knows_wave_n();
+    int pick = -1;
+    float best = -2.0f;
+    for (int i = 0; i < nc; i++) {
+        if ((!split && cand[i].splitk != 1) || (cand[i].wave_n && rank && !rank_wave_n))
+            continue;
+        float u = 0.0f;
+        if (rank) {
+            float x[kSelFeatures];
+            selector_features(cand[i], M, N, K, cus, x);
+            u = selector_predict(x);
+        }
+        if (pick < 0 || u > best) {
+            pick = i;
+            best = u;
+        }
+    }
+    if (pick < 0)
+        return prefill_unsplit(M, N);
+    GemmPlan p = cand[pick];
+    p.ws_bytes = ws_size(p);
     return p;
+}
+
+GemmPlan plan_without_workspace(GemmPlan p, int64_t M, int64_t N, int64_t K)
+{
+    p.ws_bytes = 0;
+    if (p.kind == 1) {
+        p.splitk = 0;
+        return p;
+    }
+    p.splitk = 1;
+    // an N-split or staged plan keeps the whole K slice's parameters (and
+    // activation rows) in LDS, which an unsplit long K may not fit
+    if (launchable(p, M, K))
+        return p;
+    return launchable_fallback(M, N, K, false);
+}
+
+size_t plan_lds_bytes(const GemmPlan &p, int64_t M, int64_t K)
+{
+    if (p.kind == 1)
+        return prefill_lds_bytes(p.mt);
+    return p.wave_n ? decode_ns_lds_bytes(p, K) : decode_lds_bytes(p, M, K);
 }
 
 hipError_t launch_gemm(const GemmPlan &p, const int8_t *qx, const float *s_a,

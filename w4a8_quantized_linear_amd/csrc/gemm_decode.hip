@@ -420,16 +420,13 @@ template <int MT, int NT, int WAVES, int DEPTH, bool XS>
 hipError_t launch_decode_t(const GemmPlan &p, const DecodeArgs &a, size_t lds, hipStream_t st)
 {
     // plans with staged activation rows may use more than the default 64 KB of
-    // dynamic LDS: raise this kernel's limit to what the plan needs (the
-    // largest size asked so far is remembered per kernel)
-    static size_t lds_limit = 64 * 1024;
-    if (lds > lds_limit) {
-        const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&gemm_decode_kernel<MT, NT, WAVES, DEPTH, XS>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    // dynamic LDS: the first such plan raises this kernel's limit on the
+    // device to the largest any decode plan may take
+    if (lds > 64 * 1024) {
+        const hipError_t e = raise_lds_limit(
+            reinterpret_cast<const void *>(&gemm_decode_kernel<MT, NT, WAVES, DEPTH, XS>), (int)kDecodeLdsMax);
         if (e != hipSuccess)
             return e;
-        lds_limit = lds;
     }
     dim3 grid((unsigned)p.n_blocks, (unsigned)p.splitk, (unsigned)p.m_blocks);
     hipLaunchKernelGGL((gemm_decode_kernel<MT, NT, WAVES, DEPTH, XS>), grid, dim3(64 * WAVES), lds,
@@ -567,7 +564,7 @@ hipError_t launch_gemm_decode(const GemmPlan &p, const int8_t *qx, const float *
         a.ws_part = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(ws) + kWsPartOffset);
     }
     const size_t lds = decode_lds_bytes(p, M, K);
-    if (lds == 0 || lds > 160 * 1024)
+    if (lds == 0 || lds > kDecodeLdsMax)
         return hipErrorInvalidValue;
 #define W4A8_DECODE_CASE(MT_, NT_, WV_, D_, XS_)                                           \
     if (p.mt == MT_ && p.nt == NT_ && p.waves == WV_ && p.depth == D_ && p.xstage == XS_) \

@@ -354,13 +354,11 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_decode_ns_kernel(NsArgs a)
 template <int MT, int NTW, int DEPTH>
 hipError_t launch_ns_t(const GemmPlan &p, const NsArgs &a, size_t lds, hipStream_t st)
 {
-    static size_t lds_limit = 64 * 1024;
-    if (lds > lds_limit) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_decode_ns_kernel<MT, NTW, DEPTH>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (lds > 64 * 1024) {
+        const hipError_t e = raise_lds_limit(reinterpret_cast<const void *>(&gemm_decode_ns_kernel<MT, NTW, DEPTH>),
+                                             (int)kDecodeLdsMax);
         if (e != hipSuccess)
             return e;
-        lds_limit = lds;
     }
     dim3 grid((unsigned)p.n_blocks, (unsigned)p.splitk, (unsigned)p.m_blocks);
     hipLaunchKernelGGL((gemm_decode_ns_kernel<MT, NTW, DEPTH>), grid, dim3(64 * kWaves), lds, st, a);

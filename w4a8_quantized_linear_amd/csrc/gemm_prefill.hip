@@ -546,15 +546,10 @@ hipError_t launch_tm(int P, const int8_t *qx, const float *s_a, const uint8_t *s
                      int32_t *acc_out, void *ws, hipStream_t st)
 {
     constexpr int BM = Cfg<TM>::BM;
-    static bool attr_set = false;
     const size_t lds = lds_bytes<TM>();
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_prefill_kernel<TM>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess)
-            return e;
-        attr_set = true;
-    }
+    const hipError_t e = raise_lds_limit(reinterpret_cast<const void *>(&gemm_prefill_kernel<TM>), (int)lds);
+    if (e != hipSuccess)
+        return e;
     // (rows of the last block may reach BM past M, whose offsets must not wrap)
     const int64_t rows_max = (0x7FFFFFFF / K - BM) / BM * BM;
     for (int64_t r0 = 0; r0 < M; r0 += rows_max) {
@@ -596,6 +591,16 @@ hipError_t launch_tm(int P, const int8_t *qx, const float *s_a, const uint8_t *s
 }  // namespace
 
 bool prefill_tm_supported(int tm) { return tm == 4 || tm == 8 || tm == 16; }
+
+size_t prefill_lds_bytes(int tm)
+{
+    switch (tm) {
+    case 4: return lds_bytes<4>();
+    case 8: return lds_bytes<8>();
+    case 16: return lds_bytes<16>();
+    }
+    return 0;
+}
 
 // Stream-K workspace: the counters (one per tile; at most kWsCounters tiles
 // per launch), then two partial-accumulator slots of 16 TM x 256 INT32 per range.

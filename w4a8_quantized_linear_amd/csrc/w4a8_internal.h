@@ -153,8 +153,22 @@ bool selector_knows_wave_n();
 // compute units of the current device (256 when it cannot be queried)
 int64_t num_cus();
 
-// The same computation without a workspace (no split-K, no stream-K).
-GemmPlan plan_without_workspace(GemmPlan p);
+// The same computation without a workspace (no split-K, no stream-K): the
+// plan itself with its K unsplit when that still fits its LDS, else the
+// best-scored unsplit decode candidate, else the many-token kernel.
+GemmPlan plan_without_workspace(GemmPlan p, int64_t M, int64_t N, int64_t K);
+
+// Dynamic LDS bytes per workgroup that launching the plan requests.
+size_t plan_lds_bytes(const GemmPlan &p, int64_t M, int64_t K);
+
+// Raise a kernel's dynamic-LDS limit on the current device to `bytes`, once
+// per (kernel, device); safe to call from several host threads.
+hipError_t raise_lds_limit(const void *kernel, int bytes);
+
+// Largest K the GEMM accepts: the many-token kernel addresses a block of
+// activation rows with 32-bit offsets, and needs at least two blocks of its
+// largest tile (512 rows) within them.
+constexpr int64_t kGemmMaxK = (int64_t)1 << 22;
 
 hipError_t launch_gemm(const GemmPlan &p, const int8_t *qx, const float *s_a,
                        const uint8_t *stream_bytes, const uint16_t *s0, int64_t M, int64_t N,
