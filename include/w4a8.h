@@ -57,7 +57,8 @@ typedef enum w4a8_status {
     W4A8_E_SHAPE = -2,      /* M < 0, N <= 0, K <= 0, K % 128, N % 16, ld  */
     W4A8_E_ALIGN = -3,      /* a device pointer is not 16-byte aligned      */
     W4A8_E_WORKSPACE = -4,  /* workspace smaller than required              */
-    W4A8_E_HIP = -5         /* a HIP launch or runtime call failed          */
+    W4A8_E_HIP = -5,        /* a HIP launch or runtime call failed          */
+    W4A8_E_SCRATCH = -6     /* gemm_w4a8_noalloc: workspace need > scratch  */
 } w4a8_status;
 
 /* Text for a status code (host; static storage, never NULL). */
@@ -172,6 +173,31 @@ w4a8_status gemm_w4a8(const int8_t *qx, const float *s_a, const void *wpacked,
                       const uint16_t *s0_fp16, int64_t M, int64_t N, int64_t K,
                       uint16_t *y_fp16, int32_t *acc_out, void *ws,
                       size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * gemm_w4a8 for callers that cannot allocate: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The same plan,
+ * kernels and results as gemm_w4a8 with a workspace, but the split-K /
+ * stream-K workspace is a fixed array in device memory inside the library
+ * (W4A8_NOALLOC_SCRATCH_BYTES on every device the library runs on, held
+ * until the process ends).  The call allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library routine.  Its first call on a device looks
+ * up that device's copy of the array and clears its counters with a small
+ * kernel on `stream`.
+ * Every call on one device shares that device's array: calls that overlap
+ * on one GPU (different streams, or concurrent host threads without ordering)
+ * race and may give wrong results; order them on one stream.  The array is
+ * left as the last call used it (its counters zero).
+ * A shape whose plan needs more workspace than the array holds (see
+ * gemm_w4a8_workspace_bytes) is rejected with W4A8_E_SCRATCH before any
+ * launch.  Other arguments as gemm_w4a8; the stream must belong to the
+ * current device.
+ * ------------------------------------------------------------------------ */
+#define W4A8_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+
+w4a8_status gemm_w4a8_noalloc(const int8_t *qx, const float *s_a, const void *wpacked,
+                              const uint16_t *s0_fp16, int64_t M, int64_t N, int64_t K,
+                              uint16_t *y_fp16, int32_t *acc_out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Plan introspection and the learned plan selector (host only; no GPU work).

@@ -271,6 +271,29 @@ def test_gemm_validation(lib, monkeypatch):
     assert call(M=4096, N=4096, K=4096, ws=A, wsb=need - 1) == -4
 
 
+def test_gemm_noalloc_validation(lib):
+    f = lib.gemm_w4a8_noalloc
+    ok = dict(qx=A, sa=A, w=A, s0=A, M=1, N=16, K=128, y=B, acc=NUL)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["qx"], a["sa"], a["w"], a["s0"], a["M"], a["N"], a["K"], a["y"], a["acc"], S)
+
+    assert call(M=0, qx=NUL, y=NUL) == 0
+    assert call(M=-1) == -2
+    assert call(N=24) == -2
+    assert call(K=1 << 23) == -2
+    assert call(qx=NUL) == -1
+    assert call(y=NUL) == -1
+    assert call(y=MIS) == -3
+    assert call(acc=MIS) == -3
+    # a plan whose workspace exceeds the fixed scratch is rejected before launch
+    from w4a8_quantized_linear_amd import _lib
+    assert _lib.gemm_w4a8_workspace_bytes(512, 8192, 28672) > _lib.NOALLOC_SCRATCH_BYTES
+    assert call(M=512, N=8192, K=28672) == -6
+    assert "scratch" in _lib.status_string(-6)
+
+
 CONFIG_KN = [(512, 512), (4096, 12288), (4096, 4096), (4096, 22016), (11008, 4096), (4096, 11008),
              (8192, 10240), (8192, 57344), (28672, 8192)]
 

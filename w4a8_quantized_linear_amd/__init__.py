@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     W4A8Error,
     attention_kv4_decode,
     gemm_w4a8,
+    gemm_w4a8_noalloc,
     gemm_w4a8_decode_candidates,
     gemm_w4a8_plan,
     gemm_w4a8_plan_detail,
@@ -31,7 +32,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "W4A8Error", "attention_kv4_decode", "gemm_w4a8", "gemm_w4a8_decode_candidates", "gemm_w4a8_plan", "gemm_w4a8_plan_detail",
+    "W4A8Error", "attention_kv4_decode", "gemm_w4a8", "gemm_w4a8_noalloc", "gemm_w4a8_decode_candidates", "gemm_w4a8_plan", "gemm_w4a8_plan_detail",
     "gemm_w4a8_selector_score", "gemm_w4a16", "gemm_w4a8_workspace_bytes",
     "kv4_attention_workspace_bytes", "kv4_cache_alloc", "kv4_cache_bytes", "kv4_unpack", "linear",
     "norm_quantize_act_i8", "quantize_act_per_token_i8", "quantize_kv4",

@@ -19,12 +19,14 @@ W4A8_E_SHAPE = -2
 W4A8_E_ALIGN = -3
 W4A8_E_WORKSPACE = -4
 W4A8_E_HIP = -5
+W4A8_E_SCRATCH = -6
+NOALLOC_SCRATCH_BYTES = 64 << 20     # W4A8_NOALLOC_SCRATCH_BYTES
 
 # every symbol include/w4a8.h declares
 EXPORTS = (
     "w4a8_status_string", "w4a8_version", "w4a8_packed_weight_bytes",
     "quantize_weights_w4g128", "w4a8_unpack_weights", "quantize_act_per_token_i8",
-    "norm_quantize_act_i8", "gemm_w4a8_workspace_bytes", "gemm_w4a8", "gemm_w4a16",
+    "norm_quantize_act_i8", "gemm_w4a8_workspace_bytes", "gemm_w4a8", "gemm_w4a8_noalloc", "gemm_w4a16",
     "kv4_cache_bytes", "quantize_kv4", "kv4_unpack", "kv4_attention_workspace_bytes",
     "attention_kv4_decode", "gemm_w4a8_plan", "gemm_w4a8_plan_detail", "gemm_w4a8_decode_candidates",
     "gemm_w4a8_selector_score",
@@ -69,6 +71,8 @@ def load() -> ctypes.CDLL:
         lib.gemm_w4a8_workspace_bytes.restype = SZ
         lib.gemm_w4a8.argtypes = [P, P, P, P, I64, I64, I64, P, P, P, SZ, P]
         lib.gemm_w4a8.restype = I32
+        lib.gemm_w4a8_noalloc.argtypes = [P, P, P, P, I64, I64, I64, P, P, P]
+        lib.gemm_w4a8_noalloc.restype = I32
         lib.gemm_w4a16.argtypes = [P, I64, I64, I64, P, P, I64, P, P]
         lib.gemm_w4a16.restype = I32
         lib.gemm_w4a8_plan.argtypes = [I64, I64, I64, P]
@@ -233,6 +237,16 @@ def gemm_w4a8(qx, s_a, wpacked, s0, N: int, *, y=None, acc_out=None, ws=None, us
     st = load().gemm_w4a8(_ptr(qx), _ptr(s_a), _ptr(wpacked), _ptr(s0), M, N, K, _ptr(y),
                           _ptr(acc_out), _ptr(ws), wsb, _stream(stream))
     _check(st, "gemm_w4a8")
+    return y
+
+
+def gemm_w4a8_noalloc(qx, s_a, wpacked, s0, N: int, *, y, acc_out=None, stream=None):
+    """gemm_w4a8 with the library's fixed device scratch as its workspace: allocates nothing (y is
+    required).  Calls that overlap on one GPU race."""
+    M, K = qx.shape
+    st = load().gemm_w4a8_noalloc(_ptr(qx), _ptr(s_a), _ptr(wpacked), _ptr(s0), M, N, K, _ptr(y),
+                                  _ptr(acc_out), _stream(stream))
+    _check(st, "gemm_w4a8_noalloc")
     return y
 
 

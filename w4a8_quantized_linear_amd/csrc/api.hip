@@ -2,6 +2,7 @@
 // checks on the host, then launches on the caller's stream.  Every argument
 // error is reported before anything is enqueued; nothing here allocates.
 #include <cstdint>
+#include <mutex>
 
 #include "w4a8.h"
 #include "w4a8_internal.h"
@@ -39,6 +40,8 @@ const char *w4a8_status_string(w4a8_status st)
     case W4A8_E_ALIGN: return "a device pointer is not 16-byte aligned";
     case W4A8_E_WORKSPACE: return "workspace missing or smaller than the *_workspace_bytes() size";
     case W4A8_E_HIP: return "HIP launch or runtime error";
+    case W4A8_E_SCRATCH: return "the call needs more workspace than gemm_w4a8_noalloc's fixed scratch holds "
+                                "(W4A8_NOALLOC_SCRATCH_BYTES); call gemm_w4a8 with a workspace";
     }
     return "unknown status";
 }
@@ -276,19 +279,121 @@ size_t gemm_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K)
     return plan_gemm(M, N, K).ws_bytes;
 }
 
-w4a8_status gemm_w4a8(const int8_t *qx, const float *s_a, const void *wpacked,
-                      const uint16_t *s0_fp16, int64_t M, int64_t N, int64_t K, uint16_t *y_fp16,
-                      int32_t *acc_out, void *ws, size_t ws_bytes, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by gemm_w4a8 and gemm_w4a8_noalloc, in the order
+// the header documents (shape, then M == 0 as a no-op, then pointers).
+// Returns W4A8_OK with *noop set for M == 0.
+w4a8_status gemm_args(const int8_t *qx, const float *s_a, const void *wpacked, const uint16_t *s0_fp16,
+                      int64_t M, int64_t N, int64_t K, const uint16_t *y_fp16, const int32_t *acc_out,
+                      const void *ws, bool *noop)
 {
+    *noop = false;
     if (M < 0 || M > kMaxM || !gemm_shape_ok(N, K))
         return W4A8_E_SHAPE;
-    if (M == 0)
+    if (M == 0) {
+        *noop = true;
         return W4A8_OK;
+    }
     if (!qx || !s_a || !wpacked || !s0_fp16 || !y_fp16)
         return W4A8_E_NULL;
     if (!aligned16(qx) || !aligned16(s_a) || !aligned16(wpacked) || !aligned16(s0_fp16) ||
         !aligned16(y_fp16) || (acc_out && !aligned16(acc_out)) || (ws && !aligned16(ws)))
         return W4A8_E_ALIGN;
+    return W4A8_OK;
+}
+
+// ---- the workspace of gemm_w4a8_noalloc -------------------------------------
+// A fixed array in device memory, one copy per device the library runs on,
+// held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not a device address: its address on the current device comes
+// from hipGetSymbolAddress, once per device, and only that pointer is passed
+// to kernels.  The array's arrival counters (the first kWsCounters dwords)
+// must be zero before the first GEMM that splits K; every GEMM leaves them
+// zero again, and the partial slots after them are scratch.
+static_assert(W4A8_NOALLOC_SCRATCH_BYTES % 256 == 0 && W4A8_NOALLOC_SCRATCH_BYTES > kWsPartOffset,
+              "scratch holds the counters and partial slots");
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[W4A8_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+__global__ void clear_counters_kernel(uint32_t *cnt, int n)
+{
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n)
+        cnt[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+
+// The current device's address of `scratch`.  The first call on a device
+// looks it up (hipGetSymbolAddress, return code checked) and clears the
+// counters with a fill kernel on `st` (a kernel, so that a caller capturing
+// `st` into a graph records no memset).
+hipError_t noalloc_scratch(void **ptr, hipStream_t st)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0)
+            return hipErrorInvalidSymbol;
+        hipLaunchKernelGGL(clear_counters_kernel, dim3((unsigned)(kWsCounters / 256)), dim3(256), 0, st,
+                           static_cast<uint32_t *>(p), (int)kWsCounters);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+w4a8_status gemm_w4a8_noalloc(const int8_t *qx, const float *s_a, const void *wpacked, const uint16_t *s0_fp16,
+                              int64_t M, int64_t N, int64_t K, uint16_t *y_fp16, int32_t *acc_out,
+                              hipStream_t stream)
+{
+    bool noop = false;
+    const w4a8_status st = gemm_args(qx, s_a, wpacked, s0_fp16, M, N, K, y_fp16, acc_out, nullptr, &noop);
+    if (st != W4A8_OK || noop)
+        return st;
+    const GemmPlan p = plan_gemm(M, N, K);
+    if (p.ws_bytes > (size_t)W4A8_NOALLOC_SCRATCH_BYTES)
+        return W4A8_E_SCRATCH;
+    void *ws = nullptr;
+    if (p.ws_bytes > 0 && noalloc_scratch(&ws, stream) != hipSuccess)
+        return W4A8_E_HIP;
+    return hip_status(launch_gemm(p, qx, s_a, static_cast<const uint8_t *>(wpacked), s0_fp16, M, N, K, y_fp16,
+                                  acc_out, ws, stream));
+}
+
+w4a8_status gemm_w4a8(const int8_t *qx, const float *s_a, const void *wpacked,
+                      const uint16_t *s0_fp16, int64_t M, int64_t N, int64_t K, uint16_t *y_fp16,
+                      int32_t *acc_out, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    bool noop = false;
+    const w4a8_status st = gemm_args(qx, s_a, wpacked, s0_fp16, M, N, K, y_fp16, acc_out, ws, &noop);
+    if (st != W4A8_OK || noop)
+        return st;
     GemmPlan p = plan_gemm(M, N, K);
     if (p.ws_bytes > 0 && ws == nullptr)
         p = plan_without_workspace(p, M, N, K);
