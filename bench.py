@@ -10,7 +10,9 @@ weights, rotating through enough copies to exceed the 256 MB Infinity Cache,
 so weight bytes really come from HBM.
 
 Prints one JSON line: whole-step throughput (TOPS), the roofline of the
-dominant kernel (the M=4096 GEMM), per-M kernel figures, and the CPU oracle
+dominant kernel (the M=4096 GEMM), per-M kernel figures, every shape of the
+five workload configurations ("configs": µs, GB/s, TOPS, fractions of the HBM
+and INT8 peaks and of the measured streaming-read ceiling), and the CPU oracle
 timed on a bounded sample of the same workload.  Two separate objects, not
 part of the step or of `value`, measure the other entry points on the same
 tensors against the HBM roofline, each with its oracle beside it:
@@ -51,6 +53,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="token rows per M in the oracle sample (default: every row, one whole step)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration block")
     return ap.parse_args()
 
 
@@ -68,6 +71,7 @@ def main():
     from w4a8_quantized_linear_amd.tuning import graph_time
     from w4a8_quantized_linear_amd import (gemm_w4a8, gemm_w4a16, norm_quantize_act_i8,
                                            quantize_act_per_token_i8, quantize_weights_w4g128)
+    from w4a8_quantized_linear_amd._lib import w4a8_hbm_read
     if not os.path.exists(_lib.LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
@@ -135,6 +139,8 @@ def main():
     # ---- per-M kernel figures: `reps` calls captured in one HIP graph and
     # replayed under events, so that small-M figures are the kernels' own time
     # and not the host's launch rate ----------------------------------------
+    sink = torch.zeros(64, dtype=torch.int32, device=dev)
+    ceil_us = graph_time(lambda r: w4a8_hbm_read(wcopies[r % nrot], sink), args.reps)
     per_m = []
     for M in MS:
         rec = {"M": M}
@@ -154,16 +160,24 @@ def main():
                 rec["gemm_TOPS"] = round(ops / us * 1e-6, 2)
                 rec["hbm_frac"] = round(nbytes / us * 1e-3 / (A.MI355X_HBM_BYTES_PER_S / 1e9), 4)
                 rec["mfma_frac"] = round(ops / us * 1e-6 / (A.MI355X_INT8_OPS_PER_S / 1e12), 4)
+                rec["ceiling_frac"] = round(ceil_us / us, 4)
         per_m.append(rec)
 
     # ---- roofline of the dominant kernel (M=4096 GEMM, MFMA-bound) ---------
+    # Its duration is the graph-timed per-M figure (HIP events around replays of
+    # `reps` back-to-back launches on the launch stream): the kernel's own time,
+    # which a rocprofv3 kernel trace of this command reproduces.  The events
+    # bracketing it inside the eager step also cover the markers' cache flush
+    # and dispatch; that figure is kept as eager_step_avg_us.
     dom_ops = A.gemm_ops(dom_M, N_DIM, K_DIM)
-    achieved = dom_ops / (dom_us * 1e-6) / 1e12
+    dom_graph_us = next(r for r in per_m if r["M"] == dom_M)["gemm_us"]
+    achieved = dom_ops / (dom_graph_us * 1e-6) / 1e12
     peak = A.MI355X_INT8_OPS_PER_S / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(),
                 "kernel": "gemm_w4a8 M=%d N=%d K=%d" % (dom_M, N_DIM, K_DIM),
-                "avg_us": round(dom_us, 3), "ops_per_launch": dom_ops}
+                "avg_us": round(dom_graph_us, 3), "eager_step_avg_us": round(dom_us, 3),
+                "ops_per_launch": dom_ops}
 
     # ---- fused normalization + quantizer (not part of the step) -----------
     gam = torch.from_numpy(workloads.norm_affine(K_DIM)[0]).to(dev)
@@ -200,6 +214,7 @@ def main():
                           "bytes_per_launch": A.w4a16_bytes(w16[0]["M"], N_DIM, K_DIM)}}
 
     kv4 = bench_kv4(args, stream)
+    configs = None if args.no_configs else bench_configs(args)
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TOPS", "n_gpus": 1,
@@ -211,7 +226,11 @@ def main():
                    "K": K_DIM, "N": N_DIM, "M": list(MS), "group": 128,
                    "weight_copies": nrot, "wall_s": round(wall, 4)},
         "roofline": roofline,
+        "hbm_read_ceiling": {"bytes": wbytes, "us": round(ceil_us, 3),
+                             "GBps": round(wbytes / ceil_us * 1e-3, 1),
+                             "kernel": "w4a8_hbm_read (the weight stream read once, nothing computed)"},
         "per_m": per_m,
+        "configs": configs,
         "norm_quant": norm_quant,
         "w4a16": w4a16,
         "kv4_attention": kv4,
@@ -224,6 +243,65 @@ def main():
         kv4["cpu_baseline"] = cpu_baseline_kv4()
 
     print(json.dumps(out), flush=True)
+
+
+def bench_configs(args):
+    """Every shape of the five workload configurations: the GEMM (and for the
+    prefill configuration the activation quantizer before it) timed as HIP-graph
+    replays, weights rotated through 1 GiB of copies so that their bytes come
+    from HBM, beside the streaming-read ceiling of the same weight bytes.  The
+    weights are random packed bytes (every byte is a valid code pair and group
+    parameter; the kernels' timing does not depend on the values); the
+    parity tests cover the seeded weights of each configuration."""
+    import torch
+
+    from w4a8_quantized_linear_amd import (_lib, accounting as A, gemm_w4a8, quantize_act_per_token_i8,
+                                           w4a8_packed_weight_bytes, workloads as W)
+    from w4a8_quantized_linear_amd._lib import w4a8_hbm_read
+    from w4a8_quantized_linear_amd.tuning import graph_time
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0x57A8)
+    pool = torch.randint(0, 256, (ROTATE_BYTES,), dtype=torch.uint8, device=dev, generator=gen)
+    sink = torch.zeros(64, dtype=torch.int32, device=dev)
+    reps = max(10, args.reps // 2)
+    hbm, ops_peak = A.MI355X_HBM_BYTES_PER_S, A.MI355X_INT8_OPS_PER_S
+    ridge = ops_peak / hbm
+    out = []
+    for fam in W.FAMILIES:
+        for (K, N) in fam.kns:
+            wb = w4a8_packed_weight_bytes(N, K)
+            stride = (wb + 4095) // 4096 * 4096
+            views = [pool[i * stride:i * stride + wb] for i in range(max(2, min(64, ROTATE_BYTES // stride)))]
+            s0 = (torch.rand(N, device=dev, generator=gen) * 1e-3).half()
+            cus = graph_time(lambda r: w4a8_hbm_read(views[r % len(views)], sink), reps)
+            for M in fam.ms:
+                qx = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev, generator=gen)
+                sa = torch.rand(M, device=dev, generator=gen) * 1e-2
+                y = torch.empty((M, N), dtype=torch.float16, device=dev)
+                ws = _lib.workspace(dev, _lib.gemm_w4a8_workspace_bytes(M, N, K))
+                us = graph_time(lambda r: gemm_w4a8(qx, sa, views[r % len(views)], s0, N, y=y, ws=ws), reps)
+                nbytes, ops = A.gemm_bytes(M, N, K), A.gemm_ops(M, N, K)
+                rec = {"config": fam.index, "M": M, "K": K, "N": N,
+                       "bound": "hbm" if ops / nbytes < ridge else "mfma",
+                       "gemm_us": round(us, 3), "GBps": round(nbytes / us * 1e-3, 1),
+                       "TOPS": round(ops / us * 1e-6, 2), "hbm_frac": round(nbytes / us * 1e-3 / (hbm / 1e9), 4),
+                       "mfma_frac": round(ops / us * 1e-6 / (ops_peak / 1e12), 4),
+                       "ceiling_us": round(cus, 3), "ceiling_frac": round(cus / us, 4)}
+                if fam.index == 3:
+                    # prefill: the activation quantizer is part of the timed work
+                    x = (torch.randn((M, K), device=dev, generator=gen) * 2).half()
+                    aus = graph_time(lambda r: quantize_act_per_token_i8(x, qx=qx, s_a=sa), reps)
+                    tot = aus + us
+                    rec.update({"act_quant_us": round(aus, 3), "total_us": round(tot, 3),
+                                "total_TOPS": round(ops / tot * 1e-6, 2),
+                                "total_mfma_frac": round(ops / tot * 1e-6 / (ops_peak / 1e12), 4)})
+                    del x
+                out.append(rec)
+                del qx, sa, y
+    del pool
+    torch.cuda.empty_cache()
+    return out
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_w4a8_m4096_k4096_n11008.txt")
@@ -282,18 +360,26 @@ def cpu_baseline(w_np, rows):
                       "(first rows of each M of the sweep)" % sample}
 
 
-def cpu_baseline_norm_quant(rows: int = 1024):
-    """The fused producer's oracle on a bounded sample: the first `rows` tokens of the M=4096 activations."""
+def cpu_baseline_norm_quant(rows: int = 4096):
+    """The fused producer's oracle on a bounded sample: the first `rows` tokens of the M=4096 activations.
+    The oracle is one serial C call per block of tokens; the blocks run on host threads (the C call
+    releases the interpreter lock), as many as the oracle's GEMM uses, so the baselines are comparable."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle as orc
     from w4a8_quantized_linear_amd import accounting as A, workloads
     x = workloads.activations(FAMILY, MS[-1], K_DIM, N_DIM)[:rows]
     g, b = workloads.norm_affine(K_DIM)
+    threads = max(1, min(orc.num_threads(), rows))
+    blocks = [x[i * rows // threads:(i + 1) * rows // threads] for i in range(threads)]
     t0 = time.perf_counter()
-    orc.norm_quantize_act(x, g, b, eps=1e-5)
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(lambda blk: orc.norm_quantize_act(blk, g, b, eps=1e-5), blocks))
     s = time.perf_counter() - t0
-    return {"value": round(A.norm_quant_bytes(rows, K_DIM) / s / 1e9, 3), "unit": "GB/s", "cores": 1,
+    return {"value": round(A.norm_quant_bytes(rows, K_DIM) / s / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "seconds": round(s, 3),
-            "sample": "oracle LayerNorm + per-token INT8, K=%d, the first %d tokens of M=%d" % (K_DIM, rows, MS[-1])}
+            "sample": "oracle LayerNorm + per-token INT8, K=%d, the first %d tokens of M=%d, in %d blocks on "
+                      "%d host threads" % (K_DIM, rows, MS[-1], threads, threads)}
 
 
 def bench_kv4(args, stream):

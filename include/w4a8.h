@@ -200,6 +200,22 @@ w4a8_status gemm_w4a8_noalloc(const int8_t *qx, const float *s_a, const void *wp
                               uint16_t *y_fp16, int32_t *acc_out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Measurement aid: the streaming-read ceiling (Lecture 15 notes, 15.1 and
+ * "Numbers worth memorizing": a decode-size layer cannot finish before its
+ * weight bytes have streamed from HBM).  Reads `bytes` of device memory at
+ * `buf` once, the way the GEMM reads its weight stream (16-byte
+ * non-temporal loads, 32 KB per workgroup, every load of a wave in flight at
+ * once), and computes nothing from them; its duration on the same number of
+ * bytes is the fastest a streaming kernel launch reaches on the device, the
+ * second yardstick (beside the published HBM peak) for the decode GEMM.
+ * bytes % 16 == 0 and bytes < 2^31 (W4A8_E_SHAPE otherwise; 0 is a no-op);
+ * buf 16-byte aligned, sink one 4-byte-aligned device dword that is written
+ * only in the (practically never taken) case that the data's xor equals a
+ * fixed constant.
+ * ------------------------------------------------------------------------ */
+w4a8_status w4a8_hbm_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Plan introspection and the learned plan selector (host only; no GPU work).
  *
  * gemm_w4a8_plan: the plan gemm_w4a8 would launch for (M, N, K) on the

@@ -490,7 +490,7 @@ def test_workspace_shared_across_shapes_and_kernels():
                 os.environ[k] = v
 
 
-@pytest.mark.parametrize("M,K,N", [(5, 1152, 272), (40, 2048, 528)])
+@pytest.mark.parametrize("M,K,N", [(5, 1152, 272), (24, 3072, 1040), (40, 2048, 528)])
 def test_every_decode_candidate_is_exact(M, K, N):
     """Every plan the learned selector may pick (gemm_w4a8_decode_candidates)
     runs, and gives the oracle's INT32 accumulators bit for bit."""

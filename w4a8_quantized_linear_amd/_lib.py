@@ -29,7 +29,7 @@ EXPORTS = (
     "norm_quantize_act_i8", "gemm_w4a8_workspace_bytes", "gemm_w4a8", "gemm_w4a8_noalloc", "gemm_w4a16",
     "kv4_cache_bytes", "quantize_kv4", "kv4_unpack", "kv4_attention_workspace_bytes",
     "attention_kv4_decode", "gemm_w4a8_plan", "gemm_w4a8_plan_detail", "gemm_w4a8_decode_candidates",
-    "gemm_w4a8_selector_score",
+    "gemm_w4a8_selector_score", "w4a8_hbm_read",
 )
 
 _lock = threading.Lock()
@@ -77,6 +77,8 @@ def load() -> ctypes.CDLL:
         lib.gemm_w4a16.restype = I32
         lib.gemm_w4a8_plan.argtypes = [I64, I64, I64, P]
         lib.gemm_w4a8_plan.restype = I32
+        lib.w4a8_hbm_read.argtypes = [P, SZ, P, P]
+        lib.w4a8_hbm_read.restype = I32
         lib.gemm_w4a8_plan_detail.argtypes = [I64, I64, I64, I32, P]
         lib.gemm_w4a8_plan_detail.restype = I32
         lib.gemm_w4a8_decode_candidates.argtypes = [I64, I64, I64, P, I32, P]
@@ -271,6 +273,12 @@ def gemm_w4a8_plan(M: int, N: int, K: int) -> dict:
     desc = (ctypes.c_int64 * 9)()
     _check(load().gemm_w4a8_plan(M, N, K, desc), "gemm_w4a8_plan")
     return dict(zip(PLAN_FIELDS, list(desc)))
+
+
+def w4a8_hbm_read(buf, sink, *, nbytes=None, stream=None):
+    """Stream-read nbytes (default all) of the uint8 device tensor buf once (the streaming-read ceiling)."""
+    n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    _check(load().w4a8_hbm_read(_ptr(buf), n, _ptr(sink), _stream(stream)), "w4a8_hbm_read")
 
 
 def gemm_w4a8_plan_detail(M: int, N: int, K: int, with_workspace: bool = True) -> dict:

@@ -213,7 +213,7 @@ w4a8_status gemm_w4a8_plan_detail(int64_t M, int64_t N, int64_t K, int with_work
     if (!with_workspace && p.ws_bytes > 0)
         p = plan_without_workspace(p, M, N, K);
     const int64_t d[10] = {p.kind, p.mt, p.nt, p.splitk, p.waves, p.depth, p.xstage ? 1 : 0, (int64_t)p.ws_bytes,
-                           p.wave_n ? 1 : 0, (int64_t)plan_lds_bytes(p, M, K)};
+                           p.wave_n, (int64_t)plan_lds_bytes(p, M, N, K)};
     for (int i = 0; i < 10; i++)
         desc[i] = d[i];
     return W4A8_OK;
@@ -244,7 +244,7 @@ w4a8_status gemm_w4a8_decode_candidates(int64_t M, int64_t N, int64_t K, int32_t
     *count = n;
     for (int i = 0; i < n && i < max_plans && i < 256; i++) {
         const int32_t row[7] = {cand[i].mt, cand[i].nt, cand[i].splitk, cand[i].waves, cand[i].depth,
-                                cand[i].xstage ? 1 : 0, cand[i].wave_n ? 1 : 0};
+                                cand[i].xstage ? 1 : 0, cand[i].wave_n};
         for (int j = 0; j < 7; j++)
             plans[7 * i + j] = row[j];
     }
@@ -262,8 +262,8 @@ float gemm_w4a8_selector_score(int64_t M, int64_t N, int64_t K, const int32_t *p
     p.waves = plan[3];
     p.depth = plan[4];
     p.xstage = plan[5] != 0;
-    p.wave_n = plan[6] != 0;
-    if (p.mt <= 0 || p.nt <= 0 || p.splitk <= 0 || p.waves <= 0 || p.depth <= 0)
+    p.wave_n = plan[6];
+    if (p.mt <= 0 || p.nt <= 0 || p.splitk <= 0 || p.waves <= 0 || p.depth <= 0 || p.wave_n < 0 || p.wave_n > 1)
         return -1.0f;
     p.m_blocks = (M + 16 * p.mt - 1) / (16 * p.mt);
     p.n_blocks = (N / kTileN + p.nt - 1) / p.nt;

@@ -85,9 +85,9 @@ size_t ws_size(const GemmPlan &p)
     return (size_t)kWsPartOffset + (size_t)tiles * p.splitk * 256 * p.mt * p.nt * 4;
 }
 
-bool launchable(const GemmPlan &p, int64_t M, int64_t K)
+bool launchable(const GemmPlan &p, int64_t M, int64_t N, int64_t K)
 {
-    if (p.wave_n) {
+    if (p.wave_n == 1) {
         const size_t lds = decode_ns_lds_bytes(p, K);
         return p.waves == 4 && p.nt % 4 == 0 && decode_ns_variant_exists(p.mt, p.nt / 4, p.depth) && lds > 0 &&
                lds <= kDecodeLdsMax;
@@ -134,9 +134,8 @@ GemmPlan selected_plan(int64_t M, int64_t N, int64_t K, const GemmPlan &fallback
     const int nc = std::min(decode_candidates(M, N, K, cand, 256), 256);
     GemmPlan top = fallback;
     float best = -1.0f;
-    const bool rank_wave_n = selector_knows_wave_n();
     for (int i = 0; i < nc; i++) {
-        if (cand[i].wave_n && !rank_wave_n)
+        if (!selector_knows_wave_n(cand[i].wave_n))
             continue;
         float x[kSelFeatures];
         selector_features(cand[i], M, N, K, cus, x);
@@ -210,7 +209,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     if (p.mt == 1 && p.splitk == 1) {
         GemmPlan q = p;
         q.xstage = true;
-        if (launchable(q, M, K) && decode_lds_bytes(q, M, K) <= 64 * 1024)
+        if (launchable(q, M, N, K) && decode_lds_bytes(q, M, K) <= 64 * 1024)
             p = q;
     }
     // the learned selector, when a model is compiled in: the candidate with
@@ -290,17 +289,17 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
         q.waves = wv;
         q.depth = dp;
         q.xstage = xs != 0 || wn != 0;
-        q.wave_n = wn != 0;
+        q.wave_n = wn != 0 ? 1 : 0;
         if (got >= 3 && nt > 0 && s >= 1 && s <= P && (mt == 1 || mt == 2 || mt == 4)) {
             q.m_blocks = (M + 16 * mt - 1) / (16 * mt);
             q.n_blocks = (ntiles + nt - 1) / nt;
-            if (launchable(q, M, K))
+            if (launchable(q, M, N, K))
                 p = q;
         }
     }
     if (p.splitk > 1 && p.m_blocks * p.n_blocks > kWsCounters)
         return plan_without_workspace(p, M, N, K);   // more tiles than counters: run unsplit
-    if (!launchable(p, M, K))
+    if (!launchable(p, M, N, K))
         return launchable_fallback(M, N, K, true);   // very long K: the plan's LDS does not fit
     p.ws_bytes = ws_size(p);
     return p;
@@ -331,11 +330,10 @@ GemmPlan launchable_fallback(int64_t M, int64_t N, int64_t K, bool split)
     const int nc = std::min(decode_candidates(M, N, K, cand, 256), 256);
     const int64_t cus = num_cus();
     const bool rank = selector_enabled();
-    const bool rank_wave_n = rank && selector_knows_wave_n();
     int pick = -1;
     float best = -2.0f;
     for (int i = 0; i < nc; i++) {
-        if ((!split && cand[i].splitk != 1) || (cand[i].wave_n && rank && !rank_wave_n))
+        if ((!split && cand[i].splitk != 1) || (rank && !selector_knows_wave_n(cand[i].wave_n)))
             continue;
         float u = 0.0f;
         if (rank) {
@@ -365,16 +363,16 @@ GemmPlan plan_without_workspace(GemmPlan p, int64_t M, int64_t N, int64_t K)
     p.splitk = 1;
     // an N-split or staged plan keeps the whole K slice's parameters (and
     // activation rows) in LDS, which an unsplit long K may not fit
-    if (launchable(p, M, K))
+    if (launchable(p, M, N, K))
         return p;
     return launchable_fallback(M, N, K, false);
 }
 
-size_t plan_lds_bytes(const GemmPlan &p, int64_t M, int64_t K)
+size_t plan_lds_bytes(const GemmPlan &p, int64_t M, int64_t N, int64_t K)
 {
     if (p.kind == 1)
         return prefill_lds_bytes(p.mt);
-    return p.wave_n ? decode_ns_lds_bytes(p, K) : decode_lds_bytes(p, M, K);
+    return p.wave_n == 1 ? decode_ns_lds_bytes(p, K) : decode_lds_bytes(p, M, K);
 }
 
 hipError_t launch_gemm(const GemmPlan &p, const int8_t *qx, const float *s_a,
@@ -390,7 +388,7 @@ hipError_t launch_gemm(const GemmPlan &p, const int8_t *qx, const float *s_a,
                      (long long)p.m_blocks);
     if (p.kind == 1)
         return launch_gemm_prefill(p, qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, ws, st);
-    if (p.wave_n)
+    if (p.wave_n == 1)
         return launch_gemm_decode_ns(p, qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, ws, st);
     return launch_gemm_decode(p, qx, s_a, stream_bytes, s0, M, N, K, y, acc_out, ws, st);
 }

@@ -29,53 +29,20 @@
 // (rows = channels) and the tokens as the B operand (columns = tokens; columns
 // past M carry whatever row their lane loads and are never stored).  The
 // waves' partial accumulators meet in LDS through LDS atomics; with split-K
-// the workgroups of one tile add their partials into an INT32 workspace with
-// device atomics (exact, so any arrival order gives the same bits) and the
-// last to arrive applies the epilogue and clears its part of the workspace.
-//
-// The packed rebuild.  For a dword holding four codes b in [0, 15], one per
-// byte, v_pk_mad_u16(x, s1, C) with C = 257 (128 - z s1) mod 2^16 computes in
-// each byte b s1 - z s1 + 128, which the protective range keeps in [1, 255],
-// so no carry or borrow crosses a byte; xor 0x80808080 then turns each byte
-// into the signed INT8 value b s1 - z s1.  Subtracting the zero first would
-// put negative values into the packed lanes and borrow across bytes, which is
-// the overflow hazard the QServe talk summary attributes to subtraction
-// before multiplication.
+// each workgroup of a tile stores its partial into its own workspace slot and
+// the last to arrive adds the slots in split order and applies the epilogue
+// (kernel_common.h, splitk_finish).  The packed rebuild and its byte-lane
+// arithmetic are described at rebuild4 in kernel_common.h.
 #include <algorithm>
 
-#include "w4a8_internal.h"
+#include "kernel_common.h"
 
 namespace w4a8 {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef unsigned short us2 __attribute__((ext_vector_type(2)));
-
-constexpr int kBufFlags = 0x00020000;   // raw buffer resource, dword 3 (gfx9 family)
-constexpr int kLoadNT = 2;              // non-temporal (streaming) load policy
-
-__device__ inline uint32_t rebuild4(uint32_t nib, us2 S, us2 C)
-{
-    us2 v = __builtin_bit_cast(us2, nib);
-    v = v * S + C;
-    return __builtin_bit_cast(uint32_t, v) ^ 0x80808080u;
-}
-
-__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *p, int64_t bytes)
-{
-    const int64_t lim = bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)lim, kBufFlags);
-}
+using namespace dev;
 
 __device__ inline int sgpr(int64_t v) { return __builtin_amdgcn_readfirstlane((int)v); }
-
-// decoded constants of one group: s1 in the low half, 257 (128 - z s1) in the high half
-__device__ inline uint32_t decode_param(uint32_t p)
-{
-    const uint32_t s1 = (p & 15u) + 1u;
-    const uint32_t c16 = ((128u - (p >> 4) * s1) * 257u) & 0xFFFFu;
-    return s1 | (c16 << 16);
-}
 
 struct DecodeArgs {
     const int8_t *qx;
@@ -143,19 +110,21 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
     int8_t *xlds = reinterpret_cast<int8_t *>(praw + praw_bytes);
 
     const __amdgpu_buffer_rsrc_t rw = rsrc(a.codes, code_bytes(a.N, a.K));
+    const __amdgpu_buffer_rsrc_t rp = rsrc(a.params, param_bytes(a.N, a.K));
     const int8_t *xblk = a.qx + m0 * a.K;     // this block's first token row
+    const __amdgpu_buffer_rsrc_t rx = rsrc(xblk, (int64_t)mrows * a.K);
 
     // ---- 1. staging: parameter bytes and (few tokens) activation rows go
     // straight from memory to LDS, exact counts, issued before the weights.
-    // The copies are asynchronous; the barrier below waits for them (and for
-    // the weight prologue issued meanwhile, which arrives at the same time).
+    // The copies are the buffer form of the direct-to-LDS load: the compiler
+    // adds no wait for them before LDS reads, so the counted wait below
+    // decides, and the weights issued after them are not waited for.
     for (int ch = wv; ch < praw_bytes / 256; ch += WAVES) {
         const int o = ch * 256 + 4 * l;                   // byte offset in [NT][nq*64]
         const int t = o / (nq * 64);
         const int r = o - t * (nq * 64);
         const int tt = min(nt0 + min(t, NT - 1), ntiles - 1);
-        const uint8_t *src = a.params + ((int64_t)tt * (G4 / 4) + q0) * 64 + (t < NT ? r : 0);
-        __builtin_amdgcn_global_load_lds(src, praw + ch * 256, 4, 0, 0);
+        lds_copy4(rp, praw + ch * 256, (tt * (G4 / 4) + q0) * 64 + (t < NT ? r : 0));
     }
     if constexpr (XS) {
         const int xbytes = mrows * xstride;
@@ -164,8 +133,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
             const int row = o / xstride;
             const int col = o - row * xstride;
             const bool ok = row < mrows && col < span * kGroup;
-            const int8_t *src = xblk + (ok ? (int64_t)row * K + gbase * kGroup + col : 0);
-            __builtin_amdgcn_global_load_lds(src, xlds + ch * 1024, 16, 0, 0);
+            lds_copy16(rx, xlds + ch * 1024, ok ? row * K + gbase * kGroup + col : 0);
         }
     }
     // epilogue scales of this wave's first output tile (waves without a tile skip them)
@@ -179,13 +147,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
         sa_e = a.s_a[m_e];
         s0_e = *reinterpret_cast<const uint2 *>(a.s0 + n_e);
     }
+    __builtin_amdgcn_sched_barrier(0);    // all of the above is issued before the weights
 
     // ---- 2. the weight stream: DEPTH pairs in flight per wave -----------------
     int vw[NT];                         // per-lane byte offset of each tile's stream
 #pragma unroll
     for (int t = 0; t < NT; t++)
         vw[t] = min(nt0 + t, ntiles - 1) * G * kTileBytes + 16 * l;
-    const __amdgpu_buffer_rsrc_t rx = rsrc(xblk, (int64_t)mrows * a.K);
     int vx[XS ? 1 : MT];                // per-lane offset of the activation operand row
 #pragma unroll
     for (int mt = 0; mt < (XS ? 1 : MT); mt++)
@@ -217,9 +185,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
         load(ring[u], pw0 + max(min(u, npairs - 1), 0));
 
     // ---- 3. decode the group parameters, zero the reduction buffer -----------
+    // Loads retire in order: once no more than the weight prologue is
+    // outstanding, this thread's staging copies and scale loads have landed
+    // (the count is capped at the counter's 6-bit range, which waits longer).
+    constexpr int kPrologue = DEPTH * 2 * (NT + (XS ? 0 : 2 * MT));
     for (int i = tid; i < NT * MT * 256; i += kThreads)
         red[i] = 0;
-    __syncthreads();                    // staging copies have landed
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPrologue < 63 ? kPrologue : 63) : "memory");
+    lds_barrier();                      // staging copies have landed
     for (int e = tid; e < NT * span * 16; e += kThreads) {
         const int t = e / (span * 16);
         const int rem = e - t * span * 16;
@@ -228,7 +201,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
         const uint32_t dw = reinterpret_cast<const uint32_t *>(praw)[(t * nq + (g / 4 - q0)) * 16 + cch];
         ptab[e] = decode_param((dw >> (8 * (g & 3))) & 0xFFu);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- 4. main loop ----------------------------------------------------------
     v4i acc[NT][MT];
@@ -272,14 +245,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
                 const unsigned short c16 = (unsigned short)(sc >> 16);
                 const us2 S = {s1, s1};
                 const us2 C = {c16, c16};
-                const v4i w = ch.w[t][j];
                 v4i f0, f1;
-#pragma unroll
-                for (int d = 0; d < 4; d++) {
-                    const uint32_t x = (uint32_t)w[d];
-                    f0[d] = (int)rebuild4(x & 0x0F0F0F0Fu, S, C);
-                    f1[d] = (int)rebuild4((x >> 4) & 0x0F0F0F0Fu, S, C);
-                }
+                rebuild_tile(ch.w[t][j], S, C, f0, f1);
 #pragma unroll
                 for (int mt = 0; mt < MT; mt++) {
                     acc[t][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f0, xf[mt][0], acc[t][mt], 0, 0, 0);
@@ -328,6 +295,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
     __syncthreads();
 
     const int64_t tile_id = (int64_t)blockIdx.z * gridDim.x + blockIdx.x;
+    SplitTile st;
+    st.part = a.ws_part + tile_id * a.splitk * (256 * MT * NT);
+    st.cnt = a.ws_cnt + tile_id;
+    st.splitk = a.splitk;
+    st.slot_elems = 256 * MT * NT;
+    st.row_stride = 16 * NT;
+    st.m0 = m0;
+    st.n0 = (int64_t)nt0 * kTileN;
+    st.rows = mrows;
+    st.cols = (int)min<int64_t>(NT * kTileN, a.N - st.n0);
     for (int i = wv; i < NT * MT; i += WAVES) {
         const int t = i / MT;
         const int mt = i - t * MT;
@@ -341,79 +318,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
             continue;
         if (a.splitk > 1) {
             // this split's partial: row 16 mt + c, columns 16 t + 4 kb .. + 3
-            int32_t *slot = a.ws_part + (tile_id * a.splitk + blockIdx.y) * (256 * MT * NT);
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                slot, (short)0, 256 * MT * NT * 4, kBufFlags);
-            __builtin_amdgcn_raw_buffer_store_b128(sum, rs, ((16 * mt + c) * 16 * NT + 16 * t + 4 * kb) * 4, 0, 16);
+            splitk_store(st, blockIdx.y, 16 * mt + c, 16 * t + 4 * kb, sum);
         } else {
             const float sa = (i == i0) ? sa_e : a.s_a[m];
             const uint2 s0p = (i == i0) ? s0_e : *reinterpret_cast<const uint2 *>(a.s0 + n);
-            const uint32_t s0w[2] = {s0p.x, s0p.y};
-            uint32_t out[2];
-#pragma unroll
-            for (int r = 0; r < 4; r += 2) {
-                float v0 = ((float)sum[r] * sa) * (float)__builtin_bit_cast(_Float16, (uint16_t)(s0w[r / 2] & 0xFFFF));
-                float v1 = ((float)sum[r + 1] * sa) * (float)__builtin_bit_cast(_Float16, (uint16_t)(s0w[r / 2] >> 16));
-                uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)v0);
-                uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)v1);
-                out[r / 2] = h0 | (h1 << 16);
-            }
-            *reinterpret_cast<uint2 *>(a.y + m * a.N + n) = make_uint2(out[0], out[1]);
-            if (a.acc_out)
-                *reinterpret_cast<v4i *>(a.acc_out + m * a.N + n) = sum;
+            store_out4(sum, sa, s0p, a.y, a.acc_out, m, n, a.N);
         }
     }
-    if (a.splitk <= 1)
-        return;
-
     // ---- 6. split-K: the last workgroup of the tile applies the epilogue -------
-    // Each split stores its partial tile into its own slot with agent-coherent
-    // (sc1) stores, which bypass the XCD's L2, so no cache writeback or
-    // invalidate is needed (an agent-scope fence would write back and
-    // invalidate the whole L2 of the XCD in every workgroup).  Ordering: each
-    // wave waits until its stores are acknowledged before the barrier, the
-    // counter increment is issued after the barrier, and the last arriver's
-    // sc1 loads of the other slots are issued after it has seen the final
-    // count.  It then resets the counter; the slots are scratch.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    __shared__ uint32_t arrival;
-    if (tid == 0)
-        arrival = __hip_atomic_fetch_add(a.ws_cnt + tile_id, 1u, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (arrival != (uint32_t)(a.splitk - 1))
-        return;
-    const int ncols = (int)min<int64_t>(NT * kTileN, a.N - (int64_t)nt0 * kTileN);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        a.ws_part + tile_id * a.splitk * (256 * MT * NT), (short)0, a.splitk * 256 * MT * NT * 4, kBufFlags);
-    for (int i = tid; i < mrows * ncols / 4; i += kThreads) {
-        const int r = i / (ncols / 4);
-        const int q = i - r * (ncols / 4);
-        const int64_t m = m0 + r;
-        const int64_t n = (int64_t)nt0 * kTileN + 4 * q;
-        v4i sum = {0, 0, 0, 0};
-        for (int sp = 0; sp < a.splitk; sp++)
-            sum += __builtin_amdgcn_raw_buffer_load_b128(rs, (r * 16 * NT + 4 * q) * 4,
-                                                        sp * (256 * MT * NT * 4), 16);
-        const float sa = a.s_a[m];
-        const uint2 s0p = *reinterpret_cast<const uint2 *>(a.s0 + n);
-        const uint32_t s0w[2] = {s0p.x, s0p.y};
-        uint32_t out[2];
-#pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-            float v0 = ((float)sum[e] * sa) * (float)__builtin_bit_cast(_Float16, (uint16_t)(s0w[e / 2] & 0xFFFF));
-            float v1 = ((float)sum[e + 1] * sa) * (float)__builtin_bit_cast(_Float16, (uint16_t)(s0w[e / 2] >> 16));
-            uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)v0);
-            uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)v1);
-            out[e / 2] = h0 | (h1 << 16);
-        }
-        *reinterpret_cast<uint2 *>(a.y + m * a.N + n) = make_uint2(out[0], out[1]);
-        if (a.acc_out)
-            *reinterpret_cast<v4i *>(a.acc_out + m * a.N + n) = sum;
-    }
-    if (tid == 0)
-        __hip_atomic_store(a.ws_cnt + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.splitk > 1)
+        splitk_finish<kThreads>(st, a.s_a, a.s0, a.y, a.acc_out, a.N, tid);
 }
 
 template <int MT, int NT, int WAVES, int DEPTH, bool XS>
@@ -505,7 +419,7 @@ int decode_candidates(int64_t M, int64_t N, int64_t K, GemmPlan *out, int max)
                     p.waves = 4;
                     p.depth = dp;
                     p.xstage = true;
-                    p.wave_n = true;
+                    p.wave_n = 1;
                     p.m_blocks = (M + 16 * mt - 1) / (16 * mt);
                     p.n_blocks = (ntiles + p.nt - 1) / p.nt;
                     if (s > 1 && p.m_blocks * p.n_blocks > kWsCounters)

@@ -25,60 +25,17 @@
 // counter per tile, the last arriver sums the slots in split order.
 #include <algorithm>
 
-#include "w4a8_internal.h"
+#include "kernel_common.h"
 
 namespace w4a8 {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+using namespace dev;
 
-constexpr int kBufFlags = 0x00020000;   // raw buffer resource, dword 3 (gfx9 family)
-constexpr int kLoadNT = 2;              // non-temporal (streaming) load policy
 constexpr int kWaves = 4;
 constexpr int kWin = 2;                 // group pairs per activation window: 512 bytes per row
 constexpr int kRowBytes = 2 * kWin * kGroup;
 constexpr int kRowChunks = kRowBytes / 16;
-
-__device__ inline uint32_t rebuild4(uint32_t nib, us2 S, us2 C)
-{
-    us2 v = __builtin_bit_cast(us2, nib);
-    v = v * S + C;
-    return __builtin_bit_cast(uint32_t, v) ^ 0x80808080u;
-}
-
-__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *p, int64_t bytes)
-{
-    const int64_t lim = bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)lim, kBufFlags);
-}
-
-// A workgroup barrier that waits only for this wave's LDS operations:
-// __syncthreads() would also wait for every outstanding global load, i.e.
-// drain the weight ring at each window.  Callers first wait (counted vmcnt)
-// for their own direct-to-LDS copies that the barrier must publish.
-__device__ inline void lds_barrier()
-{
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// direct-to-LDS copies of 16 and 4 bytes per lane, buffer form (see the kernel)
-__device__ inline void lds_copy16(const __amdgpu_buffer_rsrc_t &r, void *dst, int voff)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, 0, 0, 0);
-}
-
-__device__ inline void lds_copy4(const __amdgpu_buffer_rsrc_t &r, void *dst, int voff)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 4, voff, 0, 0, 0);
-}
-
-__device__ inline uint32_t decode_param(uint32_t p)
-{
-    const uint32_t s1 = (p & 15u) + 1u;
-    const uint32_t c16 = ((128u - (p >> 4) * s1) * 257u) & 0xFFFFu;
-    return s1 | (c16 << 16);
-}
 
 struct NsArgs {
     const int8_t *qx;
@@ -232,14 +189,8 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_decode_ns_kernel(NsArgs a)
                 const uint32_t sc = ptab[((wv * NTW + t) * span + gw) * 16 + c];
                 const us2 S = {(unsigned short)(sc & 0xFFFFu), (unsigned short)(sc & 0xFFFFu)};
                 const us2 C = {(unsigned short)(sc >> 16), (unsigned short)(sc >> 16)};
-                const v4i w = slot[t][j];
                 v4i f0, f1;
-#pragma unroll
-                for (int d = 0; d < 4; d++) {
-                    const uint32_t x = (uint32_t)w[d];
-                    f0[d] = (int)rebuild4(x & 0x0F0F0F0Fu, S, C);
-                    f1[d] = (int)rebuild4((x >> 4) & 0x0F0F0F0Fu, S, C);
-                }
+                rebuild_tile(slot[t][j], S, C, f0, f1);
 #pragma unroll
                 for (int mt = 0; mt < MT; mt++) {
                     acc[t][mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f0, xf[mt][0], acc[t][mt], 0, 0, 0);
@@ -273,6 +224,16 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_decode_ns_kernel(NsArgs a)
 
     // ---- 3. outputs: each wave's own tiles ---------------------------------------
     const int64_t tile_id = (int64_t)blockIdx.z * gridDim.x + blockIdx.x;
+    SplitTile st;
+    st.part = a.ws_part + tile_id * a.splitk * (256 * MT * NT);
+    st.cnt = a.ws_cnt + tile_id;
+    st.splitk = a.splitk;
+    st.slot_elems = 256 * MT * NT;
+    st.row_stride = 16 * NT;
+    st.m0 = m0;
+    st.n0 = (int64_t)nt0 * kTileN;
+    st.rows = mrows;
+    st.cols = (int)min<int64_t>(NT * kTileN, a.N - st.n0);
 #pragma unroll
     for (int t = 0; t < NTW; t++) {
 #pragma unroll
@@ -282,73 +243,16 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_decode_ns_kernel(NsArgs a)
             const int64_t n = (int64_t)(nt0 + tt) * kTileN + 4 * kb;
             if (nt0 + tt >= ntiles || m >= a.M)
                 continue;
-            const v4i sum = acc[t][mt];
-            if (a.splitk > 1) {
-                int32_t *slot = a.ws_part + (tile_id * a.splitk + blockIdx.y) * (256 * MT * NT);
-                const __amdgpu_buffer_rsrc_t rs =
-                    __builtin_amdgcn_make_buffer_rsrc(slot, (short)0, 256 * MT * NT * 4, kBufFlags);
-                __builtin_amdgcn_raw_buffer_store_b128(sum, rs, ((16 * mt + c) * 16 * NT + 16 * tt + 4 * kb) * 4, 0,
-                                                       16);
-            } else {
-                const float sa = a.s_a[m];
-                const uint2 s0p = *reinterpret_cast<const uint2 *>(a.s0 + n);
-                const uint32_t s0w[2] = {s0p.x, s0p.y};
-                uint32_t out[2];
-#pragma unroll
-                for (int r = 0; r < 4; r += 2) {
-                    const float v0 = ((float)sum[r] * sa) *
-                                     (float)__builtin_bit_cast(_Float16, (uint16_t)(s0w[r / 2] & 0xFFFF));
-                    const float v1 = ((float)sum[r + 1] * sa) *
-                                     (float)__builtin_bit_cast(_Float16, (uint16_t)(s0w[r / 2] >> 16));
-                    out[r / 2] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v0) |
-                                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v1) << 16);
-                }
-                *reinterpret_cast<uint2 *>(a.y + m * a.N + n) = make_uint2(out[0], out[1]);
-                if (a.acc_out)
-                    *reinterpret_cast<v4i *>(a.acc_out + m * a.N + n) = sum;
-            }
+            if (a.splitk > 1)
+                splitk_store(st, blockIdx.y, 16 * mt + c, 16 * tt + 4 * kb, acc[t][mt]);
+            else
+                store_out4(acc[t][mt], a.s_a[m], *reinterpret_cast<const uint2 *>(a.s0 + n), a.y, a.acc_out, m, n,
+                           a.N);
         }
     }
-    if (a.splitk <= 1)
-        return;
-
     // ---- 4. split-K: the last workgroup of the tile applies the epilogue -------
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    __shared__ uint32_t arrival;
-    if (tid == 0)
-        arrival = __hip_atomic_fetch_add(a.ws_cnt + tile_id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (arrival != (uint32_t)(a.splitk - 1))
-        return;
-    const int ncols = (int)min<int64_t>(NT * kTileN, a.N - (int64_t)nt0 * kTileN);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        a.ws_part + tile_id * a.splitk * (256 * MT * NT), (short)0, a.splitk * 256 * MT * NT * 4, kBufFlags);
-    for (int i = tid; i < mrows * ncols / 4; i += 64 * kWaves) {
-        const int r = i / (ncols / 4);
-        const int q = i - r * (ncols / 4);
-        const int64_t m = m0 + r;
-        const int64_t n = (int64_t)nt0 * kTileN + 4 * q;
-        v4i sum = {0, 0, 0, 0};
-        for (int sp = 0; sp < a.splitk; sp++)
-            sum += __builtin_amdgcn_raw_buffer_load_b128(rs, (r * 16 * NT + 4 * q) * 4, sp * (256 * MT * NT * 4), 16);
-        const float sa = a.s_a[m];
-        const uint2 s0p = *reinterpret_cast<const uint2 *>(a.s0 + n);
-        const uint32_t s0w[2] = {s0p.x, s0p.y};
-        uint32_t out[2];
-#pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-            const float v0 = ((float)sum[e] * sa) * (float)__builtin_bit_cast(_Float16, (uint16_t)(s0w[e / 2] & 0xFFFF));
-            const float v1 = ((float)sum[e + 1] * sa) * (float)__builtin_bit_cast(_Float16, (uint16_t)(s0w[e / 2] >> 16));
-            out[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v0) |
-                         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v1) << 16);
-        }
-        *reinterpret_cast<uint2 *>(a.y + m * a.N + n) = make_uint2(out[0], out[1]);
-        if (a.acc_out)
-            *reinterpret_cast<v4i *>(a.acc_out + m * a.N + n) = sum;
-    }
-    if (tid == 0)
-        __hip_atomic_store(a.ws_cnt + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.splitk > 1)
+        splitk_finish<64 * kWaves>(st, a.s_a, a.s0, a.y, a.acc_out, a.N, tid);
 }
 
 template <int MT, int NTW, int DEPTH>

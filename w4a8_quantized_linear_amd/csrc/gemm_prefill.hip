@@ -52,7 +52,7 @@
 // m-blocks by several n-blocks and share both operands in that XCD's L2.
 #include <algorithm>
 
-#include "w4a8_internal.h"
+#include "kernel_common.h"
 
 namespace w4a8 {
 namespace {
@@ -60,7 +60,8 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBufFlags = 0x00020000;   // raw buffer resource, dword 3 (gfx9 family)
+using dev::kBufFlags;
+using dev::rsrc;
 constexpr int kXcds = 8;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -86,12 +87,6 @@ struct Cfg {
     static_assert(BM <= kThreads, "one token scale per thread");
     static_assert((BM / 2) * (BN * 2 + 16) <= kAStages * kAStage, "output half-tile fits in the stages");
 };
-
-__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *p, int64_t bytes)
-{
-    const int64_t lim = bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)lim, kBufFlags);
-}
 
 // byte offset of 16-byte chunk `ch` (0..7) of activation row `row` (128-byte rows)
 __device__ inline int swz(int row, int ch) { return row * 128 + ((ch ^ ((row >> 1) & 7)) << 4); }

@@ -34,7 +34,7 @@
 #include <algorithm>
 #include <cstdlib>
 
-#include "w4a8_internal.h"
+#include "kernel_common.h"
 
 namespace w4a8 {
 namespace {
@@ -45,15 +45,10 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBufFlags = 0x00020000;   // raw buffer resource, dword 3 (gfx9 family)
+using dev::kBufFlags;
+using dev::rsrc;
 constexpr int kWaves = 4;
 constexpr int kDepth = 4;                // groups of loads in flight per wave
-
-__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *p, int64_t bytes)
-{
-    const int64_t lim = bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)lim, kBufFlags);
-}
 
 // four biased bytes u = r + 128 (k order) -> two fp16 pairs r
 __device__ inline void to_half(uint32_t u, uint32_t &lo, uint32_t &hi)

@@ -49,7 +49,7 @@
 #include <algorithm>
 #include <cmath>
 
-#include "w4a8_internal.h"
+#include "kernel_common.h"
 
 namespace w4a8 {
 namespace {
@@ -273,14 +273,10 @@ __device__ inline int seq_len(const AttnArgs &a, int64_t b)
     return L < 0 ? 0 : (int)std::min<int64_t>(L, a.S);
 }
 
-constexpr int kBufFlags = 0x00020000;   // raw buffer resource, dword 3 (gfx9 family)
-
-// a buffer resource over [p, p + bytes): the chunk's rows, addressed with
-// 32-bit offsets from a scalar base (no per-load 64-bit address arithmetic)
-__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *p, int bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, kBufFlags);
-}
+// buffer resources over the chunk's rows, addressed with 32-bit offsets from a
+// scalar base (no per-load 64-bit address arithmetic)
+using dev::kBufFlags;
+using dev::rsrc;
 
 #ifndef KV4_ATTN_WAVES
 #define KV4_ATTN_WAVES 4

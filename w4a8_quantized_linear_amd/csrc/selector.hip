@@ -63,7 +63,7 @@ void selector_features(const GemmPlan &p, int64_t M, int64_t N, int64_t K, int64
     x[9] = (float)std::log2(wgs / (double)cus);
     x[10] = (float)std::log2(G / (double)p.splitk);
     x[11] = (float)((double)M / (16.0 * (double)p.mt * (double)p.m_blocks));
-    x[12] = p.wave_n ? 1.0f : 0.0f;
+    x[12] = (float)p.wave_n;
 }
 
 float selector_predict(const float *x)
@@ -93,7 +93,7 @@ float selector_predict(const float *x)
 }
 
 // Whether the model has seen N-split plans (else they are not ranked).
-bool selector_knows_wave_n() { return kModel.trained >= 2; }
+bool selector_knows_wave_n(int wave_n) { return wave_n == 0 || (wave_n == 1 && kModel.trained >= 2); }
 
 // On when a model is compiled in, unless W4A8_SELECTOR=0.
 bool selector_enabled()

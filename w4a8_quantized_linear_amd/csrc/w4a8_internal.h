@@ -118,7 +118,8 @@ struct GemmPlan {
     int waves;       // waves per workgroup, splitting the slice (decode)
     int depth;       // pairs of groups in flight per wave (decode)
     bool xstage;     // activation rows staged in LDS (decode, few tokens)
-    bool wave_n;     // decode: the waves split the n-tiles (gemm_decode_ns.hip), not K
+    int wave_n;      // decode kernel: 0 waves split K (gemm_decode.hip); 1 waves split the
+                     // n-tiles, activations in LDS windows (gemm_decode_ns.hip)
     int64_t m_blocks;
     int64_t n_blocks;
     size_t ws_bytes; // workspace needed (0 if none)
@@ -148,7 +149,7 @@ constexpr float kSelMargin = 0.0f;
 void selector_features(const GemmPlan &p, int64_t M, int64_t N, int64_t K, int64_t cus, float *x);
 float selector_predict(const float *x);      // predicted fraction of HBM peak; < 0: no model
 bool selector_enabled();
-bool selector_knows_wave_n();
+bool selector_knows_wave_n(int wave_n);   // the model was trained on plans of this kernel
 
 // compute units of the current device (256 when it cannot be queried)
 int64_t num_cus();
@@ -159,7 +160,7 @@ int64_t num_cus();
 GemmPlan plan_without_workspace(GemmPlan p, int64_t M, int64_t N, int64_t K);
 
 // Dynamic LDS bytes per workgroup that launching the plan requests.
-size_t plan_lds_bytes(const GemmPlan &p, int64_t M, int64_t K);
+size_t plan_lds_bytes(const GemmPlan &p, int64_t M, int64_t N, int64_t K);
 
 // Raise a kernel's dynamic-LDS limit on the current device to `bytes`, once
 // per (kernel, device); safe to call from several host threads.

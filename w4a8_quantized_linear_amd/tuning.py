@@ -72,7 +72,7 @@ def graph_time(call, reps, replays=3):
     return e0.elapsed_time(e1) * 1e3 / (replays * reps)
 
 
-def measure(shapes, tag, writer, reps=10):
+def measure(shapes, tag, writer, reps=10, wave_n=None):
     import torch
 
     from w4a8_quantized_linear_amd import (accounting as A, gemm_w4a8, gemm_w4a8_decode_candidates,
@@ -93,6 +93,8 @@ def measure(shapes, tag, writer, reps=10):
         rules_t = tuple(rules[f] for f in ("mt", "nt", "splitk", "waves", "depth", "xstage", "wave_n"))
         nbytes = A.gemm_bytes(M, N, K)
         for c in gemm_w4a8_decode_candidates(M, N, K):
+            if wave_n is not None and c[6] != wave_n:
+                continue
             os.environ["W4A8_DECODE_PLAN"] = ",".join(str(v) for v in c)
             got = gemm_w4a8_plan(M, N, K)
             if tuple(got[f] for f in ("mt", "nt", "splitk", "waves", "depth", "xstage", "wave_n")) != c:
@@ -143,6 +145,12 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--eval", action="store_true")
     ap.add_argument("--compare", action="store_true")
+    ap.add_argument("--wave-n", type=int, default=None,
+                    help="time only the candidates of this decode kernel family (0, 1, 2)")
+    ap.add_argument("--shapes-from", default=None,
+                    help="time the (M, N, K) shapes of an earlier sweep's CSV (M <= --max-m)")
+    ap.add_argument("--max-m", type=int, default=64)
+    ap.add_argument("--part", default="0/1", help="i/n: time every n-th shape from the i-th (to split a sweep)")
     args = ap.parse_args(argv)
     if args.compare:
         shapes = EVAL_SHAPES + [(M, 11008, 4096) for M in (1, 8, 16, 32, 64)]
@@ -152,10 +160,17 @@ def main(argv=None):
             compare(shapes, w)
         return 0
     shapes = EVAL_SHAPES if args.eval else random_shapes(args.shapes, args.seed)
+    if args.shapes_from:
+        import gzip
+        with (gzip.open(args.shapes_from, "rt") if args.shapes_from.endswith(".gz") else open(args.shapes_from)) as f:
+            shapes = sorted({(int(r["M"]), int(r["N"]), int(r["K"])) for r in csv.DictReader(f)})
+    shapes = [s for s in shapes if s[0] <= args.max_m]
+    part, nparts = (int(v) for v in args.part.split("/"))
+    shapes = shapes[part::nparts]
     with open(args.out, "w", newline="") as f:
         w = csv.writer(f)
         w.writerow(FIELDS)
-        measure(shapes, "eval" if args.eval else "train", w)
+        measure(shapes, "eval" if args.eval else "train", w, wave_n=args.wave_n)
     return 0
 
 
