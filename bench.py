@@ -249,20 +249,21 @@ def bench_configs(args):
     """Every shape of the five workload configurations: the GEMM (and for the
     prefill configuration the activation quantizer before it) timed as HIP-graph
     replays, weights rotated through 1 GiB of copies so that their bytes come
-    from HBM, beside the streaming-read ceiling of the same weight bytes.  The
-    weights are random packed bytes (every byte is a valid code pair and group
-    parameter; the kernels' timing does not depend on the values); the
-    parity tests cover the seeded weights of each configuration."""
+    from HBM, beside the streaming-read ceiling of the same weight bytes.
+    Inputs follow each configuration's recipe, drawn on the GPU from a seeded
+    generator (the full-size host draws of the parity tests take far longer):
+    weights N(0, 0.02) -- Student-t(4) scaled to the same spread for the
+    heavy-tailed configuration -- quantized by quantize_weights_w4g128;
+    activations N(0, 1) with the configuration's outlier channels scaled up,
+    quantized per token."""
     import torch
 
     from w4a8_quantized_linear_amd import (_lib, accounting as A, gemm_w4a8, quantize_act_per_token_i8,
-                                           w4a8_packed_weight_bytes, workloads as W)
+                                           quantize_weights_w4g128, workloads as W)
     from w4a8_quantized_linear_amd._lib import w4a8_hbm_read
     from w4a8_quantized_linear_amd.tuning import graph_time
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
-    gen.manual_seed(0x57A8)
-    pool = torch.randint(0, 256, (ROTATE_BYTES,), dtype=torch.uint8, device=dev, generator=gen)
     sink = torch.zeros(64, dtype=torch.int32, device=dev)
     reps = max(10, args.reps // 2)
     hbm, ops_peak = A.MI355X_HBM_BYTES_PER_S, A.MI355X_INT8_OPS_PER_S
@@ -270,14 +271,24 @@ def bench_configs(args):
     out = []
     for fam in W.FAMILIES:
         for (K, N) in fam.kns:
-            wb = w4a8_packed_weight_bytes(N, K)
-            stride = (wb + 4095) // 4096 * 4096
-            views = [pool[i * stride:i * stride + wb] for i in range(max(2, min(64, ROTATE_BYTES // stride)))]
-            s0 = (torch.rand(N, device=dev, generator=gen) * 1e-3).half()
+            gen.manual_seed(0x57A8 * 1000 + fam.index * 100 + K % 97 + N % 89)
+            w = torch.randn((N, K), device=dev, generator=gen)
+            if fam.w_dist == "student_t4":     # z / sqrt(chi2_4 / 4), then the population std sqrt(2) out
+                chi2 = sum(torch.randn((N, K), device=dev, generator=gen) ** 2 for _ in range(4))
+                w = w / torch.sqrt(chi2 / 4) / math.sqrt(2.0)
+            wq = quantize_weights_w4g128((w * 0.02).float().contiguous(), canonical=False)
+            del w
+            wb = wq["wpacked"].numel()
+            views = [wq["wpacked"]] + [wq["wpacked"].clone() for _ in range(max(2, math.ceil(ROTATE_BYTES / wb)) - 1)]
+            s0 = wq["s0"]
             cus = graph_time(lambda r: w4a8_hbm_read(views[r % len(views)], sink), reps)
+            n_out = int(round(0.01 * K)) if fam.n_outlier < 0 else fam.n_outlier
+            outl = torch.randperm(K, device=dev, generator=gen)[:n_out]
             for M in fam.ms:
-                qx = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev, generator=gen)
-                sa = torch.rand(M, device=dev, generator=gen) * 1e-2
+                x = torch.randn((M, K), device=dev, generator=gen)
+                x[:, outl] *= fam.outlier_scale
+                x = x.half()
+                qx, sa = quantize_act_per_token_i8(x)
                 y = torch.empty((M, N), dtype=torch.float16, device=dev)
                 ws = _lib.workspace(dev, _lib.gemm_w4a8_workspace_bytes(M, N, K))
                 us = graph_time(lambda r: gemm_w4a8(qx, sa, views[r % len(views)], s0, N, y=y, ws=ws), reps)
@@ -290,17 +301,15 @@ def bench_configs(args):
                        "ceiling_us": round(cus, 3), "ceiling_frac": round(cus / us, 4)}
                 if fam.index == 3:
                     # prefill: the activation quantizer is part of the timed work
-                    x = (torch.randn((M, K), device=dev, generator=gen) * 2).half()
                     aus = graph_time(lambda r: quantize_act_per_token_i8(x, qx=qx, s_a=sa), reps)
                     tot = aus + us
                     rec.update({"act_quant_us": round(aus, 3), "total_us": round(tot, 3),
                                 "total_TOPS": round(ops / tot * 1e-6, 2),
                                 "total_mfma_frac": round(ops / tot * 1e-6 / (ops_peak / 1e12), 4)})
-                    del x
                 out.append(rec)
-                del qx, sa, y
-    del pool
-    torch.cuda.empty_cache()
+                del x, qx, sa, y
+            del views, wq
+            torch.cuda.empty_cache()
     return out
 
 

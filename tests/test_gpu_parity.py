@@ -83,13 +83,41 @@ def test_act_quant_edges_and_row_stride():
     quantize_act_per_token_i8(e)
 
 
+@pytest.mark.parametrize("waves", ["1", "4"])
+@pytest.mark.parametrize("M,K", [(2048, 4096), (1100, 11008), (4096, 1152)])
+def test_act_quant_both_layouts(waves, M, K):
+    """The two register layouts of the quantizer -- one wave per token (rows
+    held by one wave, tokens walked with a row prefetch) and four waves per
+    token -- forced in turn, on rows with outlier channels, exact ties and a
+    zero row, bit-exact against the oracle."""
+    from w4a8_quantized_linear_amd import quantize_act_per_token_i8
+    say("act quant layout waves=%s M=%d K=%d" % (waves, M, K))
+    x = workloads.activations(1, M, K, 4096)
+    x[3] = 0
+    x[5, :8] = [127, -63.5, 31.25, 0.5, -0.5, 1.5, -127, 2.5]
+    x[5, 8:] = 0
+    old = os.environ.get("W4A8_ACT_WAVES")
+    os.environ["W4A8_ACT_WAVES"] = waves
+    try:
+        qx, sa = quantize_act_per_token_i8(to_dev(x))
+        qx_h, sa_h = to_host(qx), to_host(sa)
+    finally:
+        if old is None:
+            os.environ.pop("W4A8_ACT_WAVES", None)
+        else:
+            os.environ["W4A8_ACT_WAVES"] = old
+    qx_ref, sa_ref = orc.quantize_act(x)
+    assert np.array_equal(sa_h.view(np.uint32), sa_ref.view(np.uint32))
+    assert np.array_equal(qx_h, qx_ref)
+
+
 @pytest.mark.parametrize("M", [64, 1100])
 def test_act_quant_every_half_value(M):
     """Each row holds every finite fp16 value up to its absmax (the rest 0),
     under scales that make exact ties (absmax 127, 63.5, 254: s_a = 1, 0.5, 2)
     and random ones: every quotient the division can meet for that scale,
     including those within rounding distance of a half-integer.  M spans the
-    four-waves-per-token and one-wave-per-token layouts."""
+    launch shapes of the four-waves-per-token layout the row length needs."""
     from w4a8_quantized_linear_amd import quantize_act_per_token_i8
     bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
     vals = bits.view(np.float16)

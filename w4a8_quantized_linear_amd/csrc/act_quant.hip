@@ -394,12 +394,15 @@ hipError_t launch(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int8_t *
 {
     if (M == 0)
         return hipSuccess;
-    // Few tokens, or rows too long for one wave's registers: four waves per
-    // token.  Otherwise one wave per token.  From four tokens per slot on,
-    // each slot walks its tokens with the row prefetch (two slots per SIMD,
-    // one if the two row buffers take more than half its registers); below
-    // that every token gets a slot of its own (timed faster on MI355X at
-    // 4096 tokens of 4096).  W4A8_ACT_SLOTS=n overrides the slot count,
+    // The plain quantizer: four waves per token, every token its own slot up
+    // to 16 slots per compute unit, beyond that each slot walks its tokens with
+    // the row prefetch (timed on MI355X: at 4096 tokens four waves per token
+    // beat one wave by 10% at K = 4096 and 23% at K = 11008, and were never
+    // slower up to 16384 tokens or K = 28672).  The fused normalization keeps
+    // one wave per token from 1024 tokens on, unless its rows are too long for
+    // one wave's registers; from four tokens per slot on, each slot walks its
+    // tokens (two slots per SIMD, one if the two row buffers take more than
+    // half its registers).  W4A8_ACT_SLOTS=n overrides the slot count,
     // W4A8_ACT_WAVES=1|4 the waves per token.
     int64_t slots = 0;
     if (const char *env = std::getenv("W4A8_ACT_SLOTS"))
@@ -408,12 +411,12 @@ hipError_t launch(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int8_t *
     // (the normalizing variant holds at most 16 chunks per lane in registers:
     // with 24 its two row buffers no longer fit and go to scratch)
     const bool wide = (K / 8 + 63) / 64 > (na ? 16 : 24);
-    int waves = M < 1024 || wide ? 4 : 1;
+    int waves = M < 1024 || wide || !na ? 4 : 1;
     if (const char *env = std::getenv("W4A8_ACT_WAVES"))   // 1 or 4 (sweeps; 1 only where it fits)
         waves = std::atoi(env) == 4 || wide ? 4 : (std::atoi(env) == 1 ? 1 : waves);
     if (waves == 4) {
         if (slots <= 0)
-            slots = M >= 4 * cus ? 2 * cus : M;
+            slots = !na ? std::min<int64_t>(M, 16 * cus) : (M >= 4 * cus ? 2 * cus : M);
         return launch_w<4>(x, M, K, ldx, qx, s_a, std::min(slots, M), na, st);
     }
     if (slots <= 0) {

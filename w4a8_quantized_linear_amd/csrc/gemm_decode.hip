@@ -22,7 +22,13 @@
 // operands for more tokens are loaded with the weights instead).  Weight
 // tiles are read with 16-byte buffer loads (scalar base and offset, one
 // per-lane offset register) DEPTH pairs ahead of use; every load is
-// unconditional, so the compiler's vmcnt waits are exact.  Each 16-byte lane
+// unconditional, so the compiler's vmcnt waits are exact.  An unstaged
+// activation operand is the 16 bytes of row c at k-block kb, four lanes per
+// row 16 lanes apart: as loaded, the 64 lanes touch 16 rows in 64 separate
+// cache accesses.  With more than 8 tokens the lanes instead load the block
+// row by row (lane 4 r + q takes row r, 16-byte piece q, so four neighbouring
+// lanes read 64 contiguous bytes) and ds_bpermute hands each lane the piece
+// its MFMA position needs, four dwords per operand.  Each 16-byte lane
 // load is the operand pair of two v_mfma_i32_16x16x64_i8 (the device layout
 // puts the codes in that order): mask/shift, one packed 16-bit multiply-add
 // and one xor per 4 weights, then the MFMA with the weights as the A operand
@@ -34,6 +40,7 @@
 // (kernel_common.h, splitk_finish).  The packed rebuild and its byte-lane
 // arithmetic are described at rebuild4 in kernel_common.h.
 #include <algorithm>
+#include <cstdlib>
 
 #include "kernel_common.h"
 
@@ -56,6 +63,7 @@ struct DecodeArgs {
     int32_t *acc_out;
     int32_t *ws_part;    // split-K partial tiles: slot (tile, split) of 16 MT x 16 NT int32
     uint32_t *ws_cnt;    // one arrival counter per (m-block, n-block)
+    int cx;             // unstaged activation operands: row-contiguous loads, lanes exchanged
 };
 
 // One ring slot: the loads of one pair of groups (2 x 128 k).
@@ -157,7 +165,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
     int vx[XS ? 1 : MT];                // per-lane offset of the activation operand row
 #pragma unroll
     for (int mt = 0; mt < (XS ? 1 : MT); mt++)
-        vx[mt] = min(16 * mt + c, mrows - 1) * K + 16 * kb;
+        vx[mt] = a.cx ? min(16 * mt + (l >> 2), mrows - 1) * K + 16 * (l & 3)
+                      : min(16 * mt + c, mrows - 1) * K + 16 * kb;
+    const int xsrc = 4 * (4 * c + kb);      // cx: the lane that loaded this lane's operand
 
     auto load = [&](Chunk<MT, NT, XS> &ch, int pr) {
 #pragma unroll
@@ -231,6 +241,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
                     xf[mt][0] = *reinterpret_cast<const v4i *>(xrow[mt] + gr * kGroup);
                     xf[mt][1] = *reinterpret_cast<const v4i *>(xrow[mt] + gr * kGroup + 64);
                 }
+            } else if (a.cx) {
+#pragma unroll
+                for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+                    for (int h = 0; h < 2; h++)
+#pragma unroll
+                        for (int d = 0; d < 4; d++)
+                            xf[mt][h][d] = __builtin_amdgcn_ds_bpermute(xsrc, ch.x[mt][j][h][d]);
             } else {
 #pragma unroll
                 for (int mt = 0; mt < MT; mt++) {
@@ -477,6 +495,12 @@ hipError_t launch_gemm_decode(const GemmPlan &p, const int8_t *qx, const float *
         a.ws_cnt = reinterpret_cast<uint32_t *>(ws);
         a.ws_part = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(ws) + kWsPartOffset);
     }
+    // row-contiguous activation loads pay off from nine tokens on (below,
+    // half the lanes of a block repeat the last row); W4A8_DECODE_CX=0|1
+    // overrides, for sweeps
+    a.cx = M > 8;
+    if (const char *env = std::getenv("W4A8_DECODE_CX"))
+        a.cx = std::atoi(env) != 0;
     const size_t lds = decode_lds_bytes(p, M, K);
     if (lds == 0 || lds > kDecodeLdsMax)
         return hipErrorInvalidValue;

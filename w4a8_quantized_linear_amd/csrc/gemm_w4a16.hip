@@ -31,6 +31,11 @@
 // weight tiles, parameter dwords and activation operands DEPTH groups ahead
 // (unconditional loads, so the compiler's vmcnt waits are exact).  The four
 // partial sums meet in LDS and are added in wave order (deterministic).
+// For a few tokens (XS) the workgroup first copies its tokens' fp16 rows
+// into LDS (direct-to-LDS loads, 16-byte row pad) and the waves read their
+// activation operands there: the weight tile is then the only vector-memory
+// load of a group, where four 16-byte activation loads per group would keep
+// the texture units busier than the weight stream does.
 #include <algorithm>
 #include <cstdlib>
 
@@ -65,6 +70,7 @@ struct W16Args {
     const uint16_t *s0;       // [N] fp16
     int64_t M, N, K, ldx;
     uint16_t *y;              // [M, N] fp16
+    int cx;                   // activation operands loaded row-contiguous, lanes exchanged
 };
 
 template <int NT>
@@ -74,10 +80,11 @@ struct Slot {
     v4i x[4];                 // activation operands of the group's four MFMAs
 };
 
-template <int NT>
+template <int NT, bool XS>
 __global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
 {
     __shared__ f4 red[kWaves][NT][64];
+    extern __shared__ __align__(16) uint8_t xsm[];   // XS: fp16 rows [mrows][2 K + 16]
     const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int l = threadIdx.x & 63, lr = l & 15, kb = l >> 4;
     const int nt0 = blockIdx.x * NT;                  // first 16-channel tile
@@ -95,21 +102,47 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
 #pragma unroll
     for (int t = 0; t < NT; t++)
         tile[t] = min(nt0 + t, ntiles - 1);
-    const int64_t row = min<int64_t>(m0 + lr, a.M - 1);
-    const int xoff = (int)(row * a.ldx * 2) + 32 * kb;    // bytes: token row, k-block
+    // an operand's 16 bytes for lane (lr, kb): token row lr, k-block kb.  With
+    // cx the lanes load the block row by row instead (lane 4 r + q: row r,
+    // k-block q, so four neighbouring lanes read one row's 128-byte line)
+    // and ds_bpermute gives lane (lr, kb) the piece lane 4 lr + kb loaded
+    const int64_t row = min<int64_t>(m0 + (a.cx ? l >> 2 : lr), a.M - 1);
+    const int xoff = (int)(row * a.ldx * 2) + 32 * (a.cx ? l & 3 : kb);    // bytes: token row, k-block
+    const int xsrc = 4 * (4 * lr + kb);
     const int glast = max(g1 - 1, g0);
+    const int len = g1 - g0;
 
-    auto load = [&](Slot<NT> &s, int g) {
-        g = min(g, glast);
+    // XS: the block's token rows go straight into LDS (buffer form of the
+    // direct-to-LDS load, counted below), issued before the weight prologue
+    const int mrows = (int)min<int64_t>(16, a.M - m0);
+    const int xstride = 2 * (int)a.K + 16;
+    if constexpr (XS) {
+        const int nch = (mrows * xstride + 1023) / 1024;
+        for (int ch = wv; ch < nch; ch += kWaves) {
+            const int o = ch * 1024 + 16 * l;
+            const int r = o / xstride;
+            const int col = o - r * xstride;
+            const bool ok = r < mrows && col < 2 * (int)a.K;
+            dev::lds_copy16(rx, xsm + ch * 1024, ok ? (int)((m0 + r) * a.ldx * 2) + col : 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const int8_t *xrow = reinterpret_cast<const int8_t *>(xsm) + min(lr, mrows - 1) * xstride + 32 * kb;
+
+    auto load = [&](Slot<NT> &s, int i) {
+        const int g = min(g0 + i, glast);
 #pragma unroll
         for (int t = 0; t < NT; t++) {
             s.w[t] = __builtin_amdgcn_raw_buffer_load_b128(rw, 16 * l, ((int64_t)tile[t] * G + g) * kTileBytes, 2);
             s.p[t] = __builtin_amdgcn_raw_buffer_load_b32(rp, (int)(param_index(tile[t] * 16 + lr, g, G4) & ~3),
                                                           0, 0);
         }
+        if constexpr (!XS) {
 #pragma unroll
-        for (int q = 0; q < 4; q++)
-            s.x[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff, g * 256 + 2 * (8 * (q & 1) + 64 * (q >> 1)), 0);
+            for (int q = 0; q < 4; q++)
+                s.x[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff, g * 256 + 2 * (8 * (q & 1) + 64 * (q >> 1)),
+                                                               0);
+        }
     };
 
     f4 acc[NT];
@@ -120,9 +153,27 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
     Slot<NT> ring[kDepth];
 #pragma unroll
     for (int d = 0; d < kDepth; d++)
-        load(ring[d], g0 + d);
+        load(ring[d], d);
+    if constexpr (XS) {
+        // loads retire in order: once only the weight prologue is
+        // outstanding, this thread's row copies have landed
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDepth * 2 * NT) : "memory");
+        dev::lds_barrier();
+    }
 
-    auto step = [&](Slot<NT> &s, int g) {
+    auto step = [&](Slot<NT> &s, int i) {
+        const int g = g0 + i;
+        if constexpr (XS) {
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                s.x[q] = *reinterpret_cast<const v4i *>(xrow + g * 256 + 2 * (8 * (q & 1) + 64 * (q >> 1)));
+        } else if (a.cx) {
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+#pragma unroll
+                for (int d = 0; d < 4; d++)
+                    s.x[q][d] = __builtin_amdgcn_ds_bpermute(xsrc, s.x[q][d]);
+        }
 #pragma unroll
         for (int t = 0; t < NT; t++) {
             const uint32_t pb = (s.p[t] >> (8 * (g & 3))) & 0xFFu;
@@ -148,19 +199,19 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
                                                                 __builtin_bit_cast(h8, bw), acc[t], 0, 0, 0);
             }
         }
-        load(s, g + kDepth);
+        load(s, i + kDepth);
     };
 
-    int g = g0;
-    for (; g + kDepth <= g1; g += kDepth) {
+    int i = 0;
+    for (; i + kDepth <= len; i += kDepth) {
 #pragma unroll
         for (int d = 0; d < kDepth; d++)
-            step(ring[d], g + d);
+            step(ring[d], i + d);
     }
 #pragma unroll
     for (int d = 0; d < kDepth - 1; d++)
-        if (g + d < g1)
-            step(ring[d], g + d);
+        if (i + d < len)
+            step(ring[d], i + d);
 
     // the waves' partial sums, added in wave order; lane l holds tokens
     // 4 (l / 16) + r, channel l % 16 of each tile
@@ -189,12 +240,29 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
     }
 }
 
-template <int NT>
+// LDS of the staged token rows (0 when they do not fit the 64 KB that keeps
+// several workgroups per compute unit)
+inline size_t w16_xs_bytes(int64_t M, int64_t K)
+{
+    const int64_t b = (std::min<int64_t>(16, M) * (2 * K + 16) + 1023) / 1024 * 1024;
+    return b <= 64 * 1024 ? (size_t)b : 0;
+}
+
+template <int NT, bool XS>
 hipError_t launch_nt(const W16Args &a, hipStream_t st)
 {
     const int64_t nblk = (a.N / kTileN + NT - 1) / NT;
     const int64_t mblk = (a.M + 15) / 16;
-    hipLaunchKernelGGL(gemm_w4a16_kernel<NT>, dim3((unsigned)nblk, (unsigned)mblk), dim3(64 * kWaves), 0, st, a);
+    const size_t lds = XS ? w16_xs_bytes(a.M, a.K) : 0;
+    if constexpr (XS) {
+        // staged rows plus the reduction array pass the 64 KB default
+        const hipError_t e =
+            raise_lds_limit(reinterpret_cast<const void *>(&gemm_w4a16_kernel<NT, XS>), 80 * 1024);
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL((gemm_w4a16_kernel<NT, XS>), dim3((unsigned)nblk, (unsigned)mblk), dim3(64 * kWaves), lds, st,
+                       a);
     return hipGetLastError();
 }
 
@@ -236,10 +304,30 @@ hipError_t launch_gemm_w4a16(const uint16_t *x, int64_t M, int64_t K, int64_t ld
         a.K = K;
         a.ldx = ldx;
         a.y = y + r0 * N;
-        int nt = pick_nt(a.M, N);
+        // staged rows for up to 4 tokens on wide layers (>= 512 tiles) when
+        // they fit, one tile per workgroup.  Measured on MI355X, M = 1: K =
+        // 4096, N = 11008 8.0 us against 9.9 for the best register form; K =
+        // 8192, N = 28672 24.1 against 28.9.  With 256 tiles the register
+        // form is 2-10% faster (fewer workgroups hide less of the staging),
+        // and at 8 and more tokens the two are within 3%.
+        // W4A8_W16_XS=0|1 and W4A8_W16_NT=1|2|4 override, for sweeps
+        bool xs = a.M <= 4 && N / kTileN >= 512 && w16_xs_bytes(a.M, K) > 0;
+        if (const char *env = std::getenv("W4A8_W16_XS"))
+            xs = std::atoi(env) != 0 && w16_xs_bytes(a.M, K) > 0;
+        int nt = xs ? 1 : pick_nt(a.M, N);
+        // row-contiguous activation loads from 8 tokens on (measured on
+        // MI355X, K = 4096, N = 11008: M = 32 17.5 us against 20.6; M = 8 11.0
+        // against 11.1; below 8 tokens up to 9% slower); W4A8_W16_CX=0|1
+        // overrides, for sweeps
+        a.cx = a.M >= 8;
+        if (const char *env = std::getenv("W4A8_W16_CX"))
+            a.cx = std::atoi(env) != 0;
         if (const char *env = std::getenv("W4A8_W16_NT"))
             nt = std::atoi(env) == 4 ? 4 : (std::atoi(env) == 2 ? 2 : (std::atoi(env) == 1 ? 1 : nt));
-        const hipError_t e = nt == 4 ? launch_nt<4>(a, st) : (nt == 2 ? launch_nt<2>(a, st) : launch_nt<1>(a, st));
+        const hipError_t e = xs ? (nt == 4 ? launch_nt<4, true>(a, st)
+                                           : (nt == 2 ? launch_nt<2, true>(a, st) : launch_nt<1, true>(a, st)))
+                                : (nt == 4 ? launch_nt<4, false>(a, st)
+                                           : (nt == 2 ? launch_nt<2, false>(a, st) : launch_nt<1, false>(a, st)));
         if (e != hipSuccess)
             return e;
     }

@@ -17,6 +17,10 @@ held-out set).  --compare re-times, on those shapes and the 7B MLP shape
 (W4A8_SELECTOR=0 versus the compiled-in model), interleaved, 50 calls per
 graph, three rounds, medians.  Needs a GPU; the weights are random bytes (every byte is a
 valid code pair and group parameter), timing does not depend on the values.
+
+--launch M1,M2,..  --n N --k K [--calls C] makes C eager calls per token count with the
+plan gemm_w4a8 picks (rotating weight copies, as above) and prints the plans: the
+program that profiler runs (rocprofv3 --pmc ...) trace for the decode counters.
 """
 from __future__ import annotations
 
@@ -138,9 +142,35 @@ def compare(shapes, writer, reps=50, rounds=3):
         print("compared M=%d N=%d K=%d rules %.2f us selector %.2f us" % (M, N, K, tr, ts), flush=True)
 
 
+def launch(ms, N, K, calls):
+    """`calls` eager gemm_w4a8 calls per token count, weights rotated past the caches."""
+    import torch
+    from w4a8_quantized_linear_amd import _lib, gemm_w4a8, w4a8_packed_weight_bytes
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    nbytes = w4a8_packed_weight_bytes(N, K)
+    nrot = max(2, math.ceil((1 << 30) / nbytes))
+    wbuf = torch.randint(0, 256, (nrot, nbytes), dtype=torch.uint8, device=dev, generator=g)
+    s0 = torch.full((N,), 0.01, dtype=torch.float16, device=dev)
+    ws = _lib.workspace(dev, max(_lib.gemm_w4a8_workspace_bytes(M, N, K) for M in ms))
+    for M in ms:
+        qx = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev, generator=g)
+        sa = torch.full((M,), 0.01, dtype=torch.float32, device=dev)
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        print("M=%d N=%d K=%d plan %s" % (M, N, K, _lib.gemm_w4a8_plan_detail(M, N, K)), flush=True)
+        for c in range(calls):
+            gemm_w4a8(qx, sa, wbuf[c % nrot], s0, N, y=y, ws=ws)
+        torch.cuda.synchronize()
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("out")
+    ap.add_argument("out", nargs="?")
+    ap.add_argument("--launch", default=None, help="M1,M2,..: eager calls of the chosen plan (profiler runs)")
+    ap.add_argument("--n", type=int, default=11008)
+    ap.add_argument("--k", type=int, default=4096)
+    ap.add_argument("--calls", type=int, default=30)
     ap.add_argument("--shapes", type=int, default=120)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--eval", action="store_true")
@@ -152,6 +182,11 @@ def main(argv=None):
     ap.add_argument("--max-m", type=int, default=64)
     ap.add_argument("--part", default="0/1", help="i/n: time every n-th shape from the i-th (to split a sweep)")
     args = ap.parse_args(argv)
+    if args.launch:
+        launch([int(v) for v in args.launch.split(",")], args.n, args.k, args.calls)
+        return 0
+    if args.out is None:
+        ap.error("the output CSV is required")
     if args.compare:
         shapes = EVAL_SHAPES + [(M, 11008, 4096) for M in (1, 8, 16, 32, 64)]
         with open(args.out, "w", newline="") as f:
