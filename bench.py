@@ -315,6 +315,7 @@ def bench_configs(args):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_w4a8_m4096_k4096_n11008.txt")
 TRAFFIC_SOURCES = ("w4a8_quantized_linear_amd/csrc/gemm_prefill.hip",
+                   "w4a8_quantized_linear_amd/csrc/kernel_common.h",
                    "w4a8_quantized_linear_amd/csrc/dispatch.hip")
 
 
