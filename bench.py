@@ -230,6 +230,7 @@ def main():
                              "GBps": round(wbytes / ceil_us * 1e-3, 1),
                              "kernel": "w4a8_hbm_read (the weight stream read once, nothing computed)"},
         "per_m": per_m,
+        "targets": targets(per_m, configs),
         "configs": configs,
         "norm_quant": norm_quant,
         "w4a16": w4a16,
@@ -243,6 +244,27 @@ def main():
         kv4["cpu_baseline"] = cpu_baseline_kv4()
 
     print(json.dumps(out), flush=True)
+
+
+DECODE_HBM_TARGET = 0.70     # fraction of 8 TB/s for the decode GEMM at M <= 32
+PREFILL_MFMA_TARGET = 0.50   # fraction of 5.0 POPS for the prefill GEMM at M = 4096
+
+
+def targets(per_m, configs):
+    """The two performance bars of the path, and the measured rows that fall short
+    of them, stated in the output next to the figures (met: every row reaches it)."""
+    rows = configs if configs else [dict(r, K=K_DIM, N=N_DIM) for r in per_m]
+    dec = [r for r in rows if r["M"] <= 32]
+    pre = [r for r in rows if r["M"] == 4096]
+    dec_below = [{"M": r["M"], "K": r["K"], "N": r["N"], "hbm_frac": r["hbm_frac"],
+                  "ceiling_frac": r.get("ceiling_frac")} for r in dec if r["hbm_frac"] < DECODE_HBM_TARGET]
+    pre_below = [{"M": r["M"], "K": r["K"], "N": r["N"], "mfma_frac": r["mfma_frac"],
+                  "with_act_quant": r.get("total_mfma_frac")}
+                 for r in pre if min(r["mfma_frac"], r.get("total_mfma_frac", 1.0)) < PREFILL_MFMA_TARGET]
+    return {"decode_hbm_frac": DECODE_HBM_TARGET, "decode_met": not dec_below,
+            "decode_rows": len(dec), "decode_rows_below": dec_below,
+            "prefill_mfma_frac": PREFILL_MFMA_TARGET, "prefill_met": not pre_below,
+            "prefill_rows": len(pre), "prefill_rows_below": pre_below}
 
 
 def bench_configs(args):
