@@ -13,13 +13,15 @@
 // channels, up to MT m-tiles of 16 tokens, and one K slice (split-K across
 // workgroups is optional).  The waves split the slice into runs of group
 // pairs.  At the start every thread issues its share of the small loads --
-// the slice's group-parameter bytes, the epilogue scales and, for few
-// tokens, the tokens' activation rows -- then the first DEPTH pairs of its
-// wave's weight tiles, and only then stores the small data into LDS: the
-// group parameters pre-decoded into the two 16-bit constants the rebuild
-// needs, and the activation rows.  So the weight stream starts at once and
-// its loads are the only vector-memory traffic of the main loop (activation
-// operands for more tokens are loaded with the weights instead).  Weight
+// the epilogue scales and, for few tokens, the tokens' activation rows,
+// copied straight into LDS -- then the first DEPTH pairs of its wave's
+// weight tiles.  Each pair's group-parameter dword (four groups of the lane's
+// channel) is loaded with the pair's weights and decoded in registers, so no
+// workgroup waits for a parameter table before its first MFMA: a table staged
+// in LDS had put an HBM round trip and two barriers in front of every
+// workgroup's main loop, and all workgroups of a decode launch run that
+// prologue at the same time.  Activation operands for more tokens are loaded
+// with the weights as well.  Weight
 // tiles are read with 16-byte buffer loads (scalar base and offset, one
 // per-lane offset register) DEPTH pairs ahead of use; every load is
 // unconditional, so the compiler's vmcnt waits are exact.  An unstaged
@@ -70,6 +72,7 @@ struct DecodeArgs {
 template <int MT, int NT, bool XS>
 struct Chunk {
     v4i w[NT][2];                    // weight operands: 16 B per lane per (n-tile, group)
+    uint32_t p[NT];                  // parameter dword of the lane's channel (four groups)
     v4i x[XS ? 1 : MT][2][2];        // activation operands when not staged in LDS
 };
 
@@ -105,35 +108,22 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
     const int gbase = 2 * ps0;                          // first group of the slice
     const int span = min(2 * (ps1 - ps0), G - gbase);   // groups in the slice
 
-    // LDS: reduction [NT*MT][4][64] int32 | decoded params [NT][span][16] u32 |
-    // raw parameter dwords [NT][nq][16] | activation rows [mrows][span*128 + 16]
-    // (the two staging areas are rounded up to whole copy chunks)
-    const int q0 = gbase / 4;
-    const int nq = max((gbase + span + 3) / 4 - q0, 1);
+    // LDS: reduction [NT*MT][4][64] int32 | activation rows [mrows][span*128 + 16]
+    // (rounded up to whole copy chunks)
     const int xstride = span * kGroup + 16;
     int32_t *red = reinterpret_cast<int32_t *>(smem);
-    uint32_t *ptab = reinterpret_cast<uint32_t *>(smem + NT * MT * 1024);
-    uint8_t *praw = smem + NT * MT * 1024 + NT * span * 64;
-    const int praw_bytes = (NT * nq * 64 + 255) / 256 * 256;
-    int8_t *xlds = reinterpret_cast<int8_t *>(praw + praw_bytes);
+    int8_t *xlds = reinterpret_cast<int8_t *>(smem + NT * MT * 1024);
 
     const __amdgpu_buffer_rsrc_t rw = rsrc(a.codes, code_bytes(a.N, a.K));
     const __amdgpu_buffer_rsrc_t rp = rsrc(a.params, param_bytes(a.N, a.K));
     const int8_t *xblk = a.qx + m0 * a.K;     // this block's first token row
     const __amdgpu_buffer_rsrc_t rx = rsrc(xblk, (int64_t)mrows * a.K);
 
-    // ---- 1. staging: parameter bytes and (few tokens) activation rows go
-    // straight from memory to LDS, exact counts, issued before the weights.
-    // The copies are the buffer form of the direct-to-LDS load: the compiler
-    // adds no wait for them before LDS reads, so the counted wait below
-    // decides, and the weights issued after them are not waited for.
-    for (int ch = wv; ch < praw_bytes / 256; ch += WAVES) {
-        const int o = ch * 256 + 4 * l;                   // byte offset in [NT][nq*64]
-        const int t = o / (nq * 64);
-        const int r = o - t * (nq * 64);
-        const int tt = min(nt0 + min(t, NT - 1), ntiles - 1);
-        lds_copy4(rp, praw + ch * 256, (tt * (G4 / 4) + q0) * 64 + (t < NT ? r : 0));
-    }
+    // ---- 1. staging: (few tokens) the activation rows go straight from
+    // memory to LDS, exact counts, issued before the weights.  The copies are
+    // the buffer form of the direct-to-LDS load: the compiler adds no wait for
+    // them before LDS reads, so the counted wait below decides, and the
+    // weights issued after them are not waited for.
     if constexpr (XS) {
         const int xbytes = mrows * xstride;
         for (int ch = wv; ch < (xbytes + 1023) / 1024; ch += WAVES) {
@@ -159,9 +149,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
 
     // ---- 2. the weight stream: DEPTH pairs in flight per wave -----------------
     int vw[NT];                         // per-lane byte offset of each tile's stream
+    int vp[NT];                         // ... and of its parameter dwords (channel c)
 #pragma unroll
-    for (int t = 0; t < NT; t++)
+    for (int t = 0; t < NT; t++) {
         vw[t] = min(nt0 + t, ntiles - 1) * G * kTileBytes + 16 * l;
+        vp[t] = min(nt0 + t, ntiles - 1) * (G4 / 4) * 64 + 4 * c;
+    }
     int vx[XS ? 1 : MT];                // per-lane offset of the activation operand row
 #pragma unroll
     for (int mt = 0; mt < (XS ? 1 : MT); mt++)
@@ -169,7 +162,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
                       : min(16 * mt + c, mrows - 1) * K + 16 * kb;
     const int xsrc = 4 * (4 * c + kb);      // cx: the lane that loaded this lane's operand
 
+    // a pair's parameter bytes ride with its weights: both groups of a pair
+    // are in one dword (four groups per dword, pairs start at even groups)
     auto load = [&](Chunk<MT, NT, XS> &ch, int pr) {
+        const int q = sgpr(min(2 * pr, G - 1) >> 2);
+#pragma unroll
+        for (int t = 0; t < NT; t++)
+            ch.p[t] = __builtin_amdgcn_raw_buffer_load_b32(rp, vp[t], q * 64, 0);
 #pragma unroll
         for (int j = 0; j < 2; j++) {
             const int g = sgpr(min(2 * pr + j, G - 1));
@@ -194,24 +193,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
     for (int u = 0; u < DEPTH; u++)
         load(ring[u], pw0 + max(min(u, npairs - 1), 0));
 
-    // ---- 3. decode the group parameters, zero the reduction buffer -----------
+    // ---- 3. zero the reduction buffer; with staged rows, wait for them ------
     // Loads retire in order: once no more than the weight prologue is
     // outstanding, this thread's staging copies and scale loads have landed
     // (the count is capped at the counter's 6-bit range, which waits longer).
-    constexpr int kPrologue = DEPTH * 2 * (NT + (XS ? 0 : 2 * MT));
+    constexpr int kPrologue = DEPTH * (3 * NT + (XS ? 0 : 4 * MT));
     for (int i = tid; i < NT * MT * 256; i += kThreads)
         red[i] = 0;
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPrologue < 63 ? kPrologue : 63) : "memory");
-    lds_barrier();                      // staging copies have landed
-    for (int e = tid; e < NT * span * 16; e += kThreads) {
-        const int t = e / (span * 16);
-        const int rem = e - t * span * 16;
-        const int g = rem / 16 + gbase;                  // absolute group
-        const int cch = rem - (rem / 16) * 16;
-        const uint32_t dw = reinterpret_cast<const uint32_t *>(praw)[(t * nq + (g / 4 - q0)) * 16 + cch];
-        ptab[e] = decode_param((dw >> (8 * (g & 3))) & 0xFFu);
-    }
-    lds_barrier();
+    if constexpr (XS)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPrologue < 63 ? kPrologue : 63) : "memory");
+    lds_barrier();                      // zeroed; staging copies have landed
 
     // ---- 4. main loop ----------------------------------------------------------
     v4i acc[NT][MT];
@@ -258,7 +249,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(DecodeArgs a)
             }
 #pragma unroll
             for (int t = 0; t < NT; t++) {
-                const uint32_t sc = ptab[(t * span + gr) * 16 + c];
+                const uint32_t sc = decode_param((ch.p[t] >> (8 * (g & 3))) & 0xFFu);
                 const unsigned short s1 = (unsigned short)(sc & 0xFFFFu);
                 const unsigned short c16 = (unsigned short)(sc >> 16);
                 const us2 S = {s1, s1};
@@ -457,16 +448,13 @@ size_t decode_lds_bytes(const GemmPlan &p, int64_t M, int64_t K)
 {
     const int64_t G = num_groups(K);
     const int64_t P = (G + 1) / 2;
-    int64_t span = 0, nq = 0;
+    int64_t span = 0;
     for (int s = 0; s < p.splitk; s++) {
         const int64_t ps0 = P * s / p.splitk, ps1 = P * (s + 1) / p.splitk;
-        const int64_t sp = std::min<int64_t>(2 * (ps1 - ps0), G - 2 * ps0);
-        span = std::max(span, sp);
-        nq = std::max<int64_t>(nq, std::max<int64_t>((2 * ps0 + sp + 3) / 4 - (2 * ps0) / 4, 1));
+        span = std::max(span, std::min<int64_t>(2 * (ps1 - ps0), G - 2 * ps0));
     }
     const int64_t rows = std::min<int64_t>(16 * p.mt, M);
-    int64_t bytes = (int64_t)p.nt * p.mt * 1024 + (int64_t)p.nt * span * 64 +
-                    ((int64_t)p.nt * nq * 64 + 255) / 256 * 256;
+    int64_t bytes = (int64_t)p.nt * p.mt * 1024;
     if (p.xstage)
         bytes += (rows * (span * kGroup + 16) + 1023) / 1024 * 1024;
     return (size_t)bytes;

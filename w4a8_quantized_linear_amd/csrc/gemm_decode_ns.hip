@@ -18,8 +18,8 @@
 //  * a window row is stored with its 16-byte chunks XOR-swizzled by the row
 //    (chunk k of row r at chunk k ^ (r & 15)), so the 16 token rows a wave
 //    reads at one k land in 16 different bank groups.
-// The decoded group parameters of the slice stay in LDS ([NT][span][16]), so
-// long K slices need split-K to fit; plans are filtered by their LDS size.
+// Each pair's group-parameter dword (four groups of the lane's channel) rides
+// in the weight ring next to the pair's codes and is decoded in registers.
 // Split-K across workgroups uses the workspace protocol of gemm_decode.hip:
 // per-split partial tiles stored with agent-coherent stores, an arrival
 // counter per tile, the last arriver sums the slots in split order.
@@ -51,12 +51,8 @@ struct NsArgs {
     uint32_t *ws_cnt;
 };
 
-// LDS bytes: two windows, the decoded parameters [NT][span][16] and the raw
-// parameter dwords [NT][nq][16] (rounded to whole 256-byte copies)
-__host__ __device__ inline int ns_lds_bytes(int MT, int NT, int span, int nq)
-{
-    return 2 * 16 * MT * kRowBytes + NT * span * 64 + (NT * nq * 64 + 255) / 256 * 256;
-}
+// LDS bytes: two activation windows
+__host__ __device__ inline int ns_lds_bytes(int MT) { return 2 * 16 * MT * kRowBytes; }
 
 template <int MT, int NTW, int DEPTH>
 __global__ __launch_bounds__(64 * kWaves) void gemm_decode_ns_kernel(NsArgs a)
@@ -85,15 +81,8 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_decode_ns_kernel(NsArgs a)
     const int ps0 = (int)((uint32_t)P * blockIdx.y / (uint32_t)a.splitk);
     const int ps1 = (int)((uint32_t)P * (blockIdx.y + 1) / (uint32_t)a.splitk);
     const int npairs = ps1 - ps0;
-    const int gbase = 2 * ps0;
-    const int span = min(2 * npairs, G - gbase);
-    const int q0 = gbase / 4;
-    const int nq = max((gbase + span + 3) / 4 - q0, 1);
 
     int8_t *win = reinterpret_cast<int8_t *>(smem);
-    uint32_t *ptab = reinterpret_cast<uint32_t *>(smem + 2 * kWinBytes);
-    uint8_t *praw = smem + 2 * kWinBytes + NT * span * 64;
-    const int praw_bytes = (NT * nq * 64 + 255) / 256 * 256;
 
     const __amdgpu_buffer_rsrc_t rw = rsrc(a.codes, code_bytes(a.N, a.K));
     const __amdgpu_buffer_rsrc_t rp = rsrc(a.params, param_bytes(a.N, a.K));
@@ -118,23 +107,23 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_decode_ns_kernel(NsArgs a)
         }
     };
 
-    // ---- 1. staging: parameter bytes, the first window, the weight prologue
-    for (int ch = wv; ch < praw_bytes / 256; ch += kWaves) {
-        const int o = ch * 256 + 4 * l;
-        const int t = o / (nq * 64);
-        const int r = o - t * (nq * 64);
-        const int tt = min(nt0 + min(t, NT - 1), ntiles - 1);
-        lds_copy4(rp, praw + ch * 256, (tt * (G4 / 4) + q0) * 64 + (t < NT ? r : 0));
-    }
+    // ---- 1. staging: the first window, then the weight prologue
     window_copy(0, 0);
     __builtin_amdgcn_sched_barrier(0);    // the copies stay ahead of the weight prologue
 
-    int vw[NTW];
+    int vw[NTW], vp[NTW];
 #pragma unroll
-    for (int t = 0; t < NTW; t++)
+    for (int t = 0; t < NTW; t++) {
         vw[t] = min(nt0 + wv * NTW + t, ntiles - 1) * G * kTileBytes + 16 * l;
+        vp[t] = min(nt0 + wv * NTW + t, ntiles - 1) * (G4 / 4) * 64 + 4 * c;
+    }
     v4i ring[DEPTH][NTW][2];
-    auto load = [&](v4i (&slot)[NTW][2], int pr) {
+    uint32_t pring[DEPTH][NTW];       // the pairs' parameter dwords (both groups of a pair in one)
+    auto load = [&](v4i (&slot)[NTW][2], uint32_t (&ps)[NTW], int pr) {
+        const int q = __builtin_amdgcn_readfirstlane(min(2 * pr, G - 1) >> 2);
+#pragma unroll
+        for (int t = 0; t < NTW; t++)
+            ps[t] = __builtin_amdgcn_raw_buffer_load_b32(rp, vp[t], q * 64, 0);
 #pragma unroll
         for (int j = 0; j < 2; j++) {
             const int g = __builtin_amdgcn_readfirstlane(min(2 * pr + j, G - 1));
@@ -145,20 +134,11 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_decode_ns_kernel(NsArgs a)
     };
 #pragma unroll
     for (int u = 0; u < DEPTH; u++)
-        load(ring[u], min(ps0 + u, ps1 - 1));
+        load(ring[u], pring[u], min(ps0 + u, ps1 - 1));
 
-    // this thread's parameter and window copies were issued before its weight
-    // prologue: they have landed once only the prologue is outstanding
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DEPTH * NTW * 2) : "memory");
-    lds_barrier();
-    for (int e = tid; e < NT * span * 16; e += 64 * kWaves) {
-        const int t = e / (span * 16);
-        const int rem = e - t * span * 16;
-        const int g = rem / 16 + gbase;
-        const int cch = rem - (rem / 16) * 16;
-        const uint32_t dw = reinterpret_cast<const uint32_t *>(praw)[(t * nq + (g / 4 - q0)) * 16 + cch];
-        ptab[e] = decode_param((dw >> (8 * (g & 3))) & 0xFFu);
-    }
+    // this thread's window copies were issued before its weight prologue:
+    // they have landed once only the prologue is outstanding
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DEPTH * NTW * 3) : "memory");
     lds_barrier();
 
     // ---- 2. main loop: windows of kWin pairs ---------------------------------
@@ -169,7 +149,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_decode_ns_kernel(NsArgs a)
         for (int mt = 0; mt < MT; mt++)
             acc[t][mt] = v4i{0, 0, 0, 0};
 
-    auto compute = [&](const v4i (&slot)[NTW][2], int pr, const int8_t *wbuf) {
+    auto compute = [&](const v4i (&slot)[NTW][2], const uint32_t (&ps)[NTW], int pr, const int8_t *wbuf) {
 #pragma unroll
         for (int j = 0; j < 2; j++) {
             const int g = 2 * pr + j;
@@ -186,7 +166,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_decode_ns_kernel(NsArgs a)
             }
 #pragma unroll
             for (int t = 0; t < NTW; t++) {
-                const uint32_t sc = ptab[((wv * NTW + t) * span + gw) * 16 + c];
+                const uint32_t sc = decode_param((ps[t] >> (8 * (g & 3))) & 0xFFu);
                 const us2 S = {(unsigned short)(sc & 0xFFFFu), (unsigned short)(sc & 0xFFFFu)};
                 const us2 C = {(unsigned short)(sc >> 16), (unsigned short)(sc >> 16)};
                 v4i f0, f1;
@@ -213,12 +193,12 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_decode_ns_kernel(NsArgs a)
         for (int u = 0; u < kWin; u++) {
             const int pr = ps0 + j * kWin + u;
             if (pr < ps1)
-                compute(ring[u % DEPTH], pr, wbuf);
-            load(ring[u % DEPTH], min(pr + DEPTH, ps1 - 1));
+                compute(ring[u % DEPTH], pring[u % DEPTH], pr, wbuf);
+            load(ring[u % DEPTH], pring[u % DEPTH], min(pr + DEPTH, ps1 - 1));
         }
         // window j + 1 (issued before this window's refills) has landed once
-        // only the last DEPTH pairs of weights are outstanding
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DEPTH * NTW * 2) : "memory");
+        // only the last DEPTH pairs of weights and parameters are outstanding
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DEPTH * NTW * 3) : "memory");
         lds_barrier();
     }
 
@@ -285,16 +265,8 @@ bool decode_ns_variant_exists(int mt, int ntw, int depth)
 
 size_t decode_ns_lds_bytes(const GemmPlan &p, int64_t K)
 {
-    const int64_t G = num_groups(K);
-    const int64_t P = (G + 1) / 2;
-    int64_t span = 0, nq = 0;
-    for (int s = 0; s < p.splitk; s++) {
-        const int64_t ps0 = P * s / p.splitk, ps1 = P * (s + 1) / p.splitk;
-        const int64_t sp = std::min<int64_t>(2 * (ps1 - ps0), G - 2 * ps0);
-        span = std::max(span, sp);
-        nq = std::max<int64_t>(nq, std::max<int64_t>((2 * ps0 + sp + 3) / 4 - (2 * ps0) / 4, 1));
-    }
-    return (size_t)ns_lds_bytes(p.mt, p.nt, (int)span, (int)nq);
+    (void)K;
+    return (size_t)ns_lds_bytes(p.mt);
 }
 
 hipError_t launch_gemm_decode_ns(const GemmPlan &p, const int8_t *qx, const float *s_a, const uint8_t *stream_bytes,

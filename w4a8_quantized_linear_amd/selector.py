@@ -145,15 +145,34 @@ def load_model(path_json=JSON):
     return {k: np.asarray(v, np.float64) for k, v in d.items()}
 
 
+def _train_seed(job):
+    path, seed = job
+    _, cols, X = load(path)
+    return train(X, cols["util"], seed=seed)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("train")
     ap.add_argument("--eval")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--seeds", type=int, default=1,
+                    help="train seeds seed .. seed + n - 1 in parallel and keep the one whose picks on the "
+                         "training set are closest to the best measured plans")
     ap.add_argument("--no-export", action="store_true")
     args = ap.parse_args(argv)
     rows, cols, X = load(args.train)
-    model = train(X, cols["util"], seed=args.seed)
+    if args.seeds > 1:
+        import concurrent.futures as cf
+        seeds = list(range(args.seed, args.seed + args.seeds))
+        with cf.ProcessPoolExecutor(max_workers=min(len(seeds), os.cpu_count() or 1)) as ex:
+            models = list(ex.map(_train_seed, [(args.train, sd) for sd in seeds]))
+        scores = [pick_report(m, rows, cols, X)[0]["model_over_best"] for m in models]
+        for sd, sc in zip(seeds, scores):
+            print("seed %d: training-set picks %.4f x the best" % (sd, sc))
+        model = models[int(np.argmin(scores))]
+    else:
+        model = train(X, cols["util"], seed=args.seed)
     pred = predict(model, X)
     print("train rows %d  rmse %.4f" % (len(rows), float(np.sqrt(np.mean((pred - cols["util"]) ** 2)))))
     print("train", pick_report(model, rows, cols, X)[0])
