@@ -54,6 +54,7 @@ using dev::kBufFlags;
 using dev::rsrc;
 constexpr int kWaves = 4;
 constexpr int kDepth = 4;                // groups of loads in flight per wave
+static_assert(kDepth == 4, "ring slot d holds the groups d mod 4 of a run: one parameter dword per slot-0 group");
 
 // four biased bytes u = r + 128 (k order) -> two fp16 pairs r
 __device__ inline void to_half(uint32_t u, uint32_t &lo, uint32_t &hi)
@@ -91,7 +92,10 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
     const int ntiles = (int)(a.N / kTileN);
     const int64_t m0 = (int64_t)blockIdx.y * 16;
     const int G = (int)(a.K / kGroup), G4 = (int)groups_padded(a.K);
-    const int g0 = (int)((int64_t)G * wv / kWaves), g1 = (int)((int64_t)G * (wv + 1) / kWaves);
+    // the waves split K in runs of whole parameter dwords (4 groups), so that
+    // one dword load per 4 groups serves a run (a wave's first group is 4-aligned)
+    const int nq = G4 / 4;
+    const int g0 = 4 * (nq * wv / kWaves), g1 = min(4 * (nq * (wv + 1) / kWaves), G);
 
     // tiles past N re-read the last tile (their outputs are not stored);
     // tokens past M re-read the last token's row
@@ -129,13 +133,16 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
     }
     const int8_t *xrow = reinterpret_cast<const int8_t *>(xsm) + min(lr, mrows - 1) * xstride + 32 * kb;
 
-    auto load = [&](Slot<NT> &s, int i) {
+    // ring slot d holds groups g0 + d (mod 4): slot 0 also loads the parameter
+    // dword of its quad of groups (d is a constant in the unrolled loops)
+    auto load = [&](Slot<NT> &s, int i, int d) {
         const int g = min(g0 + i, glast);
 #pragma unroll
         for (int t = 0; t < NT; t++) {
             s.w[t] = __builtin_amdgcn_raw_buffer_load_b128(rw, 16 * l, ((int64_t)tile[t] * G + g) * kTileBytes, 2);
-            s.p[t] = __builtin_amdgcn_raw_buffer_load_b32(rp, (int)(param_index(tile[t] * 16 + lr, g, G4) & ~3),
-                                                          0, 0);
+            if (d == 0)
+                s.p[t] = __builtin_amdgcn_raw_buffer_load_b32(rp, (int)(param_index(tile[t] * 16 + lr, g, G4) & ~3),
+                                                              0, 0);
         }
         if constexpr (!XS) {
 #pragma unroll
@@ -153,16 +160,22 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
     Slot<NT> ring[kDepth];
 #pragma unroll
     for (int d = 0; d < kDepth; d++)
-        load(ring[d], d);
+        load(ring[d], d, d);
     if constexpr (XS) {
         // loads retire in order: once only the weight prologue is
         // outstanding, this thread's row copies have landed
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDepth * 2 * NT) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kDepth + 1) * NT) : "memory");
         dev::lds_barrier();
     }
 
-    auto step = [&](Slot<NT> &s, int i) {
+    uint32_t pq[NT];                    // parameter dwords of the current quad of groups
+    auto step = [&](Slot<NT> &s, int i, int d) {
         const int g = g0 + i;
+        if (d == 0) {
+#pragma unroll
+            for (int t = 0; t < NT; t++)
+                pq[t] = s.p[t];
+        }
         if constexpr (XS) {
 #pragma unroll
             for (int q = 0; q < 4; q++)
@@ -176,7 +189,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
         }
 #pragma unroll
         for (int t = 0; t < NT; t++) {
-            const uint32_t pb = (s.p[t] >> (8 * (g & 3))) & 0xFFu;
+            const uint32_t pb = (pq[t] >> (8 * d)) & 0xFFu;
             const uint32_t s1 = (pb & 15u) + 1u;
             const uint32_t c16 = ((128u - (pb >> 4) * s1) * 257u) & 0xFFFFu;
             const us2 S = {(unsigned short)s1, (unsigned short)s1};
@@ -199,19 +212,19 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
                                                                 __builtin_bit_cast(h8, bw), acc[t], 0, 0, 0);
             }
         }
-        load(s, i + kDepth);
+        load(s, i + kDepth, d);
     };
 
     int i = 0;
     for (; i + kDepth <= len; i += kDepth) {
 #pragma unroll
         for (int d = 0; d < kDepth; d++)
-            step(ring[d], i + d);
+            step(ring[d], i + d, d);
     }
 #pragma unroll
     for (int d = 0; d < kDepth - 1; d++)
         if (i + d < len)
-            step(ring[d], i + d);
+            step(ring[d], i + d, d);
 
     // the waves' partial sums, added in wave order; lane l holds tokens
     // 4 (l / 16) + r, channel l % 16 of each tile
