@@ -38,11 +38,11 @@ EVAL_SHAPES = [(M, N, K) for M in (1, 8, 16, 32, 64)
                               (8192, 10240), (8192, 57344), (28672, 8192))]
 
 
-def random_shapes(n, seed):
+def random_shapes(n, seed, m_lo=1, m_hi=64):
     rng = np.random.default_rng(seed)
     out = []
     while len(out) < n:
-        M = int(round(2 ** rng.uniform(0, 6)))
+        M = int(round(2 ** rng.uniform(math.log2(m_lo), math.log2(m_hi))))
         K = 128 * int(round(2 ** rng.uniform(2, math.log2(224))))
         N = 16 * int(round(2 ** rng.uniform(5, math.log2(3584))))
         if N * K // 2 <= 512 << 20:
@@ -180,6 +180,7 @@ def main(argv=None):
     ap.add_argument("--shapes-from", default=None,
                     help="time the (M, N, K) shapes of an earlier sweep's CSV (M <= --max-m)")
     ap.add_argument("--max-m", type=int, default=64)
+    ap.add_argument("--m-range", default="1,64", help="lo,hi: token counts of the random shapes (log-uniform)")
     ap.add_argument("--part", default="0/1", help="i/n: time every n-th shape from the i-th (to split a sweep)")
     args = ap.parse_args(argv)
     if args.launch:
@@ -194,7 +195,8 @@ def main(argv=None):
             w.writerow(COMPARE_FIELDS)
             compare(shapes, w)
         return 0
-    shapes = EVAL_SHAPES if args.eval else random_shapes(args.shapes, args.seed)
+    m_lo, m_hi = (int(v) for v in args.m_range.split(","))
+    shapes = EVAL_SHAPES if args.eval else random_shapes(args.shapes, args.seed, m_lo, m_hi)
     if args.shapes_from:
         import gzip
         with (gzip.open(args.shapes_from, "rt") if args.shapes_from.endswith(".gz") else open(args.shapes_from)) as f:
