@@ -266,9 +266,13 @@ def test_gemm_validation(lib, monkeypatch):
     # a stream-K prefill plan: the same rule
     monkeypatch.delenv("W4A8_DECODE_PLAN")
     monkeypatch.setenv("W4A8_PREFILL_P", "64")
+    monkeypatch.setenv("W4A8_PREFILL_TM", "8")
     need = _lib.gemm_w4a8_workspace_bytes(4096, 4096, 4096)
-    assert need > 64 * 2 * 256 * 256 * 4
+    assert need > 64 * 2 * 128 * 256 * 4
     assert call(M=4096, N=4096, K=4096, ws=A, wsb=need - 1) == -4
+    # TM = 16 tiles are never split (no stream-K there): no workspace
+    monkeypatch.setenv("W4A8_PREFILL_TM", "16")
+    assert _lib.gemm_w4a8_workspace_bytes(4096, 4096, 4096) == 0
 
 
 def test_gemm_noalloc_validation(lib):
@@ -300,13 +304,13 @@ CONFIG_KN = [(512, 512), (4096, 12288), (4096, 4096), (4096, 22016), (11008, 409
 
 @pytest.mark.parametrize("K,N", CONFIG_KN)
 def test_every_plan_fits_its_lds_with_and_without_workspace(lib, K, N):
-    """For every config shape at 1..64 tokens (and a few prefill token
+    """For every config shape at 1..128 tokens (and a few prefill token
     counts), the plan gemm_w4a8 launches with a workspace and the one it
     launches with ws == NULL both request LDS within the kernel's limit, and
     the NULL-workspace plan needs no workspace.  (An unsplit N-split plan at
     K = 28672 once asked for 137 KB, over the 128 KB decode limit.)"""
     from w4a8_quantized_linear_amd import _lib
-    for M in list(range(1, 65)) + [96, 256, 512, 768, 4096]:
+    for M in list(range(1, 129)) + [256, 512, 768, 4096]:
         for with_ws in (True, False):
             d = _lib.gemm_w4a8_plan_detail(M, N, K, with_ws)
             limit = 160 * 1024 if d["kind"] == 1 else 128 * 1024

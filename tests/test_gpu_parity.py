@@ -431,7 +431,7 @@ def test_prefill_ragged(tm, M, K, N):
 # last contributor.  P from 1 (one workgroup does everything) to more ranges
 # than groups per tile (every tile split many ways); results are bit-exact
 # and deterministic, and the workspace counters are left at zero.
-@pytest.mark.parametrize("tm", ["4", "16"])
+@pytest.mark.parametrize("tm", ["4", "8"])
 @pytest.mark.parametrize("P", ["1", "5", "37", "256"])
 @pytest.mark.parametrize("M,K,N", [(300, 384, 272), (1100, 640, 304), (257, 1152, 1040)])
 def test_prefill_stream_k(tm, P, M, K, N):
@@ -476,7 +476,7 @@ def test_workspace_shared_across_shapes_and_kernels():
     from w4a8_quantized_linear_amd import _lib, gemm_w4a8, quantize_act_per_token_i8
     cases = [  # (M, K, N, env)
         (1100, 640, 304, {"W4A8_PREFILL_TM": "4", "W4A8_PREFILL_P": "37"}),
-        (300, 1024, 2048, {"W4A8_PREFILL_TM": "16", "W4A8_PREFILL_P": "200"}),
+        (300, 1024, 2048, {"W4A8_PREFILL_TM": "8", "W4A8_PREFILL_P": "200"}),
         (24, 1024, 2048, {"W4A8_DECODE_PLAN": "2,1,3"}),
         (257, 1152, 1040, {"W4A8_PREFILL_TM": "8", "W4A8_PREFILL_P": "64"}),
         (9, 1024, 512, {"W4A8_DECODE_PLAN": "1,2,4"}),
@@ -518,7 +518,16 @@ def test_workspace_shared_across_shapes_and_kernels():
                 os.environ[k] = v
 
 
-@pytest.mark.parametrize("M,K,N", [(5, 1152, 272), (24, 3072, 1040), (40, 2048, 528)])
+@pytest.mark.parametrize("M,K,N", [(96, 4096, 11008), (128, 11008, 4096), (113, 8192, 10240)])
+def test_gemm_mid_m_takes_the_decode_kernels(M, K, N):
+    """65..128 tokens on layers whose 64 x 256 prefill tiles would leave more
+    than half of the CUs idle run on the decode kernels; every row compared."""
+    from w4a8_quantized_linear_amd import gemm_w4a8_plan
+    assert gemm_w4a8_plan(M, N, K)["kind"] == 0
+    _gemm_case(4, M, K, N)
+
+
+@pytest.mark.parametrize("M,K,N", [(5, 1152, 272), (24, 3072, 1040), (40, 2048, 528), (100, 1152, 272)])
 def test_every_decode_candidate_is_exact(M, K, N):
     """Every plan the learned selector may pick (gemm_w4a8_decode_candidates)
     runs, and gives the oracle's INT32 accumulators bit for bit."""

@@ -237,7 +237,7 @@ w4a8_status gemm_w4a8_decode_candidates(int64_t M, int64_t N, int64_t K, int32_t
 {
     if (!count || (max_plans > 0 && !plans))
         return W4A8_E_NULL;
-    if (M <= 0 || M > 64 || max_plans < 0 || !gemm_shape_ok(N, K))
+    if (M <= 0 || M > kDecodeMaxM || max_plans < 0 || !gemm_shape_ok(N, K))
         return W4A8_E_SHAPE;
     GemmPlan cand[256];
     const int n = decode_candidates(M, N, K, cand, 256);
@@ -253,7 +253,7 @@ w4a8_status gemm_w4a8_decode_candidates(int64_t M, int64_t N, int64_t K, int32_t
 
 float gemm_w4a8_selector_score(int64_t M, int64_t N, int64_t K, const int32_t *plan, int64_t cus)
 {
-    if (!plan || M <= 0 || M > 64 || !gemm_shape_ok(N, K) || cus <= 0)
+    if (!plan || M <= 0 || M > kDecodeMaxM || !gemm_shape_ok(N, K) || cus <= 0)
         return -1.0f;
     GemmPlan p{};
     p.mt = plan[0];

@@ -212,9 +212,21 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
         if (launchable(q, M, N, K) && decode_lds_bytes(q, M, K) <= 64 * 1024)
             p = q;
     }
+    // 65..128 tokens stay on the decode kernels while the matrix-core
+    // kernel's smallest tiles (64 tokens x 256 channels) would leave more than
+    // half of the CUs idle: measured on MI355X (graph-timed), M = 96 and 128
+    // at K = 4096, N = 11008: 18.7 / 20.0 us against 26.5 / 25.2; K = 11008,
+    // N = 4096: 19.8 / 19.0 against 50.5 / 51.2; K = 8192, N = 10240: 26.1 /
+    // 31.9 against 43.1 / 43.3; at N = 22016 (172 tiles) the matrix-core
+    // kernel stays ahead (27.0 / 26.4 against 27.8 / 29.4)
+    const int64_t cus = num_cus();
+    const int64_t nblk = (ntiles * kTileN + 255) / 256;
+    auto tiles_of = [&](int t) { return (M + 16 * t - 1) / (16 * t) * nblk; };
+    const bool decode_m = M <= 64 || (M <= kDecodeMaxM && tiles_of(4) * 2 < cus);
+
     // the learned selector, when a model is compiled in: the candidate with
     // the highest predicted bandwidth utilization (remembered per shape)
-    if (M <= 64 && selector_enabled())
+    if (decode_m && selector_enabled())
         p = selected_plan(M, N, K, p);
 
     // many tokens: the matrix-core kernel with (16 TM) x 256 workgroup tiles.
@@ -231,9 +243,6 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     //    TM 16, 8, 4: smaller tiles rebuild each weight for fewer tokens).
     // W4A8_PREFILL_TM=4|8|16 forces this kernel and its TM (at any M);
     // W4A8_PREFILL_P=n forces n stream-K ranges (0: one workgroup per tile).
-    const int64_t cus = num_cus();
-    const int64_t nblk = (ntiles * kTileN + 255) / 256;
-    auto tiles_of = [&](int t) { return (M + 16 * t - 1) / (16 * t) * nblk; };
     int tm = 0;
     int64_t ranges = 0;
     if (const char *env = std::getenv("W4A8_PREFILL_TM"))
@@ -242,7 +251,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
         tm = 0;
         if (M > 32 && M <= 64 && N >= 32768)
             tm = 4;   // 33..64 tokens on the widest N: activations shared through LDS
-        else if (M > 64) {
+        else if (!decode_m) {
             if (G >= 64 && tiles_of(4) * 10 < cus * 6) {
                 tm = 4;
                 ranges = cus;

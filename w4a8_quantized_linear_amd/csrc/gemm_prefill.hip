@@ -14,7 +14,7 @@
 // channels [64 w, 64 w + 64) of the tile with v_mfma_i32_16x16x64_i8; its 64
 // 16x16 INT32 accumulator tiles fill the 256 accumulation registers.
 //   * Weights never touch LDS.  The device weight stream is already in the
-//     operand order of this MFMA (one 16-byte lane load = the two 64-k B
+//     operand order of this MFMA (one 16-byte lane load = the two 64-k A
 //     operands of one 16-channel tile), so each wave streams its four tiles
 //     per group straight into a ring of registers several groups ahead of
 //     use and rebuilds them to INT8 there (mask/shift, packed multiply-add,
@@ -41,7 +41,7 @@
 // place in the accumulation registers: the compiler's own lowering of this
 // MFMA copies accumulators between register files on every step.  The
 // compiler does not see these as MFMAs, so the hazards it would pad are
-// padded here: a VALU write of a B operand is separated from its first MFMA
+// padded here: a VALU write of a weight operand is separated from its first MFMA
 // read by a phase boundary plus s_nop, and the accumulators are read only
 // after s_nop padding that covers the MFMA result latency.
 //
@@ -59,6 +59,8 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 using dev::kBufFlags;
 using dev::rsrc;
@@ -84,18 +86,27 @@ struct Cfg {
                   "ring, register and parameter-byte indices are static in the unrolled loop");
     static_assert(kXChunks % 2 == 0, "a wave's first LDS load starts an even 8-row block");
     static_assert(TM % (kAhead + 1) == 0 && TM > kAhead, "the operand-read ring lines up with the phases");
-    static_assert(BM <= kThreads, "one token scale per thread");
-    static_assert((BM / 2) * (BN * 2 + 16) <= kAStages * kAStage, "output half-tile fits in the stages");
+    static_assert(BM <= kThreads && BN == kThreads, "one token scale and one channel scale per thread");
 };
 
 // byte offset of 16-byte chunk `ch` (0..7) of activation row `row` (128-byte rows)
 __device__ inline int swz(int row, int ch) { return row * 128 + ((ch ^ ((row >> 1) & 7)) << 4); }
 
-// acc += A * B on the matrix cores, accumulator in place in AGPRs
+// acc += A * B on the matrix cores, accumulator in place in AGPRs.  Both
+// operands put row (of A) or column (of B) l % 16 and 16-byte k-block l / 16
+// in lane l; the result puts rows 4 (l / 16) .. + 3 of column l % 16 in lane
+// l.  The weights are A and the activations B, so the result tile is channels
+// x tokens and a lane holds four consecutive channels of one token.
 __device__ inline void mfma_acc(v4i &acc, const v4i &a, const v4i &b)
 {
     asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+
+// Stream-K (a tile's K range split over workgroups) at TM = 4 and 8 only: at
+// TM = 16 the accumulators fill the accumulation registers, and the fixup
+// path's adds made the compiler spill accumulators inside the main loop.
+template <int TM>
+constexpr bool kStreamK = TM < 16;
 
 struct PrefillArgs {
     const int8_t *qx;
@@ -133,8 +144,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
     constexpr int BM = C::BM, kAStage = C::kAStage, kXChunks = C::kXChunks,
                   kBDepth = C::kBDepth, kUnroll = C::kUnroll;
     extern __shared__ __align__(16) uint8_t smem[];
-    float *sa_lds = reinterpret_cast<float *>(smem + kAStages * kAStage);   // [BM] token scales
-    constexpr int kDummy = kAStages * kAStage + BM * 4;                      // 1 KB never read
+    constexpr int kDummy = kAStages * kAStage;   // 1 KB never read
+    // the tile's token scales and channel scales, for the epilogue
+    float *sa_lds = reinterpret_cast<float *>(smem + kDummy + 1024);   // [BM]
+    float *s0_lds = sa_lds + BM;                                        // [BN]
     __shared__ uint32_t arrival;
 
     const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -201,8 +214,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
         const int poff = (nt0 * (G4 / 4) * 16 + lr) * 4;
 
         __syncthreads();   // the previous segment is done with the LDS
-        // this thread's token scale (stored to LDS after the loads below)
+        // this thread's token scale and channel scale (stored to LDS after
+        // the loads below)
         const float sa_t = a.s_a[min<int64_t>(m0 + min(tid, BM - 1), a.M - 1)];
+        const float s0_t = (float)__builtin_bit_cast(_Float16, a.s0[min<int64_t>((int64_t)nb * BN + tid, a.N - 1)]);
 
         // Loads of groups past the segment are still issued (so that every
         // group issues the same number of loads and no branch splits the
@@ -244,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
         uint32_t S1[2][TN], C16[2][TN], sc_p = 0, sc_s1 = 0;
 
         v4i af[kAhead + 1];   // activation operands in flight (one per row step)
-        v4i f0[TN], f1[TN];   // B operands: current phase / next phase
+        v4i f0[TN], f1[TN];   // weight operands: current phase / next phase
         uint32_t ru = 0;      // rebuild in progress: masked codes of one dword
         us2 rv = {0, 0};      // ... after the packed multiply-add
 
@@ -283,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
             for (int k = 0; k < kSlots; k++) {
                 const int i = k / TN, t = k % TN;
                 const v4i &av = af[i % (kAhead + 1)];
-                mfma_acc(acc(i, t), av, fc[t]);
+                mfma_acc(acc(i, t), fc[t], av);
                 if (t == 0) {
                     const int ir = i + kAhead;
                     af[ir % (kAhead + 1)] = *reinterpret_cast<const v4i *>(
@@ -379,8 +394,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
                 bload_t(ring[u], gs + u, t);
         if (tid < BM)
             sa_lds[tid] = sa_t;
+        s0_lds[tid] = s0_t;
         // groups gs and gs + 1 in LDS (group gs + 2's LDS loads and the 2 TN
-        // kBDepth weight loads may still be in flight); the token scales
+        // kBDepth weight loads may still be in flight); the scales
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kXChunks + 2 * TN * kBDepth)
                      : "memory");
 #pragma unroll
@@ -419,6 +435,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
 
         // MFMA results are read by VALU below: cover the longest result latency
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int t = 0; t < TN; t++)
+                asm volatile("" : "+a"(acc(i, t)));
 
         // ---- a tile split over several ranges: every contributor stores its
         // partial accumulators; the last to arrive adds the others' and runs
@@ -428,7 +449,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
         // issued after it has seen the final count.  No workgroup waits on
         // another.
         const int c_lo = owner((int64_t)tile * G), c_hi = owner((int64_t)tile * G + G - 1);
-        if (c_lo != c_hi) {
+        if (kStreamK<TM> && c_lo != c_hi) {
             constexpr int kSlotInts = TM * TN * kWaves * 64 * 4;
             auto slot_of = [&](int ww) {
                 const int first = (int)(range_lo(ww) / G);
@@ -464,63 +485,67 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
                 __hip_atomic_store(a.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 
-        // ---- epilogue.  Lane l holds rows 16 i + 4 (l / 16) + r, column
-        // 16 t + l % 16 of the wave's slice.  y = fp16((acc s_a) s0) goes
-        // through LDS, half a tile at a time, so that global stores are whole
-        // 16-byte pieces of output rows.  The INT32 accumulators (an optional
-        // output) are stored directly.
-        float s0f[TN];
-#pragma unroll
-        for (int t = 0; t < TN; t++)
-            s0f[t] = (float)__builtin_bit_cast(_Float16, a.s0[min(nt0 + t, ntiles - 1) * 16 + lr]);
+        // ---- epilogue.  Lane l holds token row 16 i + l % 16 and channels
+        // 16 t + 4 (l / 16) .. + 3 of the wave's slice, so y = fp16((acc s_a)
+        // s0) leaves as one 8-byte store of four consecutive channels per
+        // (i, t), straight from the registers (the caches merge the four
+        // lane groups' 8-byte pieces of a row into whole lines).  The INT32
+        // accumulators (an optional output) leave as 16-byte stores.  N is a
+        // multiple of 16, so a channel tile is wholly inside or past N.
+        const int tn = min(TN, ntiles - nt0);                // the wave's tiles inside N
+        const int64_t n0 = (int64_t)nt0 * 16 + 4 * lk;       // lane's first channel in tile 0
         if (a.acc_out) {
 #pragma unroll
             for (int i = 0; i < TM; i++) {
+                const int64_t m = (int64_t)m0 + 16 * i + lr;
 #pragma unroll
-                for (int t = 0; t < TN; t++) {
-                    const int64_t n = (int64_t)(nt0 + t) * 16 + lr;
-#pragma unroll
-                    for (int r = 0; r < 4; r++) {
-                        const int64_t m = (int64_t)m0 + 16 * i + 4 * lk + r;
-                        if (nt0 + t < ntiles && m < a.M)
-                            a.acc_out[m * a.N + n] = acc(i, t)[r];
-                    }
-                }
+                for (int t = 0; t < TN; t++)
+                    if (t < tn && m < a.M)
+                        *reinterpret_cast<v4i *>(a.acc_out + m * a.N + n0 + 16 * t) = acc(i, t);
             }
         }
-        constexpr int kYRow = BN * 2 + 16;    // padded LDS row of the fp16 tile (bytes)
-        constexpr int kHalf = BM / 2;
-        const int ncol0 = nb * BN;              // first output column of the tile
-        __syncthreads();
+        // the scales come from LDS: a global load waited for between the
+        // stores would also wait for every store issued before it
+        v4f s0f[TN];
+        float sa[TM];
 #pragma unroll
-        for (int half = 0; half < 2; half++) {
+        for (int t = 0; t < TN; t++)
+            s0f[t] = *reinterpret_cast<const v4f *>(s0_lds + wv * 64 + 16 * t + 4 * lk);
 #pragma unroll
-            for (int ii = 0; ii < TM / 2; ii++) {
-                const int i = half * (TM / 2) + ii;
+        for (int i = 0; i < TM; i++)
+            sa[i] = sa_lds[16 * i + lr];
+        auto yval = [&](int i, int t) {
+            // the tile stays in the accumulation registers up to here: the
+            // compiler would otherwise copy all of them to VGPRs (and spill)
+            // right after the main loop
+            asm volatile("" : "+a"(acc(i, t)));
+            h4 v;
 #pragma unroll
-                for (int t = 0; t < TN; t++) {
+            for (int r = 0; r < 4; r++)
+                v[r] = (_Float16)(((float)acc(i, t)[r] * sa[i]) * s0f[t][r]);
+            return v;
+        };
+        if (m0 + BM <= a.M && tn == TN) {
+            // a whole tile: straight-line code, one row tile at a time (the
+            // scheduler would otherwise move every accumulator read up front)
 #pragma unroll
-                    for (int r = 0; r < 4; r++) {
-                        const int ml = 16 * i + 4 * lk + r;
-                        const float yv = ((float)acc(i, t)[r] * sa_lds[ml]) * s0f[t];
-                        *reinterpret_cast<_Float16 *>(smem + (ml - half * kHalf) * kYRow +
-                                                      (wv * 64 + 16 * t + lr) * 2) = (_Float16)yv;
-                    }
-                }
+            for (int i = 0; i < TM; i++) {
+                uint16_t *yr = a.y + ((int64_t)m0 + 16 * i + lr) * a.N + n0;
+#pragma unroll
+                for (int t = 0; t < TN; t++)
+                    *reinterpret_cast<h4 *>(yr + 16 * t) = yval(i, t);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __syncthreads();
-            // kHalf rows x 32 pieces of 16 bytes; N is a multiple of 16, so a
-            // piece is wholly inside or wholly past the last column
-#pragma unroll 4
-            for (int c = tid; c < kHalf * (BN / 8); c += kThreads) {
-                const int row = c / (BN / 8), pc = c % (BN / 8);
-                const int64_t m = (int64_t)m0 + half * kHalf + row;
-                const int64_t n = (int64_t)ncol0 + 8 * pc;
-                if (m < a.M && n < a.N)
-                    *reinterpret_cast<v4i *>(a.y + m * a.N + n) =
-                        *reinterpret_cast<const v4i *>(smem + row * kYRow + 16 * pc);
+        } else {
+#pragma unroll
+            for (int i = 0; i < TM; i++) {
+                const int64_t m = (int64_t)m0 + 16 * i + lr;
+#pragma unroll
+                for (int t = 0; t < TN; t++)
+                    if (t < tn && m < a.M)
+                        *reinterpret_cast<h4 *>(a.y + m * a.N + n0 + 16 * t) = yval(i, t);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __syncthreads();
         }
     }
 }
@@ -528,7 +553,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
 template <int TM>
 size_t lds_bytes()
 {
-    return (size_t)kAStages * Cfg<TM>::kAStage + Cfg<TM>::BM * 4 + 1024;
+    return (size_t)kAStages * Cfg<TM>::kAStage + 1024 + (Cfg<TM>::BM + BN) * 4;
 }
 
 // The kernel addresses activations with 32-bit buffer offsets, so M is cut
@@ -564,7 +589,7 @@ hipError_t launch_tm(int P, const int8_t *qx, const float *s_a, const uint8_t *s
         a.nblocks = (int)((N + BN - 1) / BN);
         const int64_t tiles = (int64_t)a.mblocks * a.nblocks;
         const int64_t units = tiles * (K / kGroup);
-        if (P > 0 && ws != nullptr && tiles <= kWsCounters) {
+        if (kStreamK<TM> && P > 0 && ws != nullptr && tiles <= kWsCounters) {
             a.P = (int)std::min<int64_t>(P, units);
             a.cnt = reinterpret_cast<uint32_t *>(ws);
             a.part = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(ws) + kWsPartOffset);
@@ -601,7 +626,7 @@ size_t prefill_lds_bytes(int tm)
 // per launch), then two partial-accumulator slots of 16 TM x 256 INT32 per range.
 size_t prefill_ws_bytes(int tm, int P, int64_t M, int64_t N, int64_t K)
 {
-    if (P <= 0 || !prefill_tm_supported(tm))
+    if (P <= 0 || !prefill_tm_supported(tm) || tm == 16)   // no stream-K at TM = 16
         return 0;
     const int64_t bm = 16 * tm;
     const int64_t rows_max = (0x7FFFFFFF / K - bm) / bm * bm;
