@@ -8,6 +8,8 @@ fp16 rounding) + 2^-24 (fp16 subnormal spacing).  One-hot activations make
 every sum exact, and there the result is bit-exact: y = fp16(r s0), which pins
 the operand layout k by k.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -100,3 +102,35 @@ def test_w4a16_stride_tails_and_determinism():
     (ref, absref), _, _ = ref_of(x1, w1)
     check(to_host(y).view(np.uint16), ref, absref, 128, "w4a16 K=128")
     gemm_w4a16(torch.empty((0, 128), dtype=torch.float16, device=dev()), wq1["wpacked"], wq1["s0"], 64)
+
+
+@pytest.mark.parametrize("nt", ["1", "2", "4"])
+def test_w4a16_two_token_tiles_match_one(nt):
+    """Two 16-token tiles per workgroup (each rebuilt weight feeds two MFMAs)
+    give the same bits as one: every token's sum is the same MFMA sequence.
+    M = 37 leaves a partly filled second pair of tiles; N = 272 a tail tile."""
+    import torch
+    from w4a8_quantized_linear_amd import gemm_w4a16
+    K, N, M = 1152, 272, 37
+    w = workloads.weights(2, K, N)
+    x = workloads.activations(2, M, K, N)
+    say("w4a16 MT=2 vs MT=1 NT=%s M=%d K=%d N=%d" % (nt, M, K, N))
+    wq = gpu_weights(w)
+    keys = ("W4A8_W16_NT", "W4A8_W16_MT")
+    old = {k: os.environ.get(k) for k in keys}
+    try:
+        os.environ["W4A8_W16_NT"] = nt
+        out = {}
+        for mt in ("1", "2"):
+            os.environ["W4A8_W16_MT"] = mt
+            out[mt] = gemm_w4a16(to_dev(x), wq["wpacked"], wq["s0"], N)
+        torch.cuda.synchronize()
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    assert torch.equal(out["1"], out["2"])
+    (ref, absref), _, _ = ref_of(x, w)
+    check(to_host(out["2"]).view(np.uint16), ref, absref, K, "w4a16 MT=2")

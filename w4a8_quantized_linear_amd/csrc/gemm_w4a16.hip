@@ -26,8 +26,9 @@
 // the contraction still covers each k once.
 //
 // Work decomposition (decode shapes: the weight stream is read once per 16
-// tokens).  A workgroup of four waves owns NT tiles of 16 channels and 16
-// tokens; the waves split the K groups into four runs and stream their
+// MT tokens).  A workgroup of four waves owns NT tiles of 16 channels and MT
+// tiles of 16 tokens (each rebuilt weight operand feeds MT MFMAs); the waves
+// split the K groups into four runs and stream their
 // weight tiles, parameter dwords and activation operands DEPTH groups ahead
 // (unconditional loads, so the compiler's vmcnt waits are exact).  The four
 // partial sums meet in LDS and are added in wave order (deterministic).
@@ -74,23 +75,24 @@ struct W16Args {
     int cx;                   // activation operands loaded row-contiguous, lanes exchanged
 };
 
-template <int NT>
+template <int NT, int MT>
 struct Slot {
     v4i w[NT];                // codes of the NT tiles, one group
     uint32_t p[NT];           // parameter dword (four groups) of the lane's channel
-    v4i x[4];                 // activation operands of the group's four MFMAs
+    v4i x[MT][4];             // activation operands of the group's four MFMAs, per token tile
 };
 
-template <int NT, bool XS>
+template <int NT, int MT, bool XS>
 __global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
 {
-    __shared__ f4 red[kWaves][NT][64];
+    static_assert(!XS || MT == 1, "staged rows serve one token tile");
+    __shared__ f4 red[kWaves][MT][NT][64];
     extern __shared__ __align__(16) uint8_t xsm[];   // XS: fp16 rows [mrows][2 K + 16]
     const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int l = threadIdx.x & 63, lr = l & 15, kb = l >> 4;
     const int nt0 = blockIdx.x * NT;                  // first 16-channel tile
     const int ntiles = (int)(a.N / kTileN);
-    const int64_t m0 = (int64_t)blockIdx.y * 16;
+    const int64_t m0 = (int64_t)blockIdx.y * 16 * MT;
     const int G = (int)(a.K / kGroup), G4 = (int)groups_padded(a.K);
     // the waves split K in runs of whole parameter dwords (4 groups), so that
     // one dword load per 4 groups serves a run (a wave's first group is 4-aligned)
@@ -110,8 +112,12 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
     // cx the lanes load the block row by row instead (lane 4 r + q: row r,
     // k-block q, so four neighbouring lanes read one row's 128-byte line)
     // and ds_bpermute gives lane (lr, kb) the piece lane 4 lr + kb loaded
-    const int64_t row = min<int64_t>(m0 + (a.cx ? l >> 2 : lr), a.M - 1);
-    const int xoff = (int)(row * a.ldx * 2) + 32 * (a.cx ? l & 3 : kb);    // bytes: token row, k-block
+    int xoff[MT];                                        // bytes: token row, k-block
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+        const int64_t row = min<int64_t>(m0 + 16 * mt + (a.cx ? l >> 2 : lr), a.M - 1);
+        xoff[mt] = (int)(row * a.ldx * 2) + 32 * (a.cx ? l & 3 : kb);
+    }
     const int xsrc = 4 * (4 * lr + kb);
     const int glast = max(g1 - 1, g0);
     const int len = g1 - g0;
@@ -135,7 +141,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
 
     // ring slot d holds groups g0 + d (mod 4): slot 0 also loads the parameter
     // dword of its quad of groups (d is a constant in the unrolled loops)
-    auto load = [&](Slot<NT> &s, int i, int d) {
+    auto load = [&](Slot<NT, MT> &s, int i, int d) {
         const int g = min(g0 + i, glast);
 #pragma unroll
         for (int t = 0; t < NT; t++) {
@@ -146,18 +152,22 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
         }
         if constexpr (!XS) {
 #pragma unroll
-            for (int q = 0; q < 4; q++)
-                s.x[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff, g * 256 + 2 * (8 * (q & 1) + 64 * (q >> 1)),
-                                                               0);
+            for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+                    s.x[mt][q] = __builtin_amdgcn_raw_buffer_load_b128(
+                        rx, xoff[mt], g * 256 + 2 * (8 * (q & 1) + 64 * (q >> 1)), 0);
         }
     };
 
-    f4 acc[NT];
+    f4 acc[MT][NT];
 #pragma unroll
-    for (int t = 0; t < NT; t++)
-        acc[t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int t = 0; t < NT; t++)
+            acc[mt][t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    Slot<NT> ring[kDepth];
+    Slot<NT, MT> ring[kDepth];
 #pragma unroll
     for (int d = 0; d < kDepth; d++)
         load(ring[d], d, d);
@@ -169,7 +179,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
     }
 
     uint32_t pq[NT];                    // parameter dwords of the current quad of groups
-    auto step = [&](Slot<NT> &s, int i, int d) {
+    auto step = [&](Slot<NT, MT> &s, int i, int d) {
         const int g = g0 + i;
         if (d == 0) {
 #pragma unroll
@@ -179,13 +189,15 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
         if constexpr (XS) {
 #pragma unroll
             for (int q = 0; q < 4; q++)
-                s.x[q] = *reinterpret_cast<const v4i *>(xrow + g * 256 + 2 * (8 * (q & 1) + 64 * (q >> 1)));
+                s.x[0][q] = *reinterpret_cast<const v4i *>(xrow + g * 256 + 2 * (8 * (q & 1) + 64 * (q >> 1)));
         } else if (a.cx) {
 #pragma unroll
-            for (int q = 0; q < 4; q++)
+            for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-                for (int d = 0; d < 4; d++)
-                    s.x[q][d] = __builtin_amdgcn_ds_bpermute(xsrc, s.x[q][d]);
+                for (int q = 0; q < 4; q++)
+#pragma unroll
+                    for (int d = 0; d < 4; d++)
+                        s.x[mt][q][d] = __builtin_amdgcn_ds_bpermute(xsrc, s.x[mt][q][d]);
         }
 #pragma unroll
         for (int t = 0; t < NT; t++) {
@@ -208,8 +220,10 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
             for (int q = 0; q < 4; q++) {
                 const int h = q >> 1, d0 = 2 * (q & 1);
                 const v4i bw = {(int)b[h][d0][0], (int)b[h][d0][1], (int)b[h][d0 + 1][0], (int)b[h][d0 + 1][1]};
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, s.x[q]),
-                                                                __builtin_bit_cast(h8, bw), acc[t], 0, 0, 0);
+#pragma unroll
+                for (int mt = 0; mt < MT; mt++)
+                    acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, s.x[mt][q]),
+                                                                        __builtin_bit_cast(h8, bw), acc[mt][t], 0, 0, 0);
             }
         }
         load(s, i + kDepth, d);
@@ -227,27 +241,32 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
             step(ring[d], i + d, d);
 
     // the waves' partial sums, added in wave order; lane l holds tokens
-    // 4 (l / 16) + r, channel l % 16 of each tile
+    // 16 mt + 4 (l / 16) + r, channel l % 16 of each tile
 #pragma unroll
-    for (int t = 0; t < NT; t++)
-        red[wv][t][l] = acc[t];
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int t = 0; t < NT; t++)
+            red[wv][mt][t][l] = acc[mt][t];
     __syncthreads();
     if (wv == 0) {
 #pragma unroll
-        for (int t = 0; t < NT; t++) {
-            f4 v = red[0][t][l];
+        for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
-            for (int w = 1; w < kWaves; w++)
-                v += red[w][t][l];
-            if (nt0 + t >= ntiles)
-                continue;
-            const int64_t n = (int64_t)(nt0 + t) * 16 + lr;
-            const float sc = (float)__builtin_bit_cast(_Float16, a.s0[n]);
+            for (int t = 0; t < NT; t++) {
+                f4 v = red[0][mt][t][l];
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int64_t m = m0 + 4 * kb + r;
-                if (m < a.M)
-                    a.y[m * a.N + n] = __builtin_bit_cast(uint16_t, (_Float16)(v[r] * sc));
+                for (int w = 1; w < kWaves; w++)
+                    v += red[w][mt][t][l];
+                if (nt0 + t >= ntiles)
+                    continue;
+                const int64_t n = (int64_t)(nt0 + t) * 16 + lr;
+                const float sc = (float)__builtin_bit_cast(_Float16, a.s0[n]);
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int64_t m = m0 + 16 * mt + 4 * kb + r;
+                    if (m < a.M)
+                        a.y[m * a.N + n] = __builtin_bit_cast(uint16_t, (_Float16)(v[r] * sc));
+                }
             }
         }
     }
@@ -261,21 +280,21 @@ inline size_t w16_xs_bytes(int64_t M, int64_t K)
     return b <= 64 * 1024 ? (size_t)b : 0;
 }
 
-template <int NT, bool XS>
+template <int NT, int MT, bool XS>
 hipError_t launch_nt(const W16Args &a, hipStream_t st)
 {
     const int64_t nblk = (a.N / kTileN + NT - 1) / NT;
-    const int64_t mblk = (a.M + 15) / 16;
+    const int64_t mblk = (a.M + 16 * MT - 1) / (16 * MT);
     const size_t lds = XS ? w16_xs_bytes(a.M, a.K) : 0;
     if constexpr (XS) {
         // staged rows plus the reduction array pass the 64 KB default
         const hipError_t e =
-            raise_lds_limit(reinterpret_cast<const void *>(&gemm_w4a16_kernel<NT, XS>), 80 * 1024);
+            raise_lds_limit(reinterpret_cast<const void *>(&gemm_w4a16_kernel<NT, MT, XS>), 80 * 1024);
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL((gemm_w4a16_kernel<NT, XS>), dim3((unsigned)nblk, (unsigned)mblk), dim3(64 * kWaves), lds, st,
-                       a);
+    hipLaunchKernelGGL((gemm_w4a16_kernel<NT, MT, XS>), dim3((unsigned)nblk, (unsigned)mblk), dim3(64 * kWaves), lds,
+                       st, a);
     return hipGetLastError();
 }
 
@@ -297,6 +316,39 @@ static int pick_nt(int64_t M, int64_t N)
     if (tiles >= 512 || M > 16)
         return 2;
     return 1;
+}
+
+// Token tiles per workgroup (MT) at 17..64 tokens: with two, each weight
+// tile is read and rebuilt once per 32 tokens instead of 16, at the cost of
+// more registers (one wave per SIMD at four channel tiles) and, for 17..32
+// tokens, half the workgroups.  Graph-timed on MI355X (K = 4096 unless
+// noted; NT x MT, us):
+//   N = 22016 (1376 tiles): M = 17 2x2 21.4 against 24.7 for the rule above,
+//     M = 32 2x2 25.3 / 26.2, M = 48 4x2 39.6 / 39.7, M = 64 4x2 42.0 / 48.9;
+//   N = 11008 and 12288 (688, 768 tiles): M = 17 and 32 4x2 13.6-15.0 against
+//     16.4-18.7; at 48 and 64 tokens 4x1 stays (within 2-6% of the best);
+//   N = 4096 (256 tiles; K = 4096 and 11008): at 17 and 32 tokens 2x1 stays
+//     (two token tiles halve the workgroups and run 10-40% slower); M = 48
+//     and 64 2x2 10.0-10.2 against 11.2-11.5 (K = 11008: 19.2-19.6 / 23.1-23.4).
+// Each token's sum is the same MFMA sequence either way: the results are
+// bit-identical.  W4A8_W16_MT=1|2 overrides (sweeps).
+static void pick_tokens(int64_t M, int64_t N, int &nt, int &mt)
+{
+    const int64_t tiles = N / kTileN;
+    if (M <= 16 || M > 64)
+        return;
+    if (tiles >= 1024) {
+        mt = 2;
+        nt = M <= 32 ? 2 : 4;
+    } else if (tiles >= 512) {
+        if (M <= 32) {
+            mt = 2;
+            nt = 4;
+        }
+    } else if (M > 32) {
+        mt = 2;
+        nt = 2;
+    }
 }
 
 hipError_t launch_gemm_w4a16(const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
@@ -337,10 +389,23 @@ hipError_t launch_gemm_w4a16(const uint16_t *x, int64_t M, int64_t K, int64_t ld
             a.cx = std::atoi(env) != 0;
         if (const char *env = std::getenv("W4A8_W16_NT"))
             nt = std::atoi(env) == 4 ? 4 : (std::atoi(env) == 2 ? 2 : (std::atoi(env) == 1 ? 1 : nt));
-        const hipError_t e = xs ? (nt == 4 ? launch_nt<4, true>(a, st)
-                                           : (nt == 2 ? launch_nt<2, true>(a, st) : launch_nt<1, true>(a, st)))
-                                : (nt == 4 ? launch_nt<4, false>(a, st)
-                                           : (nt == 2 ? launch_nt<2, false>(a, st) : launch_nt<1, false>(a, st)));
+        int mt = 1;
+        if (!xs)
+            pick_tokens(a.M, N, nt, mt);
+        if (const char *env = std::getenv("W4A8_W16_MT"))
+            mt = std::atoi(env) == 2 ? 2 : 1;
+        if (xs)
+            mt = 1;
+        hipError_t e;
+        if (xs)
+            e = nt == 4 ? launch_nt<4, 1, true>(a, st)
+                        : (nt == 2 ? launch_nt<2, 1, true>(a, st) : launch_nt<1, 1, true>(a, st));
+        else if (mt == 2)
+            e = nt == 4 ? launch_nt<4, 2, false>(a, st)
+                        : (nt == 2 ? launch_nt<2, 2, false>(a, st) : launch_nt<1, 2, false>(a, st));
+        else
+            e = nt == 4 ? launch_nt<4, 1, false>(a, st)
+                        : (nt == 2 ? launch_nt<2, 1, false>(a, st) : launch_nt<1, 1, false>(a, st));
         if (e != hipSuccess)
             return e;
     }
