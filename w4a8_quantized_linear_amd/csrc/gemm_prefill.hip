@@ -380,24 +380,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(PrefillArgs a
 
         // prologue: groups gs .. gs + 2's activations into LDS, the first
         // kBDepth groups of weights in flight, group gs's (s1, C), first
-        // operands and first operand reads
+        // operands and first operand reads.  Each group's weights follow its
+        // activations, so the wait below covers only what the first group
+        // needs (a wait for three stages and then the first weights made
+        // every CU of a round wait for more of the start-up burst)
         BSlot ring[kBDepth];
 #pragma unroll
-        for (int q = 0; q < 3; q++)
+        for (int q = 0; q < 3; q++) {
 #pragma unroll
             for (int j = 0; j < kXChunks; j++)
                 xdma(q * kAStage, gs + q < ge, gs + q, j);
 #pragma unroll
-        for (int u = 0; u < kBDepth; u++)
+            for (int t = 0; t < TN; t++)
+                bload_t(ring[q], gs + q, t);
+        }
+#pragma unroll
+        for (int u = 3; u < kBDepth; u++)
 #pragma unroll
             for (int t = 0; t < TN; t++)
                 bload_t(ring[u], gs + u, t);
         if (tid < BM)
             sa_lds[tid] = sa_t;
         s0_lds[tid] = s0_t;
-        // groups gs and gs + 1 in LDS (group gs + 2's LDS loads and the 2 TN
-        // kBDepth weight loads may still be in flight); the scales
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kXChunks + 2 * TN * kBDepth)
+        // groups gs and gs + 1 in LDS with group gs's weights (group gs + 1's
+        // weights, group gs + 2's LDS loads and the later weights, kXChunks +
+        // 2 TN (kBDepth - 1) loads, may still be in flight); the scales
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kXChunks + 2 * TN * (kBDepth - 1))
                      : "memory");
 #pragma unroll
         for (int t = 0; t < TN; t++) {
