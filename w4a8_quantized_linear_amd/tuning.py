@@ -21,6 +21,15 @@ valid code pair and group parameter), timing does not depend on the values.
 --launch M1,M2,..  --n N --k K [--calls C] makes C eager calls per token count with the
 plan gemm_w4a8 picks (rotating weight copies, as above) and prints the plans: the
 program that profiler runs (rocprofv3 --pmc ...) trace for the decode counters.
+
+--route OUT.csv times, at 72, 96, 112 and 128 tokens on the 7B / 70B layers, the best
+decode plan (every candidate) against the many-token kernel at each TM, and the plan
+gemm_w4a8 picks: the evidence behind sending 65..128 tokens to the decode kernels
+when the many-token tiles are few.
+
+--w16 OUT.csv times gemm_w4a16 at 17, 32, 48 and 64 tokens on the 7B layers for
+every (tiles per workgroup, token tiles per workgroup) and the launcher's own
+choice, and checks that two token tiles give the bits of one.
 """
 from __future__ import annotations
 
@@ -112,6 +121,93 @@ def measure(shapes, tag, writer, reps=10, wave_n=None):
 
 
 COMPARE_FIELDS = ("M", "N", "K", "rules_plan", "selector_plan", "rules_us", "selector_us", "ratio")
+ROUTE_FIELDS = ("M", "N", "K", "decode_best_us", "decode_best_plan", "prefill_best_us", "prefill_best_tm",
+                "picked_kind", "picked_us")
+W16_FIELDS = ("M", "N", "K", "nt", "mt", "us", "default_us")
+ROUTE_LAYERS = ((4096, 11008), (11008, 4096), (8192, 10240), (4096, 22016), (4096, 12288), (28672, 8192))
+W16_LAYERS = ((4096, 11008), (4096, 4096), (4096, 22016), (11008, 4096), (4096, 12288))
+
+
+def _weight_views(pool, N, K):
+    from w4a8_quantized_linear_amd import w4a8_packed_weight_bytes
+    wb = w4a8_packed_weight_bytes(N, K)
+    stride = (wb + 4095) // 4096 * 4096
+    return [pool[i * stride:i * stride + wb] for i in range(min(max(1, (1 << 30) // stride), 64))]
+
+
+def route(writer, ms=(72, 96, 112, 128), reps=10):
+    """Best decode plan against the many-token kernel (each TM) per shape."""
+    import torch
+
+    from w4a8_quantized_linear_amd import _lib, gemm_w4a8, gemm_w4a8_decode_candidates, gemm_w4a8_plan
+    dev = torch.device("cuda:0")
+    pool = torch.randint(0, 256, (1 << 30,), dtype=torch.uint8, device=dev)
+    keys = ("W4A8_DECODE_PLAN", "W4A8_PREFILL_TM", "W4A8_PREFILL_P")
+    fields = ("mt", "nt", "splitk", "waves", "depth", "xstage", "wave_n")
+    ws = _lib.workspace(dev, 512 << 20)
+    for (K, N) in ROUTE_LAYERS:
+        views = _weight_views(pool, N, K)
+        for M in ms:
+            qx = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev)
+            sa = torch.rand(M, device=dev) * 0.01
+            s0 = (torch.rand(N, device=dev) * 1e-3).half()
+            y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            call = lambda r: gemm_w4a8(qx, sa, views[r % len(views)], s0, N, y=y, ws=ws)
+            best_d, plan_d = float("inf"), ""
+            for c in gemm_w4a8_decode_candidates(M, N, K):
+                os.environ["W4A8_DECODE_PLAN"] = ",".join(str(v) for v in c)
+                if tuple(gemm_w4a8_plan(M, N, K)[f] for f in fields) != c:
+                    continue
+                us = graph_time(call, reps)
+                if us < best_d:
+                    best_d, plan_d = us, ",".join(str(v) for v in c)
+            os.environ.pop("W4A8_DECODE_PLAN", None)
+            best_p, tm_p = float("inf"), 0
+            for tm in (4, 8, 16):
+                os.environ["W4A8_PREFILL_TM"] = str(tm)
+                us = graph_time(call, reps)
+                if us < best_p:
+                    best_p, tm_p = us, tm
+            for k in keys:
+                os.environ.pop(k, None)
+            picked = gemm_w4a8_plan(M, N, K)
+            us = graph_time(call, reps)
+            writer.writerow([M, N, K, round(best_d, 3), plan_d, round(best_p, 3), tm_p, picked["kind"], round(us, 3)])
+            print("route M=%d N=%d K=%d decode %.2f us prefill %.2f us picked kind %d %.2f us"
+                  % (M, N, K, best_d, best_p, picked["kind"], us), flush=True)
+
+
+def w16(writer, ms=(17, 32, 48, 64), reps=20):
+    """gemm_w4a16 over (NT, MT); MT = 2 must give the bits of MT = 1."""
+    import torch
+
+    from w4a8_quantized_linear_amd import gemm_w4a16
+    dev = torch.device("cuda:0")
+    pool = torch.randint(0, 256, (1 << 30,), dtype=torch.uint8, device=dev)
+    keys = ("W4A8_W16_NT", "W4A8_W16_MT")
+    for (K, N) in W16_LAYERS:
+        views = _weight_views(pool, N, K)
+        s0 = (torch.rand(N, device=dev) * 1e-3).half()
+        for M in ms:
+            x = (torch.randn((M, K), device=dev) * 0.5).half()
+            y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            call = lambda r: gemm_w4a16(x, views[r % len(views)], s0, N, y=y)
+            for k in keys:
+                os.environ.pop(k, None)
+            default = graph_time(call, reps)
+            for nt in (1, 2, 4):
+                ref = None
+                for mt in (1, 2):
+                    os.environ["W4A8_W16_NT"], os.environ["W4A8_W16_MT"] = str(nt), str(mt)
+                    out = gemm_w4a16(x, views[0], s0, N)
+                    if ref is None:
+                        ref = out
+                    elif not torch.equal(out, ref):
+                        raise SystemExit("two token tiles differ from one: M=%d N=%d K=%d NT=%d" % (M, N, K, nt))
+                    writer.writerow([M, N, K, nt, mt, round(graph_time(call, reps), 3), round(default, 3)])
+            for k in keys:
+                os.environ.pop(k, None)
+            print("w16 M=%d N=%d K=%d default %.2f us" % (M, N, K, default), flush=True)
 
 
 def compare(shapes, writer, reps=50, rounds=3):
@@ -175,6 +271,8 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--eval", action="store_true")
     ap.add_argument("--compare", action="store_true")
+    ap.add_argument("--route", action="store_true", help="decode against many-token kernel at 72..128 tokens")
+    ap.add_argument("--w16", action="store_true", help="gemm_w4a16 tiles-per-workgroup sweep at 17..64 tokens")
     ap.add_argument("--wave-n", type=int, default=None,
                     help="time only the candidates of this decode kernel family (0, 1, 2)")
     ap.add_argument("--shapes-from", default=None,
@@ -188,6 +286,12 @@ def main(argv=None):
         return 0
     if args.out is None:
         ap.error("the output CSV is required")
+    if args.route or args.w16:
+        with open(args.out, "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(ROUTE_FIELDS if args.route else W16_FIELDS)
+            (route if args.route else w16)(w)
+        return 0
     if args.compare:
         shapes = EVAL_SHAPES + [(M, 11008, 4096) for M in (1, 8, 16, 32, 64)]
         with open(args.out, "w", newline="") as f:
