@@ -239,14 +239,19 @@ def test_gemm_70b_layers(K, N):
     torch.cuda.empty_cache()
 
 
-def test_gemm_prefill_tm4_stream_k_full():
-    """The default plan at K = 11008, N = 4096, M = 768 is stream-K with
-    TM = 4 (long K, tiles that fill at most 15/16 of the CUs); compared in
-    full."""
+@pytest.mark.parametrize("M,K,N,tm,ranges", [
+    (768, 11008, 4096, 8, 192),     # TM 4 tiles fill the CUs: TM 8, each of 96 tiles in two ranges
+    (384, 11008, 4096, 4, 192),     # 96 TM 4 tiles, two ranges each
+    (160, 8192, 10240, 4, 240),     # 120 TM 4 tiles (the last m-block ragged), two ranges each
+])
+def test_gemm_prefill_split_tiles_full(M, K, N, tm, ranges):
+    """The default plans of long-K layers whose tiles fit one round split
+    every tile into equal K ranges (no range straddles two tiles); compared
+    in full."""
     from w4a8_quantized_linear_amd import gemm_w4a8_plan
-    p = gemm_w4a8_plan(768, 4096, 11008)
-    assert p["kind"] == 1 and p["mt"] == 4 and p["splitk"] > 1 and p["ws_bytes"] > 0, p
-    _gemm_case(3, 768, 11008, 4096)
+    p = gemm_w4a8_plan(M, N, K)
+    assert p["kind"] == 1 and p["mt"] == tm and p["splitk"] == ranges and p["ws_bytes"] > 0, p
+    _gemm_case(3, M, K, N)
 
 
 def test_gemm_without_workspace_long_k():

@@ -230,14 +230,20 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
         p = selected_plan(M, N, K, p);
 
     // many tokens: the matrix-core kernel with (16 TM) x 256 workgroup tiles.
-    // Rules fitted to rocprofv3 sweeps (TM x stream-K on/off, M = 128..4096,
-    // the 7B and 70B shapes) on MI355X:
-    //  * long K (>= 64 groups) with few tiles: stream-K over all CUs, with the
-    //    largest-count tile (TM 4, else 8) that still leaves the CUs under
-    //    60% filled by whole tiles; up to 96 groups TM 4 is kept while its
-    //    tiles fill at most 15/16 of the CUs (its partial sums are half the
-    //    size, which outweighs its slower MFMA rate when each range holds few
-    //    groups; measured 12-19% faster on K = 8192 and 11008 at M = 96..768);
+    // Rules fitted to graph-timed sweeps on MI355X (TM x splits per tile,
+    // M = 96..768, K = 4096..28672, the 7B and 70B layers):
+    //  * when TM 4 tiles fit one round (at most one per CU): split every tile
+    //    into s equal K ranges, s = CUs / tiles (at most 4, and at least 16
+    //    groups per range), so that P = tiles x s workgroups still fit one
+    //    round and no range straddles two tiles.  Where TM 4 allows no split
+    //    (s = 1) but TM 8 tiles split in two still fit one round and K has
+    //    at least 80 groups, TM 8 with two ranges per tile (at 64 groups TM 4
+    //    unsplit stayed 8-10% ahead).  Measured against
+    //    P = CUs ranges (which straddle tiles): K = 11008, N = 4096, M = 160
+    //    36.2 against 50.7 us, M = 384 39.8 against 53.7; K = 8192, N = 10240,
+    //    M = 160 34.6 against 48.2; K = 28672, N = 8192, M = 384 112.6 against
+    //    145.4 (TM 8, two ranges); with whole tiles past one round,
+    //    splitting lost everywhere;
     //  * otherwise one workgroup per tile, TM minimising workgroup rounds x
     //    TM x the relative time per MFMA at that TM (1.0, 1.23, 1.75 for
     //    TM 16, 8, 4: smaller tiles rebuild each weight for fewer tokens).
@@ -252,15 +258,16 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
         if (M > 32 && M <= 64 && N >= 32768)
             tm = 4;   // 33..64 tokens on the widest N: activations shared through LDS
         else if (!decode_m) {
-            if (G >= 64 && tiles_of(4) * 10 < cus * 6) {
-                tm = 4;
-                ranges = cus;
-            } else if (G >= 64 && G <= 96 && tiles_of(4) * 16 <= cus * 15) {
-                tm = 4;
-                ranges = cus;
-            } else if (G >= 64 && tiles_of(8) * 10 < cus * 6) {
-                tm = 8;
-                ranges = cus;
+            const int64_t t4 = tiles_of(4), t8 = tiles_of(8);
+            if (t4 <= cus) {
+                const int64_t s4 = std::max<int64_t>(1, std::min<int64_t>({cus / t4, G / 16, 4}));
+                if (s4 == 1 && G >= 80 && t8 * 2 <= cus) {
+                    tm = 8;
+                    ranges = t8 * 2;
+                } else {
+                    tm = 4;
+                    ranges = s4 > 1 ? t4 * s4 : 0;
+                }
             } else {
                 const struct { int tm; double rel; } cand[] = {{16, 1.0}, {8, 1.23}, {4, 1.75}};
                 double best = 0;

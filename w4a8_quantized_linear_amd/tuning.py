@@ -27,6 +27,10 @@ decode plan (every candidate) against the many-token kernel at each TM, and the 
 gemm_w4a8 picks: the evidence behind sending 65..128 tokens to the decode kernels
 when the many-token tiles are few.
 
+--splits OUT.csv times the many-token kernel at 96..768 tokens on long-K layers for TM 4
+and 8 with every tile split into s = 1, 2, 3, 4, 6, 8 equal K ranges (W4A8_PREFILL_P =
+tiles x s) and TM 16 whole, next to the plan gemm_w4a8 picks.
+
 --w16 OUT.csv times gemm_w4a16 at 17, 32, 48 and 64 tokens on the 7B layers for
 every (tiles per workgroup, token tiles per workgroup) and the launcher's own
 choice, and checks that two token tiles give the bits of one.
@@ -124,6 +128,9 @@ COMPARE_FIELDS = ("M", "N", "K", "rules_plan", "selector_plan", "rules_us", "sel
 ROUTE_FIELDS = ("M", "N", "K", "decode_best_us", "decode_best_plan", "prefill_best_us", "prefill_best_tm",
                 "picked_kind", "picked_us")
 W16_FIELDS = ("M", "N", "K", "nt", "mt", "us", "default_us")
+SPLIT_FIELDS = ("M", "N", "K", "tm", "splits", "ranges", "us", "picked_plan", "picked_us")
+SPLIT_LAYERS = ((8192, 10240), (11008, 4096), (28672, 8192), (8192, 8192), (14336, 4096), (4096, 11008),
+                (4096, 4096), (8192, 28672))
 ROUTE_LAYERS = ((4096, 11008), (11008, 4096), (8192, 10240), (4096, 22016), (4096, 12288), (28672, 8192))
 W16_LAYERS = ((4096, 11008), (4096, 4096), (4096, 22016), (11008, 4096), (4096, 12288))
 
@@ -175,6 +182,42 @@ def route(writer, ms=(72, 96, 112, 128), reps=10):
             writer.writerow([M, N, K, round(best_d, 3), plan_d, round(best_p, 3), tm_p, picked["kind"], round(us, 3)])
             print("route M=%d N=%d K=%d decode %.2f us prefill %.2f us picked kind %d %.2f us"
                   % (M, N, K, best_d, best_p, picked["kind"], us), flush=True)
+
+
+def splits(writer, ms=(96, 160, 256, 384, 512, 768), reps=10):
+    """Many-token kernel: TM 4 / 8 with each tile split into s equal K ranges, TM 16 whole."""
+    import torch
+
+    from w4a8_quantized_linear_amd import _lib, gemm_w4a8, gemm_w4a8_plan
+    dev = torch.device("cuda:0")
+    pool = torch.randint(0, 256, (1 << 30,), dtype=torch.uint8, device=dev)
+    ws = _lib.workspace(dev, 1 << 30)
+    keys = ("W4A8_PREFILL_TM", "W4A8_PREFILL_P")
+    for (K, N) in SPLIT_LAYERS:
+        views = _weight_views(pool, N, K)
+        s0 = (torch.rand(N, device=dev) * 1e-3).half()
+        nblk = -(-N // 256)
+        for M in ms:
+            qx = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev)
+            sa = torch.rand(M, device=dev) * 0.01
+            y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            call = lambda r: gemm_w4a8(qx, sa, views[r % len(views)], s0, N, y=y, ws=ws)
+            for k in keys:
+                os.environ.pop(k, None)
+            p = gemm_w4a8_plan(M, N, K)
+            picked = "%d:%d:%d" % (p["kind"], p["mt"], p["splitk"])
+            picked_us = graph_time(call, reps)
+            runs = [(tm, s) for tm in (4, 8) for s in (1, 2, 3, 4, 6, 8)] + [(16, 1)]
+            for tm, s in runs:
+                tiles = -(-M // (16 * tm)) * nblk
+                P = tiles * s if s > 1 else 0
+                if P > 512 or (s > 1 and (K // 128) // s < 4):
+                    continue
+                os.environ["W4A8_PREFILL_TM"], os.environ["W4A8_PREFILL_P"] = str(tm), str(P)
+                writer.writerow([M, N, K, tm, s, P, round(graph_time(call, reps), 3), picked, round(picked_us, 3)])
+            for k in keys:
+                os.environ.pop(k, None)
+            print("splits M=%d N=%d K=%d picked %s %.2f us" % (M, N, K, picked, picked_us), flush=True)
 
 
 def w16(writer, ms=(17, 32, 48, 64), reps=20):
@@ -273,6 +316,7 @@ def main(argv=None):
     ap.add_argument("--compare", action="store_true")
     ap.add_argument("--route", action="store_true", help="decode against many-token kernel at 72..128 tokens")
     ap.add_argument("--w16", action="store_true", help="gemm_w4a16 tiles-per-workgroup sweep at 17..64 tokens")
+    ap.add_argument("--splits", action="store_true", help="many-token kernel: splits per tile at 96..768 tokens")
     ap.add_argument("--wave-n", type=int, default=None,
                     help="time only the candidates of this decode kernel family (0, 1, 2)")
     ap.add_argument("--shapes-from", default=None,
@@ -286,11 +330,12 @@ def main(argv=None):
         return 0
     if args.out is None:
         ap.error("the output CSV is required")
-    if args.route or args.w16:
+    if args.route or args.w16 or args.splits:
+        fields, fn = (ROUTE_FIELDS, route) if args.route else ((W16_FIELDS, w16) if args.w16 else (SPLIT_FIELDS, splits))
         with open(args.out, "w", newline="") as f:
             w = csv.writer(f)
-            w.writerow(ROUTE_FIELDS if args.route else W16_FIELDS)
-            (route if args.route else w16)(w)
+            w.writerow(fields)
+            fn(w)
         return 0
     if args.compare:
         shapes = EVAL_SHAPES + [(M, 11008, 4096) for M in (1, 8, 16, 32, 64)]
