@@ -61,8 +61,9 @@ def test_noalloc_matches_gemm_w4a8_on_calls_in_a_row():
 
 
 def test_noalloc_rejects_a_plan_larger_than_the_scratch():
-    """The 70B down projection at 512 tokens plans stream-K with TM = 8 over
-    256 ranges: 67,174,400 bytes of workspace, more than the 64 MiB scratch.
+    """The 70B down projection at 512 tokens plans TM = 8 with each of its 128
+    tiles split into two K ranges (256 ranges): 67,174,400 bytes of
+    workspace, more than the 64 MiB scratch.
     The call returns W4A8_E_SCRATCH and launches nothing (y keeps its
     contents); M = 0 stays a no-op."""
     import torch
