@@ -373,8 +373,10 @@ hipError_t launch_gemm_w4a16(const uint16_t *x, int64_t M, int64_t K, int64_t ld
         // they fit, one tile per workgroup.  Measured on MI355X, M = 1: K =
         // 4096, N = 11008 8.0 us against 9.9 for the best register form; K =
         // 8192, N = 28672 24.1 against 28.9.  With 256 tiles the register
-        // form is 2-10% faster (fewer workgroups hide less of the staging),
-        // and at 8 and more tokens the two are within 3%.
+        // form is 2-10% faster (fewer workgroups hide less of the staging).
+        // At 6 and 8 tokens (rows staged in up to 72 KB, a build that allowed
+        // it) staging was 4-30% slower on the 7B layers (K = 4096, N = 11008,
+        // M = 8: 11.0-12.6 us against 10.6).
         // W4A8_W16_XS=0|1 and W4A8_W16_NT=1|2|4 override, for sweeps
         bool xs = a.M <= 4 && N / kTileN >= 512 && w16_xs_bytes(a.M, K) > 0;
         if (const char *env = std::getenv("W4A8_W16_XS"))
