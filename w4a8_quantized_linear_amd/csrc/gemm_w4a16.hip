@@ -222,8 +222,8 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_w4a16_kernel(W16Args a)
                 const v4i bw = {(int)b[h][d0][0], (int)b[h][d0][1], (int)b[h][d0 + 1][0], (int)b[h][d0 + 1][1]};
 #pragma unroll
                 for (int mt = 0; mt < MT; mt++)
-                    acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, s.x[mt][q]),
-                                                                        __builtin_bit_cast(h8, bw), acc[mt][t], 0, 0, 0);
+                    acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        __builtin_bit_cast(h8, s.x[mt][q]), __builtin_bit_cast(h8, bw), acc[mt][t], 0, 0, 0);
             }
         }
         load(s, i + kDepth, d);

@@ -331,7 +331,8 @@ def main(argv=None):
     if args.out is None:
         ap.error("the output CSV is required")
     if args.route or args.w16 or args.splits:
-        fields, fn = (ROUTE_FIELDS, route) if args.route else ((W16_FIELDS, w16) if args.w16 else (SPLIT_FIELDS, splits))
+        fields, fn = {"route": (ROUTE_FIELDS, route), "w16": (W16_FIELDS, w16),
+                      "splits": (SPLIT_FIELDS, splits)}[next(k for k in ("route", "w16", "splits") if getattr(args, k))]
         with open(args.out, "w", newline="") as f:
             w = csv.writer(f)
             w.writerow(fields)
