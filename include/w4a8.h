@@ -229,9 +229,10 @@ w4a8_status w4a8_hbm_read(const void *buf, size_t bytes, uint32_t *sink, hipStre
  * desc[9] = the dynamic LDS bytes per workgroup its launch requests.
  *
  * gemm_w4a8_decode_candidates: the decode-kernel plans that can run (M <=
- * 128; gemm_w4a8 takes the decode kernels up to 64 tokens, and up to 128
- * when the prefill kernel's 64 x 256 tiles would fill under half of the
- * compute units): *count is their number; the first max_plans are written to plans as
+ * 256; gemm_w4a8 takes the decode kernels up to 64 tokens, up to 128 when
+ * the prefill kernel's 64 x 256 tiles would fill under half of the compute
+ * units, and up to 256 when M x N is at most 2^20 as well): *count is their
+ * number; the first max_plans are written to plans as
  * rows of seven int32 (m-tiles, n-tiles, split-K, waves, depth, staged,
  * waves splitting N).  Each row, set in W4A8_DECODE_PLAN as
  * "mt,nt,splitk,waves,depth,staged,wave_n", makes gemm_w4a8 run that plan

@@ -304,13 +304,13 @@ CONFIG_KN = [(512, 512), (4096, 12288), (4096, 4096), (4096, 22016), (11008, 409
 
 @pytest.mark.parametrize("K,N", CONFIG_KN)
 def test_every_plan_fits_its_lds_with_and_without_workspace(lib, K, N):
-    """For every config shape at 1..128 tokens (and a few prefill token
-    counts), the plan gemm_w4a8 launches with a workspace and the one it
+    """For every config shape at 1..128 tokens (and a few more token counts
+    up to 4096), the plan gemm_w4a8 launches with a workspace and the one it
     launches with ws == NULL both request LDS within the kernel's limit, and
     the NULL-workspace plan needs no workspace.  (An unsplit N-split plan at
     K = 28672 once asked for 137 KB, over the 128 KB decode limit.)"""
     from w4a8_quantized_linear_amd import _lib
-    for M in list(range(1, 129)) + [256, 512, 768, 4096]:
+    for M in list(range(1, 129)) + [136, 160, 200, 256, 257, 512, 768, 4096]:
         for with_ws in (True, False):
             d = _lib.gemm_w4a8_plan_detail(M, N, K, with_ws)
             limit = 160 * 1024 if d["kind"] == 1 else 128 * 1024
@@ -319,6 +319,38 @@ def test_every_plan_fits_its_lds_with_and_without_workspace(lib, K, N):
                 assert d["ws_bytes"] == 0 and d["splitk"] in (0, 1), (M, d)
             else:
                 assert d == dict(_lib.gemm_w4a8_plan(M, N, K), lds_bytes=d["lds_bytes"])
+
+
+@pytest.mark.parametrize("M,K,N,kind", [
+    (64, 4096, 11008, 0), (128, 11008, 4096, 0), (128, 4096, 22016, 1),
+    (129, 11008, 4096, 0), (256, 11008, 4096, 0), (256, 4096, 2048, 0), (192, 13824, 5120, 0),
+    (224, 13824, 5120, 1), (257, 11008, 4096, 1), (160, 28672, 8192, 1), (256, 4096, 11008, 1),
+    (160, 8192, 6144, 0), (165, 16512, 5760, 1), (136, 9984, 7296, 1)])
+def test_token_count_routes(lib, M, K, N, kind):
+    """gemm_w4a8 takes the decode kernels up to 64 tokens, up to 128 while
+    the 64 x 256 many-token tiles would fill under half of the CUs, and up
+    to 256 on layers with at most 2^20 outputs (M x N) whose weights are
+    small (N x K <= 2^26) or whose four-m-tile workgroups fit one round on
+    the CUs; the rest goes to the matrix-core kernel."""
+    from w4a8_quantized_linear_amd import _lib
+    p = _lib.gemm_w4a8_plan(M, N, K)
+    assert p["kind"] == kind, (M, K, N, p)
+
+
+@pytest.mark.parametrize("M,K,N,plan", [
+    (129, 11008, 4096, (4, 4, 1, 4, 0, 0)), (256, 11008, 4096, (4, 4, 1, 4, 0, 0)),
+    (256, 2048, 4096, (2, 4, 1, 4, 1, 1)), (192, 13824, 5120, (4, 4, 1, 4, 0, 0)),
+    (200, 4096, 1024, (2, 2, 1, 4, 0, 0)), (160, 4096, 768, (1, 2, 1, 8, 1, 0)),
+    (160, 12288, 768, (1, 2, 1, 8, 0, 0)), (200, 28672, 2048, (4, 4, 2, 4, 0, 0)),
+    (160, 28672, 2048, (2, 4, 4, 4, 1, 1)), (160, 8192, 6144, (2, 4, 1, 4, 0, 0)),
+    (232, 4096, 4096, (2, 4, 1, 4, 1, 1)), (252, 24192, 1152, (2, 4, 4, 4, 1, 1))])
+def test_wide_decode_plan_rule(lib, M, K, N, plan):
+    """Past 128 tokens the decode plan comes from a fixed tree (the learned
+    selector, trained on 1..64 tokens, is not consulted): (m-tiles, n-tiles,
+    split-K, waves, staged, waves splitting N) for shapes on each branch."""
+    from w4a8_quantized_linear_amd import _lib
+    p = _lib.gemm_w4a8_plan(M, N, K)
+    assert p["kind"] == 0 and (p["mt"], p["nt"], p["splitk"], p["waves"], p["xstage"], p["wave_n"]) == plan, p
 
 
 def test_gemm_k_limit(lib):

@@ -523,16 +523,21 @@ def test_workspace_shared_across_shapes_and_kernels():
                 os.environ[k] = v
 
 
-@pytest.mark.parametrize("M,K,N", [(96, 4096, 11008), (128, 11008, 4096), (113, 8192, 10240)])
+@pytest.mark.parametrize("M,K,N", [(96, 4096, 11008), (128, 11008, 4096), (113, 8192, 10240),
+                                   (256, 11008, 4096), (200, 8192, 2048), (137, 4096, 4096), (160, 4096, 768),
+                                   (232, 4096, 4096), (160, 28672, 2048), (200, 28672, 2048), (160, 8192, 6144),
+                                   (252, 24192, 1152)])
 def test_gemm_mid_m_takes_the_decode_kernels(M, K, N):
     """65..128 tokens on layers whose 64 x 256 prefill tiles would leave more
-    than half of the CUs idle run on the decode kernels; every row compared."""
+    than half of the CUs idle, and 129..256 tokens on layers with at most
+    2^20 outputs, run on the decode kernels; every row compared."""
     from w4a8_quantized_linear_amd import gemm_w4a8_plan
     assert gemm_w4a8_plan(M, N, K)["kind"] == 0
     _gemm_case(4, M, K, N)
 
 
-@pytest.mark.parametrize("M,K,N", [(5, 1152, 272), (24, 3072, 1040), (40, 2048, 528), (100, 1152, 272)])
+@pytest.mark.parametrize("M,K,N", [(5, 1152, 272), (24, 3072, 1040), (40, 2048, 528), (100, 1152, 272),
+                                   (233, 1152, 272)])
 def test_every_decode_candidate_is_exact(M, K, N):
     """Every plan the learned selector may pick (gemm_w4a8_decode_candidates)
     runs, and gives the oracle's INT32 accumulators bit for bit."""

@@ -4,8 +4,9 @@
 // parameters and pick an instantiation per shape; here the pick is a small
 // deterministic rule of (M, N, K), so the workspace size a caller queries and
 // the plan gemm_w4a8 launches always agree.  W4A8_DECODE_PLAN=
-// "mt,nt,splitk[,waves[,depth[,xstage]]]" overrides the decode choice (for
-// tuning sweeps); an override that names no instantiated variant is ignored.
+// "mt,nt,splitk[,waves[,depth[,xstage[,wave_n]]]]" overrides the decode
+// choice and sends every M <= 256 to the decode kernels (for tuning sweeps);
+// an override that names no instantiated variant is ignored.
 #include <algorithm>
 #include <atomic>
 #include <cstdio>
@@ -194,6 +195,47 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
             p.nt = 4;
             p.splitk = 4;
         }
+    } else if (M > 128) {
+        // 129..256 tokens (layers with at most 2^20 outputs, below): a small
+        // decision tree over the weight size, N, K and the workgroup counts
+        // of the plan families, fitted (least total log-time over the best
+        // plan) to graph-timed sweeps of every decode plan on MI355X at
+        // 129..256 tokens: 150 random shapes (N = 512..7296, K = 2048..28672),
+        // 60 more and 15 layers of the 7B / 70B family.  Its plan runs at
+        // 1.02-1.05x the best plan's time on average (at most 1.24x).
+        const int64_t cus = num_cus();
+        auto wg = [&](int mt, int nt) { return (M + 16 * mt - 1) / (16 * mt) * ((ntiles + nt - 1) / nt); };
+        auto use = [&](int mt, int nt, int s, int waves, bool xstage, int wave_n) {
+            p.mt = mt;
+            p.nt = nt;
+            p.splitk = s;
+            p.waves = waves;
+            p.xstage = xstage;
+            p.wave_n = wave_n;
+        };
+        if (N * K <= (int64_t{1} << 25)) {
+            if (wg(1, 2) <= cus)
+                use(1, 2, 1, 8, K <= 8192, 0);             // one m-tile, the token rows staged when short
+            else if (wg(2, 4) <= cus + cus / 2 && K >= 12288)
+                use(2, 4, 4, 4, true, 1);                  // few workgroups, long K: split K four ways
+            else if (wg(2, 4) <= cus + cus / 2)
+                use(2, 2, 1, 4, false, 0);
+            else
+                use(2, 4, 1, 4, true, 1);                  // waves splitting N
+        } else if (N <= 2560) {
+            if (wg(2, 4) <= cus * 3 / 4)
+                use(2, 4, 4, 4, true, 1);
+            else
+                use(4, 4, 2, 4, false, 0);
+        } else if (wg(4, 4) <= cus) {
+            use(4, 4, 1, 4, false, 0);
+        } else {
+            use(2, 4, 1, 4, false, 0);
+        }
+        if (!launchable(p, M, N, K)) {   // staged and N-split forms need LDS that grows with K
+            p.xstage = false;
+            p.wave_n = 0;
+        }
     } else if (K >= 8192 && N >= 8192) {
         p.mt = 4;
         p.nt = 4;
@@ -222,11 +264,27 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     const int64_t cus = num_cus();
     const int64_t nblk = (ntiles * kTileN + 255) / 256;
     auto tiles_of = [&](int t) { return (M + 16 * t - 1) / (16 * t) * nblk; };
-    const bool decode_m = M <= 64 || (M <= kDecodeMaxM && tiles_of(4) * 2 < cus);
+    // 129..256 tokens stay on the decode kernels on layers with at most 2^20
+    // outputs (M x N), unless the weights are large (N x K above 2^26) and
+    // four-m-tile workgroups would not fit one round on the CUs.  Graph-timed
+    // on MI355X against the matrix-core kernel's best TM and K split on the
+    // 277 shapes of the plan rule above: on the 274 it sends to the decode
+    // kernels their rule plan ran 0.92-4.6x the speed of the best matrix-core
+    // run (K = 11008, N = 4096, M = 136: 25.7 against 34.9 us; K = 13824,
+    // N = 5120, M = 160: 30.3 against 40.4); on the three it excludes, 0.64-
+    // 0.89x (K = 16512, N = 5760, M = 165: 71.1 against 45.3).  Wider layers
+    // stay on the matrix-core kernel (K = 28672, N = 8192, M = 160: 79.5
+    // against 88.7 for the best decode plan)
+    const int64_t wg44 = (M + 63) / 64 * ((ntiles + 3) / 4);
+    const bool decode_m = M <= 64 || (M <= 128 && tiles_of(4) * 2 < cus) ||
+                          (M <= kDecodeMaxM && M * N <= (int64_t{1} << 20) && tiles_of(4) * 2 < cus &&
+                           (N * K <= (int64_t{1} << 26) || wg44 <= cus));
 
     // the learned selector, when a model is compiled in: the candidate with
-    // the highest predicted bandwidth utilization (remembered per shape)
-    if (decode_m && selector_enabled())
+    // the highest predicted bandwidth utilization (remembered per shape);
+    // its model was trained on 1..64 tokens, and past 128 its picks ran up
+    // to 1.3x the best plan's time, so the rule above keeps those
+    if (decode_m && M <= 128 && selector_enabled())
         p = selected_plan(M, N, K, p);
 
     // many tokens: the matrix-core kernel with (16 TM) x 256 workgroup tiles.
@@ -253,7 +311,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     int64_t ranges = 0;
     if (const char *env = std::getenv("W4A8_PREFILL_TM"))
         tm = std::atoi(env);
-    if (!prefill_tm_supported(tm)) {
+    const bool force_decode = M <= kDecodeMaxM && std::getenv("W4A8_DECODE_PLAN") != nullptr;
+    if (!prefill_tm_supported(tm) && !force_decode) {
         tm = 0;
         if (M > 32 && M <= 64 && N >= 32768)
             tm = 4;   // 33..64 tokens on the widest N: activations shared through LDS

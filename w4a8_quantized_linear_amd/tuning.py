@@ -22,14 +22,21 @@ valid code pair and group parameter), timing does not depend on the values.
 plan gemm_w4a8 picks (rotating weight copies, as above) and prints the plans: the
 program that profiler runs (rocprofv3 --pmc ...) trace for the decode counters.
 
---route OUT.csv times, at 72, 96, 112 and 128 tokens on the 7B / 70B layers, the best
-decode plan (every candidate) against the many-token kernel at each TM, and the plan
-gemm_w4a8 picks: the evidence behind sending 65..128 tokens to the decode kernels
-when the many-token tiles are few.
+--route OUT.csv times, at 72..256 tokens on the 7B / 70B layers and on narrow layers,
+the best decode plan (every candidate) against the many-token kernel at each TM and
+K split, and the plan gemm_w4a8 picks: the evidence behind sending 65..128 tokens to
+the decode kernels when the many-token tiles are few, and 129..256 tokens when the
+layer has at most 2^20 outputs.
 
 --splits OUT.csv times the many-token kernel at 96..768 tokens on long-K layers for TM 4
 and 8 with every tile split into s = 1, 2, 3, 4, 6, 8 equal K ranges (W4A8_PREFILL_P =
 tiles x s) and TM 16 whole, next to the plan gemm_w4a8 picks.
+
+--wide OUT.csv [--shapes 150 --seed 5] times, on random shapes with 129..256 tokens and
+at most 2^20 outputs, every decode plan, the many-token kernel at TM 4 / 8 with 1..4
+K ranges per tile, and the plan gemm_w4a8 picks; --wide-layers does the same on 15
+7B / 70B layers at 136..256 tokens.  The data behind the 129..256-token route and
+its decode plan tree.
 
 --w16 OUT.csv times gemm_w4a16 at 17, 32, 48 and 64 tokens on the 7B layers for
 every (tiles per workgroup, token tiles per workgroup) and the launcher's own
@@ -125,13 +132,16 @@ def measure(shapes, tag, writer, reps=10, wave_n=None):
 
 
 COMPARE_FIELDS = ("M", "N", "K", "rules_plan", "selector_plan", "rules_us", "selector_us", "ratio")
-ROUTE_FIELDS = ("M", "N", "K", "decode_best_us", "decode_best_plan", "prefill_best_us", "prefill_best_tm",
-                "picked_kind", "picked_us")
+ROUTE_FIELDS = ("M", "N", "K", "decode_best_us", "decode_best_plan", "prefill_best_us", "prefill_best_cfg",
+                "picked_plan", "picked_us")
 W16_FIELDS = ("M", "N", "K", "nt", "mt", "us", "default_us")
 SPLIT_FIELDS = ("M", "N", "K", "tm", "splits", "ranges", "us", "picked_plan", "picked_us")
 SPLIT_LAYERS = ((8192, 10240), (11008, 4096), (28672, 8192), (8192, 8192), (14336, 4096), (4096, 11008),
                 (4096, 4096), (8192, 28672))
 ROUTE_LAYERS = ((4096, 11008), (11008, 4096), (8192, 10240), (4096, 22016), (4096, 12288), (28672, 8192))
+# narrow layers (N <= 6144) outside the set the 129..256-token plan rule was fitted on
+ROUTE_NARROW_LAYERS = ((3072, 3072), (6144, 2048), (18432, 4096), (7168, 4096), (12288, 1536), (5120, 5120),
+                       (8192, 3072))
 W16_LAYERS = ((4096, 11008), (4096, 4096), (4096, 22016), (11008, 4096), (4096, 12288))
 
 
@@ -142,8 +152,8 @@ def _weight_views(pool, N, K):
     return [pool[i * stride:i * stride + wb] for i in range(min(max(1, (1 << 30) // stride), 64))]
 
 
-def route(writer, ms=(72, 96, 112, 128), reps=10):
-    """Best decode plan against the many-token kernel (each TM) per shape."""
+def route(writer, ms=(72, 96, 112, 128, 136, 160, 192, 256), reps=10):
+    """Best decode plan against the many-token kernel's best TM and K split per shape."""
     import torch
 
     from w4a8_quantized_linear_amd import _lib, gemm_w4a8, gemm_w4a8_decode_candidates, gemm_w4a8_plan
@@ -151,10 +161,14 @@ def route(writer, ms=(72, 96, 112, 128), reps=10):
     pool = torch.randint(0, 256, (1 << 30,), dtype=torch.uint8, device=dev)
     keys = ("W4A8_DECODE_PLAN", "W4A8_PREFILL_TM", "W4A8_PREFILL_P")
     fields = ("mt", "nt", "splitk", "waves", "depth", "xstage", "wave_n")
-    ws = _lib.workspace(dev, 512 << 20)
-    for (K, N) in ROUTE_LAYERS:
+    ws = _lib.workspace(dev, 1 << 30)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    for (K, N) in ROUTE_LAYERS + ROUTE_NARROW_LAYERS:
         views = _weight_views(pool, N, K)
+        nblk = -(-N // 256)
         for M in ms:
+            if M > 128 and (K, N) in ROUTE_LAYERS and M not in (160, 256):
+                continue
             qx = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev)
             sa = torch.rand(M, device=dev) * 0.01
             s0 = (torch.rand(N, device=dev) * 1e-3).half()
@@ -169,19 +183,108 @@ def route(writer, ms=(72, 96, 112, 128), reps=10):
                 if us < best_d:
                     best_d, plan_d = us, ",".join(str(v) for v in c)
             os.environ.pop("W4A8_DECODE_PLAN", None)
-            best_p, tm_p = float("inf"), 0
+            best_p, cfg_p = float("inf"), ""
             for tm in (4, 8, 16):
-                os.environ["W4A8_PREFILL_TM"] = str(tm)
-                us = graph_time(call, reps)
-                if us < best_p:
-                    best_p, tm_p = us, tm
+                tiles = -(-M // (16 * tm)) * nblk
+                for s in ((1, 2, 3, 4) if tm < 16 else (1,)):
+                    if s > 1 and (tiles * s > cus or (K // 128) // s < 16):
+                        continue
+                    os.environ["W4A8_PREFILL_TM"] = str(tm)
+                    os.environ["W4A8_PREFILL_P"] = str(tiles * s if s > 1 else 0)
+                    us = graph_time(call, reps)
+                    if us < best_p:
+                        best_p, cfg_p = us, "tm%d s%d" % (tm, s)
             for k in keys:
                 os.environ.pop(k, None)
-            picked = gemm_w4a8_plan(M, N, K)
+            p = gemm_w4a8_plan(M, N, K)
+            picked = ("%d:" % p["kind"]) + ",".join(str(p[f]) for f in fields)
             us = graph_time(call, reps)
-            writer.writerow([M, N, K, round(best_d, 3), plan_d, round(best_p, 3), tm_p, picked["kind"], round(us, 3)])
-            print("route M=%d N=%d K=%d decode %.2f us prefill %.2f us picked kind %d %.2f us"
-                  % (M, N, K, best_d, best_p, picked["kind"], us), flush=True)
+            writer.writerow([M, N, K, round(best_d, 3), plan_d, round(best_p, 3), cfg_p, picked, round(us, 3)])
+            print("route M=%d N=%d K=%d decode %.2f us prefill %.2f us picked %s %.2f us"
+                  % (M, N, K, best_d, best_p, picked, us), flush=True)
+
+
+WIDE_FIELDS = ("M", "N", "K", "kind", "plan", "us")
+# 15 layers of the 7B / 70B family and their tensor-parallel shards (K, N)
+WIDE_LAYERS = ((11008, 4096), (14336, 4096), (28672, 4096), (8192, 4096), (5120, 4096), (4096, 4096),
+               (11008, 2048), (8192, 2048), (4096, 2048), (28672, 2048), (13824, 5120), (8192, 6144),
+               (4096, 6144), (8192, 1024), (2048, 4096))
+
+
+def wide_shapes(n, seed):
+    """Random (M, N, K) with 129..256 tokens and at most 2^20 outputs: M
+    uniform, K log-uniform in 2048..28672, N log-uniform in 512..2^20 / M
+    (multiples of 128)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(rng.integers(129, 257))
+        K = 128 * int(round(2 ** rng.uniform(math.log2(16), math.log2(224))))
+        N = 128 * int(round(2 ** rng.uniform(math.log2(4), math.log2(((1 << 20) // M) / 128))))
+        if N >= 512 and M * N <= (1 << 20):
+            out.append((M, N, K))
+    return out
+
+
+def wide(writer, shapes, reps=10):
+    """129..256 tokens: every decode candidate, the many-token kernel at TM 4 / 8
+    with every tile split into s = 1..4 K ranges, and the plan gemm_w4a8 picks."""
+    import torch
+
+    from w4a8_quantized_linear_amd import _lib, gemm_w4a8, gemm_w4a8_decode_candidates, gemm_w4a8_plan
+    dev = torch.device("cuda:0")
+    pool = torch.randint(0, 256, (1 << 30,), dtype=torch.uint8, device=dev)
+    ws = _lib.workspace(dev, 1 << 30)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    fields = ("mt", "nt", "splitk", "waves", "depth", "xstage", "wave_n")
+    keys = ("W4A8_DECODE_PLAN", "W4A8_PREFILL_TM", "W4A8_PREFILL_P")
+    ratios, route = [], []
+    for (M, N, K) in shapes:
+        views = _weight_views(pool, N, K)
+        qx = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev)
+        sa = torch.rand(M, device=dev) * 0.01
+        s0 = (torch.rand(N, device=dev) * 1e-3).half()
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        call = lambda r: gemm_w4a8(qx, sa, views[r % len(views)], s0, N, y=y, ws=ws)
+        dec, pre = {}, {}
+        for c in gemm_w4a8_decode_candidates(M, N, K):
+            os.environ["W4A8_DECODE_PLAN"] = ",".join(str(v) for v in c)
+            if tuple(gemm_w4a8_plan(M, N, K)[f] for f in fields) == c:
+                dec[os.environ["W4A8_DECODE_PLAN"]] = graph_time(call, reps)
+        os.environ.pop("W4A8_DECODE_PLAN", None)
+        nblk = -(-N // 256)
+        for tm in (4, 8):
+            tiles = -(-M // (16 * tm)) * nblk
+            for sp in (1, 2, 3, 4):
+                if sp > 1 and (tiles * sp > cus or (K // 128) // sp < 16):
+                    continue
+                os.environ["W4A8_PREFILL_TM"] = str(tm)
+                os.environ["W4A8_PREFILL_P"] = str(tiles * sp if sp > 1 else 0)
+                pre["tm%d s%d" % (tm, sp)] = graph_time(call, reps)
+        for k in keys:
+            os.environ.pop(k, None)
+        p = gemm_w4a8_plan(M, N, K)
+        picked = ("%d:" % p["kind"]) + ",".join(str(p[f]) for f in fields)
+        us = graph_time(call, reps)
+        for kind, d in (("decode", dec), ("prefill", pre)):
+            for plan, t in d.items():
+                writer.writerow([M, N, K, kind, plan, round(t, 3)])
+        writer.writerow([M, N, K, "picked", picked, round(us, 3)])
+        bd, bp = min(dec.values()), min(pre.values())
+        if p["kind"] == 0:
+            ratios.append(us / bd)
+        route.append((p["kind"], bp / us if p["kind"] == 0 else bd / us))
+        print("wide M=%d N=%d K=%d best decode %.2f us best prefill %.2f us picked %s %.2f us"
+              % (M, N, K, bd, bp, picked, us), flush=True)
+    if ratios:
+        geo = math.exp(sum(math.log(r) for r in ratios) / len(ratios))
+        print("picked decode plan / best decode plan: geomean %.3f, max %.3f over %d shapes"
+              % (geo, max(ratios), len(ratios)))
+    for kind in (0, 1):
+        r = [v for k, v in route if k == kind]
+        if r:
+            print("picked %s: the other kernel's best at %.2f-%.2fx the picked time (%d shapes)"
+                  % ("decode" if kind == 0 else "many-token", min(r), max(r), len(r)), flush=True)
 
 
 def splits(writer, ms=(96, 160, 256, 384, 512, 768), reps=10):
@@ -314,9 +417,12 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--eval", action="store_true")
     ap.add_argument("--compare", action="store_true")
-    ap.add_argument("--route", action="store_true", help="decode against many-token kernel at 72..128 tokens")
+    ap.add_argument("--route", action="store_true", help="decode against many-token kernel at 72..256 tokens")
     ap.add_argument("--w16", action="store_true", help="gemm_w4a16 tiles-per-workgroup sweep at 17..64 tokens")
     ap.add_argument("--splits", action="store_true", help="many-token kernel: splits per tile at 96..768 tokens")
+    ap.add_argument("--wide", action="store_true",
+                    help="129..256 tokens: every decode plan and many-token split, random shapes (--shapes, --seed)")
+    ap.add_argument("--wide-layers", action="store_true", help="as --wide, on 15 7B / 70B layers at 136..256 tokens")
     ap.add_argument("--wave-n", type=int, default=None,
                     help="time only the candidates of this decode kernel family (0, 1, 2)")
     ap.add_argument("--shapes-from", default=None,
@@ -330,6 +436,14 @@ def main(argv=None):
         return 0
     if args.out is None:
         ap.error("the output CSV is required")
+    if args.wide or args.wide_layers:
+        shapes = wide_shapes(args.shapes, args.seed) if args.wide else \
+            [(M, N, K) for (K, N) in WIDE_LAYERS for M in (136, 160, 192, 224, 256) if M * N <= (1 << 20)]
+        with open(args.out, "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(WIDE_FIELDS)
+            wide(w, shapes)
+        return 0
     if args.route or args.w16 or args.splits:
         fields, fn = {"route": (ROUTE_FIELDS, route), "w16": (W16_FIELDS, w16),
                       "splits": (SPLIT_FIELDS, splits)}[next(k for k in ("route", "w16", "splits") if getattr(args, k))]
