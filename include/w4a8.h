@@ -231,12 +231,13 @@ w4a8_status w4a8_hbm_read(const void *buf, size_t bytes, uint32_t *sink, hipStre
  * gemm_w4a8_decode_candidates: the decode-kernel plans that can run (M <=
  * 256; gemm_w4a8 takes the decode kernels up to 64 tokens, up to 128 when
  * the prefill kernel's 64 x 256 tiles would fill under half of the compute
- * units, and up to 256 when M x N is at most 2^20 as well): *count is their
- * number; the first max_plans are written to plans as
- * rows of seven int32 (m-tiles, n-tiles, split-K, waves, depth, staged,
- * waves splitting N).  Each row, set in W4A8_DECODE_PLAN as
+ * units, and up to 256 when M x N is at most 2^20 as well, except on very
+ * large weights whose four-m-tile workgroups would take two rounds): *count
+ * is their number; the first max_plans are written to plans as rows of
+ * seven int32 (m-tiles, n-tiles, split-K, waves, depth, staged, waves
+ * splitting N).  Each row, set in W4A8_DECODE_PLAN as
  * "mt,nt,splitk,waves,depth,staged,wave_n", makes gemm_w4a8 run that plan
- * (for tuning sweeps).
+ * on the decode kernels at any M <= 256 (for tuning sweeps).
  *
  * gemm_w4a8_selector_score: the compiled-in model's predicted fraction of the
  * HBM peak for one such plan row on a device with `cus` compute units, or a
@@ -244,8 +245,8 @@ w4a8_status w4a8_hbm_read(const void *buf, size_t bytes, uint32_t *sink, hipStre
  * The model follows the QFactory reading notes (6.2, "ML-based kernel
  * selector"): a small multilayer perceptron over the matrix shape and the
  * tiling parameters, trained on measured bandwidth utilization; gemm_w4a8
- * takes the candidate it scores highest (W4A8_SELECTOR=0 restores the fixed
- * rules).
+ * takes the candidate it scores highest at 1..64 tokens (W4A8_SELECTOR=0
+ * restores the fixed rules; past 64 tokens fixed decision trees pick).
  * ------------------------------------------------------------------------ */
 w4a8_status gemm_w4a8_plan(int64_t M, int64_t N, int64_t K, int64_t *desc);   /* desc: 9 int64 */
 

@@ -236,6 +236,37 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
             p.xstage = false;
             p.wave_n = 0;
         }
+    } else if (M > 64) {
+        // 65..128 tokens (where the decode kernels take them, below): a
+        // decision tree over the workgroup counts of the (1, 2), (2, 4) and
+        // (4, 4) tilings, N x K and K, fitted like the one above to
+        // graph-timed sweeps of every decode plan: 210 random shapes
+        // (M = 65..128, N = 512..16384, K = 2048..28672) and 26 7B / 70B and
+        // narrow layers at 72..128 tokens.  Its plan runs at 1.02-1.04x the
+        // best plan's time on average on each set (at most 1.26x); the
+        // selector's picks ran at 1.08-1.11x (at most 1.66x).
+        const int64_t cus = num_cus();
+        auto wg = [&](int mt, int nt) { return (M + 16 * mt - 1) / (16 * mt) * ((ntiles + nt - 1) / nt); };
+        p.splitk = 1;
+        if (wg(1, 2) <= 2 * cus) {
+            p.mt = wg(1, 2) <= cus ? 1 : 2;
+            p.nt = wg(1, 2) <= cus / 2 ? 1 : 2;
+            p.waves = wg(1, 2) <= cus / 2 || (p.mt == 2 && N * K < (int64_t{1} << 23)) ? 8 : 4;
+            p.xstage = p.mt == 2 && N * K < (int64_t{1} << 23);
+        } else if (wg(2, 4) <= 2 * cus) {
+            p.mt = wg(2, 4) <= cus || wg(4, 4) > cus ? 2 : 4;   // four m-tiles only in one round
+            p.nt = 4;
+        } else {
+            p.mt = 4;
+            p.nt = K <= 10240 ? 4 : 8;
+            p.splitk = K <= 10240 ? 1 : 2;
+            p.xstage = true;
+            p.wave_n = 1;   // waves splitting N
+        }
+        if (!launchable(p, M, N, K)) {
+            p.xstage = false;
+            p.wave_n = 0;
+        }
     } else if (K >= 8192 && N >= 8192) {
         p.mt = 4;
         p.nt = 4;
@@ -248,7 +279,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     p.splitk = (int)std::min<int64_t>(p.splitk, P);
     p.m_blocks = (M + 16 * p.mt - 1) / (16 * p.mt);
     p.n_blocks = (ntiles + p.nt - 1) / p.nt;
-    if (p.mt == 1 && p.splitk == 1) {
+    if (M <= 64 && p.mt == 1 && p.splitk == 1) {
         GemmPlan q = p;
         q.xstage = true;
         if (launchable(q, M, N, K) && decode_lds_bytes(q, M, K) <= 64 * 1024)
@@ -256,11 +287,14 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     }
     // 65..128 tokens stay on the decode kernels while the matrix-core
     // kernel's smallest tiles (64 tokens x 256 channels) would leave more than
-    // half of the CUs idle: measured on MI355X (graph-timed), M = 96 and 128
-    // at K = 4096, N = 11008: 18.7 / 20.0 us against 26.5 / 25.2; K = 11008,
-    // N = 4096: 19.8 / 19.0 against 50.5 / 51.2; K = 8192, N = 10240: 26.1 /
-    // 31.9 against 43.1 / 43.3; at N = 22016 (172 tiles) the matrix-core
-    // kernel stays ahead (27.0 / 26.4 against 27.8 / 29.4)
+    // half of the CUs idle, unless the weights are very large (N x K above
+    // 2^27) and four-m-tile workgroups would take two rounds.  Measured on
+    // MI355X (graph-timed) against the matrix-core kernel's best TM and K
+    // split, M = 96: K = 4096, N = 11008: 19.0 against 25.1 us; K = 11008,
+    // N = 4096: 18.2 against 34.3; K = 12288, N = 1536: 13.0 against 35.2.
+    // At N = 22016 (172 tiles) the matrix-core kernel stays ahead (27.1
+    // against 28.1), and on the excluded large weights it ran up to 1.35x
+    // faster (K = 19584, N = 8448, M = 122)
     const int64_t cus = num_cus();
     const int64_t nblk = (ntiles * kTileN + 255) / 256;
     auto tiles_of = [&](int t) { return (M + 16 * t - 1) / (16 * t) * nblk; };
@@ -276,15 +310,17 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     // stay on the matrix-core kernel (K = 28672, N = 8192, M = 160: 79.5
     // against 88.7 for the best decode plan)
     const int64_t wg44 = (M + 63) / 64 * ((ntiles + 3) / 4);
-    const bool decode_m = M <= 64 || (M <= 128 && tiles_of(4) * 2 < cus) ||
+    const bool decode_m = M <= 64 ||
+                          (M <= 128 && tiles_of(4) * 2 < cus && (N * K <= (int64_t{1} << 27) || wg44 <= cus)) ||
                           (M <= kDecodeMaxM && M * N <= (int64_t{1} << 20) && tiles_of(4) * 2 < cus &&
                            (N * K <= (int64_t{1} << 26) || wg44 <= cus));
 
     // the learned selector, when a model is compiled in: the candidate with
     // the highest predicted bandwidth utilization (remembered per shape);
-    // its model was trained on 1..64 tokens, and past 128 its picks ran up
-    // to 1.3x the best plan's time, so the rule above keeps those
-    if (decode_m && M <= 128 && selector_enabled())
+    // its model was trained on 1..64 tokens, and past 64 its picks ran
+    // 1.1x the best plan's time on average (up to 1.7x), so the trees above
+    // keep those
+    if (decode_m && M <= 64 && selector_enabled())
         p = selected_plan(M, N, K, p);
 
     // many tokens: the matrix-core kernel with (16 TM) x 256 workgroup tiles.

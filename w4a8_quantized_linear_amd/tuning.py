@@ -36,7 +36,9 @@ tiles x s) and TM 16 whole, next to the plan gemm_w4a8 picks.
 at most 2^20 outputs, every decode plan, the many-token kernel at TM 4 / 8 with 1..4
 K ranges per tile, and the plan gemm_w4a8 picks; --wide-layers does the same on 15
 7B / 70B layers at 136..256 tokens.  The data behind the 129..256-token route and
-its decode plan tree.
+its decode plan tree.  --mid does the same on random shapes with 65..128 tokens
+that the dispatcher sends to the decode kernels, --mid-layers on the 7B / 70B and
+narrow layers above at 72..128 tokens.
 
 --w16 OUT.csv times gemm_w4a16 at 17, 32, 48 and 64 tokens on the 7B layers for
 every (tiles per workgroup, token tiles per workgroup) and the launcher's own
@@ -222,6 +224,22 @@ def wide_shapes(n, seed):
         K = 128 * int(round(2 ** rng.uniform(math.log2(16), math.log2(224))))
         N = 128 * int(round(2 ** rng.uniform(math.log2(4), math.log2(((1 << 20) // M) / 128))))
         if N >= 512 and M * N <= (1 << 20):
+            out.append((M, N, K))
+    return out
+
+
+def mid_shapes(n, seed):
+    """Random (M, N, K) with 65..128 tokens on which gemm_w4a8 takes the decode
+    kernels (the 64 x 256 many-token tiles fill under half of 256 CUs): M
+    uniform, K log-uniform in 2048..28672, N log-uniform in 512..16384
+    (multiples of 128)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(rng.integers(65, 129))
+        K = 128 * int(round(2 ** rng.uniform(math.log2(16), math.log2(224))))
+        N = 128 * int(round(2 ** rng.uniform(math.log2(4), math.log2(128))))
+        if -(-M // 64) * -(-N // 256) * 2 < 256:
             out.append((M, N, K))
     return out
 
@@ -423,6 +441,8 @@ def main(argv=None):
     ap.add_argument("--wide", action="store_true",
                     help="129..256 tokens: every decode plan and many-token split, random shapes (--shapes, --seed)")
     ap.add_argument("--wide-layers", action="store_true", help="as --wide, on 15 7B / 70B layers at 136..256 tokens")
+    ap.add_argument("--mid", action="store_true", help="as --wide, on random shapes with 65..128 tokens")
+    ap.add_argument("--mid-layers", action="store_true", help="as --wide, on 7B / 70B and narrow layers at 72..128 tokens")
     ap.add_argument("--wave-n", type=int, default=None,
                     help="time only the candidates of this decode kernel family (0, 1, 2)")
     ap.add_argument("--shapes-from", default=None,
@@ -436,9 +456,17 @@ def main(argv=None):
         return 0
     if args.out is None:
         ap.error("the output CSV is required")
-    if args.wide or args.wide_layers:
-        shapes = wide_shapes(args.shapes, args.seed) if args.wide else \
-            [(M, N, K) for (K, N) in WIDE_LAYERS for M in (136, 160, 192, 224, 256) if M * N <= (1 << 20)]
+    if args.wide or args.wide_layers or args.mid or args.mid_layers:
+        if args.mid:
+            shapes = mid_shapes(args.shapes, args.seed)
+        elif args.mid_layers:
+            layers = sorted(set(ROUTE_LAYERS + ROUTE_NARROW_LAYERS + WIDE_LAYERS))
+            shapes = [(M, N, K) for (K, N) in layers for M in (72, 96, 112, 128)
+                      if -(-M // 64) * -(-N // 256) * 2 < 256]
+        elif args.wide:
+            shapes = wide_shapes(args.shapes, args.seed)
+        else:
+            shapes = [(M, N, K) for (K, N) in WIDE_LAYERS for M in (136, 160, 192, 224, 256) if M * N <= (1 << 20)]
         with open(args.out, "w", newline="") as f:
             w = csv.writer(f)
             w.writerow(WIDE_FIELDS)
