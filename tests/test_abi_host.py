@@ -326,12 +326,13 @@ def test_every_plan_fits_its_lds_with_and_without_workspace(lib, K, N):
     (129, 11008, 4096, 0), (256, 11008, 4096, 0), (256, 4096, 2048, 0), (192, 13824, 5120, 0),
     (224, 13824, 5120, 1), (257, 11008, 4096, 1), (160, 28672, 8192, 1), (256, 4096, 11008, 1),
     (160, 8192, 6144, 0), (165, 16512, 5760, 1), (136, 9984, 7296, 1),
-    (72, 8192, 10240, 0), (122, 19584, 8448, 1), (100, 27776, 8448, 1)])
+    (72, 8192, 10240, 0), (122, 19584, 8448, 1), (100, 27776, 8448, 1), (111, 12544, 9344, 1),
+    (111, 6656, 14592, 0)])
 def test_token_count_routes(lib, M, K, N, kind):
     """gemm_w4a8 takes the decode kernels up to 64 tokens; up to 128 while
     the 64 x 256 many-token tiles would fill under half of the CUs and the
-    weights are not very large (N x K <= 2^27, or four-m-tile workgroups fit
-    one round on the CUs); and up to 256 on layers with at most 2^20 outputs
+    weights are not very large (N x K <= 3 x 2^25, or four-m-tile workgroups
+    fit one round on the CUs); and up to 256 on layers with at most 2^20 outputs
     (M x N) whose weights are small (N x K <= 2^26) or whose four-m-tile
     workgroups fit one round.  The rest goes to the matrix-core kernel."""
     from w4a8_quantized_linear_amd import _lib
@@ -349,7 +350,7 @@ def test_token_count_routes(lib, M, K, N, kind):
     (100, 1152, 272, (1, 1, 1, 8, 0, 0)), (80, 4096, 1536, (1, 2, 1, 4, 0, 0)), (100, 8192, 768, (1, 2, 1, 4, 0, 0)),
     (128, 2048, 2048, (2, 2, 1, 8, 1, 0)), (96, 11008, 4096, (2, 4, 1, 4, 0, 0)), (96, 4096, 11008, (4, 4, 1, 4, 1, 1)),
     (72, 8192, 10240, (2, 4, 1, 4, 0, 0)), (112, 28672, 8192, (4, 4, 1, 4, 0, 0)),
-    (128, 12288, 10240, (4, 8, 2, 4, 1, 1))])
+    (128, 11008, 8448, (4, 8, 2, 4, 1, 1))])
 def test_wide_decode_plan_rule(lib, M, K, N, plan):
     """Past 64 tokens the decode plan comes from fixed trees, one for 65..128
     tokens and one for 129..256 (the learned selector, trained on 1..64

@@ -527,7 +527,7 @@ def test_workspace_shared_across_shapes_and_kernels():
                                    (256, 11008, 4096), (200, 8192, 2048), (137, 4096, 4096), (160, 4096, 768),
                                    (232, 4096, 4096), (160, 28672, 2048), (200, 28672, 2048), (160, 8192, 6144),
                                    (252, 24192, 1152), (80, 4096, 1536), (100, 8192, 768), (128, 2048, 2048),
-                                   (128, 12288, 10240)])
+                                   (128, 11008, 8448)])
 def test_gemm_mid_m_takes_the_decode_kernels(M, K, N):
     """65..128 tokens on layers whose 64 x 256 prefill tiles would leave more
     than half of the CUs idle, and 129..256 tokens on layers with at most

@@ -288,13 +288,16 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     // 65..128 tokens stay on the decode kernels while the matrix-core
     // kernel's smallest tiles (64 tokens x 256 channels) would leave more than
     // half of the CUs idle, unless the weights are very large (N x K above
-    // 2^27) and four-m-tile workgroups would take two rounds.  Measured on
-    // MI355X (graph-timed) against the matrix-core kernel's best TM and K
-    // split, M = 96: K = 4096, N = 11008: 19.0 against 25.1 us; K = 11008,
-    // N = 4096: 18.2 against 34.3; K = 12288, N = 1536: 13.0 against 35.2.
+    // 3 x 2^25, about 10^8) and four-m-tile workgroups would take two rounds.
+    // Measured on MI355X (graph-timed) against the matrix-core kernel's best
+    // TM and K split, M = 96: K = 4096, N = 11008: 19.0 against 25.1 us;
+    // K = 11008, N = 4096: 18.2 against 34.3; K = 12288, N = 1536: 13.0
+    // against 35.2.
     // At N = 22016 (172 tiles) the matrix-core kernel stays ahead (27.1
     // against 28.1), and on the excluded large weights it ran up to 1.35x
-    // faster (K = 19584, N = 8448, M = 122)
+    // faster (K = 19584, N = 8448, M = 122; K = 12544, N = 9344, M = 111:
+    // 1.22x), while below the bound the decode plans stayed within 6% or
+    // ahead (K = 8192, N = 10240, M = 72: 1.24x ahead)
     const int64_t cus = num_cus();
     const int64_t nblk = (ntiles * kTileN + 255) / 256;
     auto tiles_of = [&](int t) { return (M + 16 * t - 1) / (16 * t) * nblk; };
@@ -311,7 +314,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     // against 88.7 for the best decode plan)
     const int64_t wg44 = (M + 63) / 64 * ((ntiles + 3) / 4);
     const bool decode_m = M <= 64 ||
-                          (M <= 128 && tiles_of(4) * 2 < cus && (N * K <= (int64_t{1} << 27) || wg44 <= cus)) ||
+                          (M <= 128 && tiles_of(4) * 2 < cus && (N * K <= (int64_t{3} << 25) || wg44 <= cus)) ||
                           (M <= kDecodeMaxM && M * N <= (int64_t{1} << 20) && tiles_of(4) * 2 < cus &&
                            (N * K <= (int64_t{1} << 26) || wg44 <= cus));
 
