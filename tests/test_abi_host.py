@@ -361,6 +361,22 @@ def test_wide_decode_plan_rule(lib, M, K, N, plan):
     assert p["kind"] == 0 and (p["mt"], p["nt"], p["splitk"], p["waves"], p["xstage"], p["wave_n"]) == plan, p
 
 
+def test_decode_plan_override_forces_the_decode_kernels(lib, monkeypatch):
+    """W4A8_DECODE_PLAN runs the named decode plan at any M <= 256, also on
+    shapes the dispatcher would send to the matrix-core kernel (tuning
+    sweeps time decode plans there); past 256 tokens it is ignored, and a
+    plan no kernel variant implements still selects the decode kernels, with
+    the dispatcher's own decode plan."""
+    from w4a8_quantized_linear_amd import _lib
+    assert _lib.gemm_w4a8_plan(165, 5760, 16512)["kind"] == 1
+    monkeypatch.setenv("W4A8_DECODE_PLAN", "4,4,1,4,2,0,0")
+    p = _lib.gemm_w4a8_plan(165, 5760, 16512)
+    assert p["kind"] == 0 and (p["mt"], p["nt"], p["splitk"]) == (4, 4, 1), p
+    assert _lib.gemm_w4a8_plan(4096, 11008, 4096)["kind"] == 1
+    monkeypatch.setenv("W4A8_DECODE_PLAN", "3,4,1,4,2,0,0")
+    assert _lib.gemm_w4a8_plan(165, 5760, 16512)["kind"] == 0
+
+
 def test_gemm_k_limit(lib):
     from w4a8_quantized_linear_amd import _lib
     assert _lib.gemm_w4a8_workspace_bytes(1, 16, 1 << 23) == 0

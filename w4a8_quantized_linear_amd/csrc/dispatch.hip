@@ -6,7 +6,8 @@
 // the plan gemm_w4a8 launches always agree.  W4A8_DECODE_PLAN=
 // "mt,nt,splitk[,waves[,depth[,xstage[,wave_n]]]]" overrides the decode
 // choice and sends every M <= 256 to the decode kernels (for tuning sweeps);
-// an override that names no instantiated variant is ignored.
+// a plan that names no instantiated variant is replaced by the decode
+// kernels' own plan for the shape.
 #include <algorithm>
 #include <atomic>
 #include <cstdio>
@@ -201,8 +202,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
         // of the plan families, fitted (least total log-time over the best
         // plan) to graph-timed sweeps of every decode plan on MI355X at
         // 129..256 tokens: 150 random shapes (N = 512..7296, K = 2048..28672),
-        // 60 more and 15 layers of the 7B / 70B family.  Its plan runs at
-        // 1.02-1.05x the best plan's time on average (at most 1.24x).
+        // 60 more and 15 layers of the 7B / 70B family.  Re-timed live, its
+        // plan runs at 1.04-1.07x the best plan's time on average over each
+        // set (at most 1.3x).
         const int64_t cus = num_cus();
         auto wg = [&](int mt, int nt) { return (M + 16 * mt - 1) / (16 * mt) * ((ntiles + nt - 1) / nt); };
         auto use = [&](int mt, int nt, int s, int waves, bool xstage, int wave_n) {
@@ -242,9 +244,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
         // (4, 4) tilings, N x K and K, fitted like the one above to
         // graph-timed sweeps of every decode plan: 210 random shapes
         // (M = 65..128, N = 512..16384, K = 2048..28672) and 26 7B / 70B and
-        // narrow layers at 72..128 tokens.  Its plan runs at 1.02-1.04x the
-        // best plan's time on average on each set (at most 1.26x); the
-        // selector's picks ran at 1.08-1.11x (at most 1.66x).
+        // narrow layers at 72..128 tokens.  Re-timed live, its plan runs at
+        // 1.06x the best plan's time on average over each set (at most
+        // 1.3x); the selector's picks ran at 1.12x (at most 1.7x).
         const int64_t cus = num_cus();
         auto wg = [&](int mt, int nt) { return (M + 16 * mt - 1) / (16 * mt) * ((ntiles + nt - 1) / nt); };
         p.splitk = 1;
@@ -292,12 +294,11 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     // Measured on MI355X (graph-timed) against the matrix-core kernel's best
     // TM and K split, M = 96: K = 4096, N = 11008: 19.0 against 25.1 us;
     // K = 11008, N = 4096: 18.2 against 34.3; K = 12288, N = 1536: 13.0
-    // against 35.2.
-    // At N = 22016 (172 tiles) the matrix-core kernel stays ahead (27.1
-    // against 28.1), and on the excluded large weights it ran up to 1.35x
-    // faster (K = 19584, N = 8448, M = 122; K = 12544, N = 9344, M = 111:
-    // 1.22x), while below the bound the decode plans stayed within 6% or
-    // ahead (K = 8192, N = 10240, M = 72: 1.24x ahead)
+    // against 35.2.  At N = 22016 (172 tiles) the matrix-core kernel stays
+    // ahead (27.1 against 28.1), and on the excluded large weights it ran up
+    // to 1.35x faster (K = 19584, N = 8448, M = 122; K = 12544, N = 9344,
+    // M = 111: 1.22x), while below the bound the decode plans stayed within
+    // 6% or ahead (K = 8192, N = 10240, M = 72: 1.24x ahead)
     const int64_t cus = num_cus();
     const int64_t nblk = (ntiles * kTileN + 255) / 256;
     auto tiles_of = [&](int t) { return (M + 16 * t - 1) / (16 * t) * nblk; };
@@ -314,7 +315,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     // against 88.7 for the best decode plan)
     const int64_t wg44 = (M + 63) / 64 * ((ntiles + 3) / 4);
     const bool decode_m = M <= 64 ||
-                          (M <= 128 && tiles_of(4) * 2 < cus && (N * K <= (int64_t{3} << 25) || wg44 <= cus)) ||
+                          (M <= 128 && tiles_of(4) * 2 < cus &&
+                           (N * K <= (int64_t{3} << 25) || wg44 <= cus)) ||
                           (M <= kDecodeMaxM && M * N <= (int64_t{1} << 20) && tiles_of(4) * 2 < cus &&
                            (N * K <= (int64_t{1} << 26) || wg44 <= cus));
 
