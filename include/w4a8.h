@@ -232,7 +232,8 @@ w4a8_status w4a8_hbm_read(const void *buf, size_t bytes, uint32_t *sink, hipStre
  * 256; gemm_w4a8 takes the decode kernels up to 64 tokens, up to 128 when
  * the prefill kernel's 64 x 256 tiles would fill under half of the compute
  * units, and up to 256 when M x N is at most 2^20 as well, except on very
- * large weights whose four-m-tile workgroups would take two rounds): *count
+ * large weights whose four-m-tile workgroups would take two rounds, or at
+ * most 2^21 with N x K at most 2^25): *count
  * is their number; the first max_plans are written to plans as rows of
  * seven int32 (m-tiles, n-tiles, split-K, waves, depth, staged, waves
  * splitting N).  Each row, set in W4A8_DECODE_PLAN as

@@ -327,14 +327,16 @@ def test_every_plan_fits_its_lds_with_and_without_workspace(lib, K, N):
     (224, 13824, 5120, 1), (257, 11008, 4096, 1), (160, 28672, 8192, 1), (256, 4096, 11008, 1),
     (160, 8192, 6144, 0), (165, 16512, 5760, 1), (136, 9984, 7296, 1),
     (72, 8192, 10240, 0), (122, 19584, 8448, 1), (100, 27776, 8448, 1), (111, 12544, 9344, 1),
-    (111, 6656, 14592, 0)])
+    (111, 6656, 14592, 0), (229, 2176, 5376, 0), (131, 2048, 12544, 0), (160, 4096, 12288, 1),
+    (256, 4096, 8192, 0), (257, 2048, 4096, 1)])
 def test_token_count_routes(lib, M, K, N, kind):
     """gemm_w4a8 takes the decode kernels up to 64 tokens; up to 128 while
     the 64 x 256 many-token tiles would fill under half of the CUs and the
     weights are not very large (N x K <= 3 x 2^25, or four-m-tile workgroups
-    fit one round on the CUs); and up to 256 on layers with at most 2^20 outputs
-    (M x N) whose weights are small (N x K <= 2^26) or whose four-m-tile
-    workgroups fit one round.  The rest goes to the matrix-core kernel."""
+    fit one round on the CUs); and up to 256 on layers with at most 2^20
+    outputs (M x N) whose weights are small (N x K <= 2^26) or whose
+    four-m-tile workgroups fit one round, or with at most 2^21 outputs and
+    N x K <= 2^25.  The rest goes to the matrix-core kernel."""
     from w4a8_quantized_linear_amd import _lib
     p = _lib.gemm_w4a8_plan(M, N, K)
     assert p["kind"] == kind, (M, K, N, p)

@@ -307,18 +307,23 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     // four-m-tile workgroups would not fit one round on the CUs.  Graph-timed
     // on MI355X against the matrix-core kernel's best TM and K split on the
     // 277 shapes of the plan rule above: on the 274 it sends to the decode
-    // kernels their rule plan ran 0.92-4.6x the speed of the best matrix-core
+    // kernels their rule plan ran 0.90-4.5x the speed of the best matrix-core
     // run (K = 11008, N = 4096, M = 136: 25.7 against 34.9 us; K = 13824,
     // N = 5120, M = 160: 30.3 against 40.4); on the three it excludes, 0.64-
-    // 0.89x (K = 16512, N = 5760, M = 165: 71.1 against 45.3).  Wider layers
-    // stay on the matrix-core kernel (K = 28672, N = 8192, M = 160: 79.5
-    // against 88.7 for the best decode plan)
+    // 0.89x (K = 16512, N = 5760, M = 165: 71.1 against 45.3).  Up to 2^21
+    // outputs the decode kernels keep small weights (N x K <= 2^25): on 33 such
+    // random shapes their plan ran 0.96-1.45x the speed of the best
+    // matrix-core run (K = 2944, N = 5120, M = 254: 1.45x); past 2^25 the
+    // matrix-core kernel was mostly ahead.  Wider layers stay on the
+    // matrix-core kernel (K = 28672, N = 8192, M = 160: 79.5 against 88.7 for
+    // the best decode plan)
     const int64_t wg44 = (M + 63) / 64 * ((ntiles + 3) / 4);
     const bool decode_m = M <= 64 ||
                           (M <= 128 && tiles_of(4) * 2 < cus &&
                            (N * K <= (int64_t{3} << 25) || wg44 <= cus)) ||
                           (M <= kDecodeMaxM && M * N <= (int64_t{1} << 20) && tiles_of(4) * 2 < cus &&
-                           (N * K <= (int64_t{1} << 26) || wg44 <= cus));
+                           (N * K <= (int64_t{1} << 26) || wg44 <= cus)) ||
+                          (M <= kDecodeMaxM && M * N <= (int64_t{1} << 21) && N * K <= (int64_t{1} << 25));
 
     // the learned selector, when a model is compiled in: the candidate with
     // the highest predicted bandwidth utilization (remembered per shape);

@@ -213,17 +213,18 @@ WIDE_LAYERS = ((11008, 4096), (14336, 4096), (28672, 4096), (8192, 4096), (5120,
                (4096, 6144), (8192, 1024), (2048, 4096))
 
 
-def wide_shapes(n, seed):
-    """Random (M, N, K) with 129..256 tokens and at most 2^20 outputs: M
-    uniform, K log-uniform in 2048..28672, N log-uniform in 512..2^20 / M
-    (multiples of 128)."""
+def wide_shapes(n, seed, outputs=(0, 1 << 20)):
+    """Random (M, N, K) with 129..256 tokens and M x N in the `outputs` range
+    (default: at most 2^20): M uniform, K log-uniform in 2048..28672, N
+    log-uniform in max(512, lo / M)..hi / M (multiples of 128)."""
     rng = np.random.default_rng(seed)
+    lo, hi = outputs
     out = []
     while len(out) < n:
         M = int(rng.integers(129, 257))
         K = 128 * int(round(2 ** rng.uniform(math.log2(16), math.log2(224))))
-        N = 128 * int(round(2 ** rng.uniform(math.log2(4), math.log2(((1 << 20) // M) / 128))))
-        if N >= 512 and M * N <= (1 << 20):
+        N = 128 * int(round(2 ** rng.uniform(math.log2(max(512, lo // M) / 128), math.log2((hi // M) / 128))))
+        if N >= 512 and lo < M * N <= hi:
             out.append((M, N, K))
     return out
 
@@ -442,6 +443,7 @@ def main(argv=None):
                     help="129..256 tokens: every decode plan and many-token split, random shapes (--shapes, --seed)")
     ap.add_argument("--wide-layers", action="store_true", help="as --wide, on 15 7B / 70B layers at 136..256 tokens")
     ap.add_argument("--mid", action="store_true", help="as --wide, on random shapes with 65..128 tokens")
+    ap.add_argument("--outputs", default="0,1048576", help="lo,hi: the M x N range of --wide's random shapes")
     ap.add_argument("--mid-layers", action="store_true", help="as --wide, on 7B / 70B and narrow layers at 72..128 tokens")
     ap.add_argument("--wave-n", type=int, default=None,
                     help="time only the candidates of this decode kernel family (0, 1, 2)")
@@ -464,7 +466,7 @@ def main(argv=None):
             shapes = [(M, N, K) for (K, N) in layers for M in (72, 96, 112, 128)
                       if -(-M // 64) * -(-N // 256) * 2 < 256]
         elif args.wide:
-            shapes = wide_shapes(args.shapes, args.seed)
+            shapes = wide_shapes(args.shapes, args.seed, tuple(int(v) for v in args.outputs.split(",")))
         else:
             shapes = [(M, N, K) for (K, N) in WIDE_LAYERS for M in (136, 160, 192, 224, 256) if M * N <= (1 << 20)]
         with open(args.out, "w", newline="") as f:
