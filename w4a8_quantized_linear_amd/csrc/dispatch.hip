@@ -5,7 +5,7 @@
 // deterministic rule of (M, N, K), so the workspace size a caller queries and
 // the plan gemm_w4a8 launches always agree.  W4A8_DECODE_PLAN=
 // "mt,nt,splitk[,waves[,depth[,xstage[,wave_n]]]]" overrides the decode
-// choice and sends every M <= 256 to the decode kernels (for tuning sweeps);
+// choice and sends every M <= 512 to the decode kernels (for tuning sweeps);
 // a plan that names no instantiated variant is replaced by the decode
 // kernels' own plan for the shape.
 #include <algorithm>
@@ -197,14 +197,14 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
             p.splitk = 4;
         }
     } else if (M > 128) {
-        // 129..256 tokens (layers with at most 2^20 outputs, below): a small
+        // 129..512 tokens (layers with at most 2^20 outputs, below): a small
         // decision tree over the weight size, N, K and the workgroup counts
         // of the plan families, fitted (least total log-time over the best
         // plan) to graph-timed sweeps of every decode plan on MI355X at
         // 129..256 tokens: 150 random shapes (N = 512..7296, K = 2048..28672),
         // 60 more and 15 layers of the 7B / 70B family.  Re-timed live, its
         // plan runs at 1.04-1.07x the best plan's time on average over each
-        // set (at most 1.3x).
+        // set (at most 1.3x); at 320..512 tokens on narrow layers, 1.11x.
         const int64_t cus = num_cus();
         auto wg = [&](int mt, int nt) { return (M + 16 * mt - 1) / (16 * mt) * ((ntiles + nt - 1) / nt); };
         auto use = [&](int mt, int nt, int s, int waves, bool xstage, int wave_n) {
@@ -302,7 +302,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     const int64_t cus = num_cus();
     const int64_t nblk = (ntiles * kTileN + 255) / 256;
     auto tiles_of = [&](int t) { return (M + 16 * t - 1) / (16 * t) * nblk; };
-    // 129..256 tokens stay on the decode kernels on layers with at most 2^20
+    // 129..512 tokens stay on the decode kernels on layers with at most 2^20
     // outputs (M x N), unless the weights are large (N x K above 2^26) and
     // four-m-tile workgroups would not fit one round on the CUs.  Graph-timed
     // on MI355X against the matrix-core kernel's best TM and K split on the
@@ -316,13 +316,18 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     // matrix-core run (K = 2944, N = 5120, M = 254: 1.45x); past 2^25 the
     // matrix-core kernel was mostly ahead.  Wider layers stay on the
     // matrix-core kernel (K = 28672, N = 8192, M = 160: 79.5 against 88.7 for
-    // the best decode plan)
+    // the best decode plan).  Past 256 tokens only small weights (N x K <=
+    // 2^25) stay: on 100 random shapes with 257..512 tokens and the 7B / 70B
+    // layers at 320..512, those ran 0.91-3.4x the speed of the best
+    // matrix-core run (geomean 1.5-1.8x; K = 4096, N = 1024, M = 512: 9.8
+    // against 22.5 us), while larger weights lost up to 1.25x there
     const int64_t wg44 = (M + 63) / 64 * ((ntiles + 3) / 4);
     const bool decode_m = M <= 64 ||
                           (M <= 128 && tiles_of(4) * 2 < cus &&
                            (N * K <= (int64_t{3} << 25) || wg44 <= cus)) ||
                           (M <= kDecodeMaxM && M * N <= (int64_t{1} << 20) && tiles_of(4) * 2 < cus &&
-                           (N * K <= (int64_t{1} << 26) || wg44 <= cus)) ||
+                           (N * K <= (int64_t{1} << 26) || wg44 <= cus) &&
+                           (M <= 256 || N * K <= (int64_t{1} << 25))) ||
                           (M <= kDecodeMaxM && M * N <= (int64_t{1} << 21) && N * K <= (int64_t{1} << 25));
 
     // the learned selector, when a model is compiled in: the candidate with

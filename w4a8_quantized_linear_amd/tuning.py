@@ -25,7 +25,7 @@ program that profiler runs (rocprofv3 --pmc ...) trace for the decode counters.
 --route OUT.csv times, at 72..256 tokens on the 7B / 70B layers and on narrow layers,
 the best decode plan (every candidate) against the many-token kernel at each TM and
 K split, and the plan gemm_w4a8 picks: the evidence behind sending 65..128 tokens to
-the decode kernels when the many-token tiles are few, and 129..256 tokens when the
+the decode kernels when the many-token tiles are few, and 129..512 tokens when the
 layer has at most 2^20 outputs.
 
 --splits OUT.csv times the many-token kernel at 96..768 tokens on long-K layers for TM 4
@@ -34,8 +34,8 @@ tiles x s) and TM 16 whole, next to the plan gemm_w4a8 picks.
 
 --wide OUT.csv [--shapes 150 --seed 5] times, on random shapes with 129..256 tokens and
 at most 2^20 outputs, every decode plan, the many-token kernel at TM 4 / 8 with 1..4
-K ranges per tile, and the plan gemm_w4a8 picks; --wide-layers does the same on 15
-7B / 70B layers at 136..256 tokens.  The data behind the 129..256-token route and
+K ranges per tile, and the plan gemm_w4a8 picks (--wide-m and --outputs move the token
+and M x N ranges); --wide-layers does the same on 15 7B / 70B layers at 136..512 tokens.  The data behind the 129..256-token route and
 its decode plan tree.  --mid does the same on random shapes with 65..128 tokens
 that the dispatcher sends to the decode kernels, --mid-layers on the 7B / 70B and
 narrow layers above at 72..128 tokens.
@@ -213,15 +213,16 @@ WIDE_LAYERS = ((11008, 4096), (14336, 4096), (28672, 4096), (8192, 4096), (5120,
                (4096, 6144), (8192, 1024), (2048, 4096))
 
 
-def wide_shapes(n, seed, outputs=(0, 1 << 20)):
-    """Random (M, N, K) with 129..256 tokens and M x N in the `outputs` range
-    (default: at most 2^20): M uniform, K log-uniform in 2048..28672, N
-    log-uniform in max(512, lo / M)..hi / M (multiples of 128)."""
+def wide_shapes(n, seed, outputs=(0, 1 << 20), tokens=(129, 256)):
+    """Random (M, N, K) with M in `tokens` (default 129..256) and M x N in
+    the `outputs` range (default: at most 2^20): M uniform, K log-uniform in
+    2048..28672, N log-uniform in max(512, lo / M)..hi / M (multiples of
+    128)."""
     rng = np.random.default_rng(seed)
     lo, hi = outputs
     out = []
     while len(out) < n:
-        M = int(rng.integers(129, 257))
+        M = int(rng.integers(tokens[0], tokens[1] + 1))
         K = 128 * int(round(2 ** rng.uniform(math.log2(16), math.log2(224))))
         N = 128 * int(round(2 ** rng.uniform(math.log2(max(512, lo // M) / 128), math.log2((hi // M) / 128))))
         if N >= 512 and lo < M * N <= hi:
@@ -246,7 +247,7 @@ def mid_shapes(n, seed):
 
 
 def wide(writer, shapes, reps=10):
-    """129..256 tokens: every decode candidate, the many-token kernel at TM 4 / 8
+    """129..512 tokens: every decode candidate, the many-token kernel at TM 4 / 8
     with every tile split into s = 1..4 K ranges, and the plan gemm_w4a8 picks."""
     import torch
 
@@ -441,9 +442,10 @@ def main(argv=None):
     ap.add_argument("--splits", action="store_true", help="many-token kernel: splits per tile at 96..768 tokens")
     ap.add_argument("--wide", action="store_true",
                     help="129..256 tokens: every decode plan and many-token split, random shapes (--shapes, --seed)")
-    ap.add_argument("--wide-layers", action="store_true", help="as --wide, on 15 7B / 70B layers at 136..256 tokens")
+    ap.add_argument("--wide-layers", action="store_true", help="as --wide, on 15 7B / 70B layers at 136..512 tokens")
     ap.add_argument("--mid", action="store_true", help="as --wide, on random shapes with 65..128 tokens")
     ap.add_argument("--outputs", default="0,1048576", help="lo,hi: the M x N range of --wide's random shapes")
+    ap.add_argument("--wide-m", default="129,256", help="lo,hi: the token counts of --wide's random shapes")
     ap.add_argument("--mid-layers", action="store_true", help="as --wide, on 7B / 70B and narrow layers at 72..128 tokens")
     ap.add_argument("--wave-n", type=int, default=None,
                     help="time only the candidates of this decode kernel family (0, 1, 2)")
@@ -466,9 +468,11 @@ def main(argv=None):
             shapes = [(M, N, K) for (K, N) in layers for M in (72, 96, 112, 128)
                       if -(-M // 64) * -(-N // 256) * 2 < 256]
         elif args.wide:
-            shapes = wide_shapes(args.shapes, args.seed, tuple(int(v) for v in args.outputs.split(",")))
+            shapes = wide_shapes(args.shapes, args.seed, tuple(int(v) for v in args.outputs.split(",")),
+                                 tuple(int(v) for v in args.wide_m.split(",")))
         else:
-            shapes = [(M, N, K) for (K, N) in WIDE_LAYERS for M in (136, 160, 192, 224, 256) if M * N <= (1 << 20)]
+            shapes = [(M, N, K) for (K, N) in WIDE_LAYERS for M in (136, 160, 192, 224, 256, 320, 384, 448, 512)
+                      if M * N <= (1 << 20)]
         with open(args.out, "w", newline="") as f:
             w = csv.writer(f)
             w.writerow(WIDE_FIELDS)
