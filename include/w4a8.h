@@ -229,16 +229,17 @@ w4a8_status w4a8_hbm_read(const void *buf, size_t bytes, uint32_t *sink, hipStre
  * desc[9] = the dynamic LDS bytes per workgroup its launch requests.
  *
  * gemm_w4a8_decode_candidates: the decode-kernel plans that can run (M <=
- * 512; gemm_w4a8 takes the decode kernels up to 64 tokens, up to 128 when
+ * 1024; gemm_w4a8 takes the decode kernels up to 64 tokens, up to 128 when
  * the prefill kernel's 64 x 256 tiles would fill under half of the compute
- * units, and up to 512 when M x N is at most 2^20 as well, except on very
+ * units, and up to 1024 when M x N is at most 2^20 as well, except on very
  * large weights whose four-m-tile workgroups would take two rounds, or at
- * most 2^21 with N x K at most 2^25): *count
+ * most 2^21 with N x K at most 2^25; past 256 tokens only N x K up to 2^25,
+ * past 512 up to 2^23): *count
  * is their number; the first max_plans are written to plans as rows of
  * seven int32 (m-tiles, n-tiles, split-K, waves, depth, staged, waves
  * splitting N).  Each row, set in W4A8_DECODE_PLAN as
  * "mt,nt,splitk,waves,depth,staged,wave_n", makes gemm_w4a8 run that plan
- * on the decode kernels at any M <= 512 (for tuning sweeps).
+ * on the decode kernels at any M <= 1024 (for tuning sweeps).
  *
  * gemm_w4a8_selector_score: the compiled-in model's predicted fraction of the
  * HBM peak for one such plan row on a device with `cus` compute units, or a

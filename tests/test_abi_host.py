@@ -310,7 +310,7 @@ def test_every_plan_fits_its_lds_with_and_without_workspace(lib, K, N):
     the NULL-workspace plan needs no workspace.  (An unsplit N-split plan at
     K = 28672 once asked for 137 KB, over the 128 KB decode limit.)"""
     from w4a8_quantized_linear_amd import _lib
-    for M in list(range(1, 129)) + [136, 160, 200, 256, 257, 320, 384, 511, 512, 513, 768, 4096]:
+    for M in list(range(1, 129)) + [136, 160, 200, 256, 257, 320, 384, 511, 512, 513, 768, 1024, 1025, 4096]:
         for with_ws in (True, False):
             d = _lib.gemm_w4a8_plan_detail(M, N, K, with_ws)
             limit = 160 * 1024 if d["kind"] == 1 else 128 * 1024
@@ -329,17 +329,18 @@ def test_every_plan_fits_its_lds_with_and_without_workspace(lib, K, N):
     (72, 8192, 10240, 0), (122, 19584, 8448, 1), (100, 27776, 8448, 1), (111, 12544, 9344, 1),
     (111, 6656, 14592, 0), (229, 2176, 5376, 0), (131, 2048, 12544, 0), (160, 4096, 12288, 1),
     (256, 4096, 8192, 0), (257, 2048, 4096, 0), (384, 8192, 2048, 0), (512, 4096, 1024, 0),
-    (512, 4096, 4096, 0), (512, 11008, 4096, 1), (320, 4096, 4096, 0), (513, 4096, 1024, 1),
-    (448, 28672, 2048, 1), (256, 28672, 2048, 0)])
+    (512, 4096, 4096, 0), (512, 11008, 4096, 1), (320, 4096, 4096, 0), (513, 4096, 1024, 0),
+    (448, 28672, 2048, 1), (256, 28672, 2048, 0), (1024, 4096, 1024, 0), (1024, 28672, 1024, 1),
+    (768, 8192, 2048, 1), (640, 4096, 2048, 0), (1025, 4096, 512, 1)])
 def test_token_count_routes(lib, M, K, N, kind):
     """gemm_w4a8 takes the decode kernels up to 64 tokens; up to 128 while
     the 64 x 256 many-token tiles would fill under half of the CUs and the
     weights are not very large (N x K <= 3 x 2^25, or four-m-tile workgroups
     fit one round on the CUs); and up to 256 on layers with at most 2^20
     outputs (M x N) whose weights are small (N x K <= 2^26) or whose
-    four-m-tile workgroups fit one round (past 256 tokens N x K <= 2^25), or
-    with at most 2^21 outputs and N x K <= 2^25.  The rest goes to the
-    matrix-core kernel."""
+    four-m-tile workgroups fit one round, or with at most 2^21 outputs and
+    N x K <= 2^25 (up to 1024 tokens; past 256 tokens N x K <= 2^25, past
+    512 N x K <= 2^23).  The rest goes to the matrix-core kernel."""
     from w4a8_quantized_linear_amd import _lib
     p = _lib.gemm_w4a8_plan(M, N, K)
     assert p["kind"] == kind, (M, K, N, p)
@@ -367,9 +368,9 @@ def test_wide_decode_plan_rule(lib, M, K, N, plan):
 
 
 def test_decode_plan_override_forces_the_decode_kernels(lib, monkeypatch):
-    """W4A8_DECODE_PLAN runs the named decode plan at any M <= 512, also on
+    """W4A8_DECODE_PLAN runs the named decode plan at any M <= 1024, also on
     shapes the dispatcher would send to the matrix-core kernel (tuning
-    sweeps time decode plans there); past 512 tokens it is ignored, and a
+    sweeps time decode plans there); past 1024 tokens it is ignored, and a
     plan no kernel variant implements still selects the decode kernels, with
     the dispatcher's own decode plan."""
     from w4a8_quantized_linear_amd import _lib

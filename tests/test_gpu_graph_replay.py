@@ -23,7 +23,7 @@ CASES = [
     (8, 2048, 1024, {"W4A8_DECODE_PLAN": "1,2,4,4,2,0,0"}, {"kind": 0, "splitk": 4, "wave_n": 0}),
     (24, 2048, 2048, {"W4A8_DECODE_PLAN": "2,4,2,4,2,1,1"}, {"kind": 0, "splitk": 2, "wave_n": 1}),
     (257, 1152, 1040, {"W4A8_PREFILL_TM": "8", "W4A8_PREFILL_P": "64"}, {"kind": 1, "mt": 8, "splitk": 64}),
-    (600, 1024, 2048, {}, {"kind": 1, "splitk": 0}),
+    (1100, 1024, 2048, {}, {"kind": 1, "splitk": 0}),
 ]
 
 

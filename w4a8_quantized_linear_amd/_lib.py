@@ -289,7 +289,7 @@ def gemm_w4a8_plan_detail(M: int, N: int, K: int, with_workspace: bool = True) -
 
 
 def gemm_w4a8_decode_candidates(M: int, N: int, K: int) -> list:
-    """Every decode-kernel plan that can run (M <= 512), as tuples (mt, nt, splitk, waves, depth, xstage, wave_n)."""
+    """Every decode-kernel plan that can run (M <= 1024), as tuples (mt, nt, splitk, waves, depth, xstage, wave_n)."""
     n = ctypes.c_int32(0)
     _check(load().gemm_w4a8_decode_candidates(M, N, K, None, 0, ctypes.byref(n)), "gemm_w4a8_decode_candidates")
     buf = (ctypes.c_int32 * (7 * max(1, n.value)))()

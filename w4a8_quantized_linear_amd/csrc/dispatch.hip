@@ -5,11 +5,12 @@
 // deterministic rule of (M, N, K), so the workspace size a caller queries and
 // the plan gemm_w4a8 launches always agree.  W4A8_DECODE_PLAN=
 // "mt,nt,splitk[,waves[,depth[,xstage[,wave_n]]]]" overrides the decode
-// choice and sends every M <= 512 to the decode kernels (for tuning sweeps);
+// choice and sends every M <= 1024 to the decode kernels (for tuning sweeps);
 // a plan that names no instantiated variant is replaced by the decode
 // kernels' own plan for the shape.
 #include <algorithm>
 #include <atomic>
+#include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <mutex>
@@ -197,14 +198,14 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
             p.splitk = 4;
         }
     } else if (M > 128) {
-        // 129..512 tokens (layers with at most 2^20 outputs, below): a small
+        // 129..1024 tokens (layers with at most 2^20 outputs, below): a small
         // decision tree over the weight size, N, K and the workgroup counts
         // of the plan families, fitted (least total log-time over the best
         // plan) to graph-timed sweeps of every decode plan on MI355X at
         // 129..256 tokens: 150 random shapes (N = 512..7296, K = 2048..28672),
         // 60 more and 15 layers of the 7B / 70B family.  Re-timed live, its
         // plan runs at 1.04-1.07x the best plan's time on average over each
-        // set (at most 1.3x); at 320..512 tokens on narrow layers, 1.11x.
+        // set (at most 1.3x); at 257..1024 tokens on narrow layers, 1.1x.
         const int64_t cus = num_cus();
         auto wg = [&](int mt, int nt) { return (M + 16 * mt - 1) / (16 * mt) * ((ntiles + nt - 1) / nt); };
         auto use = [&](int mt, int nt, int s, int waves, bool xstage, int wave_n) {
@@ -302,7 +303,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     const int64_t cus = num_cus();
     const int64_t nblk = (ntiles * kTileN + 255) / 256;
     auto tiles_of = [&](int t) { return (M + 16 * t - 1) / (16 * t) * nblk; };
-    // 129..512 tokens stay on the decode kernels on layers with at most 2^20
+    // 129..1024 tokens stay on the decode kernels on layers with at most 2^20
     // outputs (M x N), unless the weights are large (N x K above 2^26) and
     // four-m-tile workgroups would not fit one round on the CUs.  Graph-timed
     // on MI355X against the matrix-core kernel's best TM and K split on the
@@ -320,15 +321,19 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     // 2^25) stay: on 100 random shapes with 257..512 tokens and the 7B / 70B
     // layers at 320..512, those ran 0.91-3.4x the speed of the best
     // matrix-core run (geomean 1.5-1.8x; K = 4096, N = 1024, M = 512: 9.8
-    // against 22.5 us), while larger weights lost up to 1.25x there
+    // against 22.5 us), while larger weights lost up to 1.25x there.  Past
+    // 512 tokens only N x K <= 2^23 stays (K = 4096, N = 1024, M = 1024:
+    // 15.3 against 24.0 us; K = 8192, N = 2048 and K = 14336, N = 1024 were
+    // even or lost)
     const int64_t wg44 = (M + 63) / 64 * ((ntiles + 3) / 4);
+    const int64_t nk_cap = M <= 256 ? INT64_MAX : (M <= 512 ? int64_t{1} << 25 : int64_t{1} << 23);
     const bool decode_m = M <= 64 ||
                           (M <= 128 && tiles_of(4) * 2 < cus &&
                            (N * K <= (int64_t{3} << 25) || wg44 <= cus)) ||
                           (M <= kDecodeMaxM && M * N <= (int64_t{1} << 20) && tiles_of(4) * 2 < cus &&
-                           (N * K <= (int64_t{1} << 26) || wg44 <= cus) &&
-                           (M <= 256 || N * K <= (int64_t{1} << 25))) ||
-                          (M <= kDecodeMaxM && M * N <= (int64_t{1} << 21) && N * K <= (int64_t{1} << 25));
+                           (N * K <= (int64_t{1} << 26) || wg44 <= cus) && N * K <= nk_cap) ||
+                          (M <= kDecodeMaxM && M * N <= (int64_t{1} << 21) &&
+                           N * K <= std::min<int64_t>(int64_t{1} << 25, nk_cap));
 
     // the learned selector, when a model is compiled in: the candidate with
     // the highest predicted bandwidth utilization (remembered per shape);

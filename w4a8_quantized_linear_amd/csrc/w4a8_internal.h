@@ -141,7 +141,7 @@ hipError_t launch_gemm_decode_ns(const GemmPlan &p, const int8_t *qx, const floa
 // one workgroup per compute unit anyway.
 constexpr size_t kDecodeLdsMax = 128 * 1024;
 // the decode kernels take up to this many tokens (plan_gemm decides from 65 on)
-constexpr int64_t kDecodeMaxM = 512;
+constexpr int64_t kDecodeMaxM = 1024;
 
 // Learned plan selector (selector.hip): the QFactory reading notes (6.2) rank
 // kernel configurations by a small MLP's predicted memory-bandwidth

@@ -25,7 +25,7 @@ program that profiler runs (rocprofv3 --pmc ...) trace for the decode counters.
 --route OUT.csv times, at 72..256 tokens on the 7B / 70B layers and on narrow layers,
 the best decode plan (every candidate) against the many-token kernel at each TM and
 K split, and the plan gemm_w4a8 picks: the evidence behind sending 65..128 tokens to
-the decode kernels when the many-token tiles are few, and 129..512 tokens when the
+the decode kernels when the many-token tiles are few, and 129..1024 tokens when the
 layer has at most 2^20 outputs.
 
 --splits OUT.csv times the many-token kernel at 96..768 tokens on long-K layers for TM 4
@@ -247,7 +247,7 @@ def mid_shapes(n, seed):
 
 
 def wide(writer, shapes, reps=10):
-    """129..512 tokens: every decode candidate, the many-token kernel at TM 4 / 8
+    """129..1024 tokens: every decode candidate, the many-token kernel at TM 4 / 8
     with every tile split into s = 1..4 K ranges, and the plan gemm_w4a8 picks."""
     import torch
 
