@@ -330,8 +330,8 @@ def test_every_plan_fits_its_lds_with_and_without_workspace(lib, K, N):
     (111, 6656, 14592, 0), (229, 2176, 5376, 0), (131, 2048, 12544, 0), (160, 4096, 12288, 1),
     (256, 4096, 8192, 0), (257, 2048, 4096, 0), (384, 8192, 2048, 0), (512, 4096, 1024, 0),
     (512, 4096, 4096, 0), (512, 11008, 4096, 1), (320, 4096, 4096, 0), (513, 4096, 1024, 0),
-    (448, 28672, 2048, 1), (256, 28672, 2048, 0), (1024, 4096, 1024, 0), (1024, 28672, 1024, 1),
-    (768, 8192, 2048, 1), (640, 4096, 2048, 0), (1025, 4096, 512, 1)])
+    (448, 28672, 2048, 0), (256, 28672, 2048, 0), (1024, 4096, 1024, 0), (1024, 28672, 1024, 0),
+    (768, 8192, 2048, 1), (640, 4096, 2048, 0), (1025, 4096, 512, 1), (389, 27264, 2688, 1)])
 def test_token_count_routes(lib, M, K, N, kind):
     """gemm_w4a8 takes the decode kernels up to 64 tokens; up to 128 while
     the 64 x 256 many-token tiles would fill under half of the CUs and the
@@ -340,7 +340,8 @@ def test_token_count_routes(lib, M, K, N, kind):
     outputs (M x N) whose weights are small (N x K <= 2^26) or whose
     four-m-tile workgroups fit one round, or with at most 2^21 outputs and
     N x K <= 2^25 (up to 1024 tokens; past 256 tokens N x K <= 2^25, past
-    512 N x K <= 2^23).  The rest goes to the matrix-core kernel."""
+    512 N x K <= 2^23, unless four-m-tile workgroups fit one round).  The
+    rest goes to the matrix-core kernel."""
     from w4a8_quantized_linear_amd import _lib
     p = _lib.gemm_w4a8_plan(M, N, K)
     assert p["kind"] == kind, (M, K, N, p)
@@ -356,7 +357,8 @@ def test_token_count_routes(lib, M, K, N, kind):
     (100, 1152, 272, (1, 1, 1, 8, 0, 0)), (80, 4096, 1536, (1, 2, 1, 4, 0, 0)), (100, 8192, 768, (1, 2, 1, 4, 0, 0)),
     (128, 2048, 2048, (2, 2, 1, 8, 1, 0)), (96, 11008, 4096, (2, 4, 1, 4, 0, 0)), (96, 4096, 11008, (4, 4, 1, 4, 1, 1)),
     (72, 8192, 10240, (2, 4, 1, 4, 0, 0)), (112, 28672, 8192, (4, 4, 1, 4, 0, 0)),
-    (128, 11008, 8448, (4, 8, 2, 4, 1, 1))])
+    (128, 11008, 8448, (4, 8, 2, 4, 1, 1)), (448, 28672, 2048, (4, 4, 1, 4, 0, 0)),
+    (1012, 18176, 512, (4, 4, 1, 4, 0, 0))])
 def test_wide_decode_plan_rule(lib, M, K, N, plan):
     """Past 64 tokens the decode plan comes from fixed trees, one for 65..128
     tokens and one for 129..256 (the learned selector, trained on 1..64

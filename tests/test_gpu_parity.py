@@ -528,7 +528,8 @@ def test_workspace_shared_across_shapes_and_kernels():
                                    (232, 4096, 4096), (160, 28672, 2048), (200, 28672, 2048), (160, 8192, 6144),
                                    (252, 24192, 1152), (80, 4096, 1536), (100, 8192, 768), (128, 2048, 2048),
                                    (128, 11008, 8448), (229, 2176, 5376), (131, 2048, 12544), (384, 8192, 2048),
-                                   (512, 4096, 1024), (449, 6144, 2048), (1024, 4096, 1024), (700, 2048, 1024)])
+                                   (512, 4096, 1024), (449, 6144, 2048), (1024, 4096, 1024), (700, 2048, 1024),
+                                   (448, 28672, 2048)])
 def test_gemm_mid_m_takes_the_decode_kernels(M, K, N):
     """65..128 tokens on layers whose 64 x 256 prefill tiles would leave more
     than half of the CUs idle, and 129..1024 tokens on layers with at most

@@ -207,6 +207,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
         // plan runs at 1.04-1.07x the best plan's time on average over each
         // set (at most 1.3x); at 257..1024 tokens on narrow layers, 1.1x.
         const int64_t cus = num_cus();
+        const int64_t nk_cap = M <= 256 ? INT64_MAX : (M <= 512 ? int64_t{1} << 25 : int64_t{1} << 23);
         auto wg = [&](int mt, int nt) { return (M + 16 * mt - 1) / (16 * mt) * ((ntiles + nt - 1) / nt); };
         auto use = [&](int mt, int nt, int s, int waves, bool xstage, int wave_n) {
             p.mt = mt;
@@ -216,7 +217,13 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
             p.xstage = xstage;
             p.wave_n = wave_n;
         };
-        if (N * K <= (int64_t{1} << 25)) {
+        if (N * K > nk_cap) {
+            // past 256 tokens, weights above the tree's range (taken only
+            // when these workgroups fit one round): four m-tiles, unsplit.
+            // Against the matrix-core kernel's best run on 41 such shapes
+            // with 257..1024 tokens: 0.99-1.58x its speed
+            use(4, 4, 1, 4, false, 0);
+        } else if (N * K <= (int64_t{1} << 25)) {
             if (wg(1, 2) <= cus)
                 use(1, 2, 1, 8, K <= 8192, 0);             // one m-tile, the token rows staged when short
             else if (wg(2, 4) <= cus + cus / 2 && K >= 12288)
@@ -321,17 +328,18 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K)
     // 2^25) stay: on 100 random shapes with 257..512 tokens and the 7B / 70B
     // layers at 320..512, those ran 0.91-3.4x the speed of the best
     // matrix-core run (geomean 1.5-1.8x; K = 4096, N = 1024, M = 512: 9.8
-    // against 22.5 us), while larger weights lost up to 1.25x there.  Past
-    // 512 tokens only N x K <= 2^23 stays (K = 4096, N = 1024, M = 1024:
-    // 15.3 against 24.0 us; K = 8192, N = 2048 and K = 14336, N = 1024 were
-    // even or lost)
+    // against 22.5 us).  Past 512 tokens the tree's plans hold to
+    // N x K <= 2^23 (K = 4096, N = 1024, M = 1024: 15.3 against 24.0 us).
+    // Past those caps the tree's long-K plans lost up to 1.25x, so there the
+    // decode kernels run four m-tiles unsplit, and only where those
+    // workgroups fit one round (at 294 workgroups that plan lost 1.6x)
     const int64_t wg44 = (M + 63) / 64 * ((ntiles + 3) / 4);
     const int64_t nk_cap = M <= 256 ? INT64_MAX : (M <= 512 ? int64_t{1} << 25 : int64_t{1} << 23);
     const bool decode_m = M <= 64 ||
                           (M <= 128 && tiles_of(4) * 2 < cus &&
                            (N * K <= (int64_t{3} << 25) || wg44 <= cus)) ||
                           (M <= kDecodeMaxM && M * N <= (int64_t{1} << 20) && tiles_of(4) * 2 < cus &&
-                           (N * K <= (int64_t{1} << 26) || wg44 <= cus) && N * K <= nk_cap) ||
+                           (N * K <= (int64_t{1} << 26) || wg44 <= cus) && (N * K <= nk_cap || wg44 <= cus)) ||
                           (M <= kDecodeMaxM && M * N <= (int64_t{1} << 21) &&
                            N * K <= std::min<int64_t>(int64_t{1} << 25, nk_cap));
 
